@@ -1,0 +1,37 @@
+"""Oracle for the MoE grouped GEMM: plain, slow, obviously correct CPU code.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports this package:
+only the tests, the smoke check and the bench's CPU-baseline leg call it.  It
+shares no code with the HIP path (no kernels, headers, helpers or tables); the
+two meet only through the seeded inputs of the `workloads` package.
+
+What it computes (fp64 throughout, per-expert dense GEMMs, one library matmul
+per expert; nothing blocked, fused or reordered):
+  * M-grouped forward (RapidGEMM README, "Kernels", Mgemm): for the rows
+    offsets[e] <= i < offsets[e+1] of expert e,  Y[i, n] = sum_k X[i, k] W[e, n, k].
+  * M-grouped input gradient (same passage, the input-gradient form; the
+    DeepGEMM issue #10 thread: a GEMM's backward is two GEMMs, dgrad and wgrad):
+    dX[i, k] = sum_n dY[i, n] W[e, n, k].
+  * K-grouped weight gradient (RapidGEMM README, "Kernels", Kgemm: the grouped
+    FP32 weight gradient; DeepGEMM issue #10: wgrad is x^T dy):
+    dW[e, n, k] = sum_{offsets[e] <= i < offsets[e+1]} dY[i, n] X[i, k],
+    laid out like W so that it can update W.
+  * bf16 outputs are the fp64 result rounded once, directly, to bf16 with
+    round-to-nearest-even.
+
+Pins (tests/test_oracle_pins.py): exact rational brute force on tiny inputs,
+closed forms on one-hot inputs, a hand-worked example (tests/golden/), the
+adjoint identity tying fwd/dgrad/wgrad together, empty-group insertion,
+exhaustive codec round trips and tie cases.  Every function here is pinned;
+none is "parity unpinned".
+"""
+from .bf16 import bf16_bits_to_f64, f64_to_bf16_bits, bf16_ulp  # noqa: F401
+from .grouped_gemm import (  # noqa: F401
+    grouped_fwd,
+    grouped_dgrad,
+    grouped_wgrad,
+    sample_fwd,
+    sample_dgrad,
+    sample_wgrad,
+)
+from .gate import check_bf16, check_fp32, GateReport  # noqa: F401

@@ -1,0 +1,120 @@
+"""fp64 oracle of the M-grouped and K-grouped GEMMs (test infrastructure only).
+
+Shapes follow the RapidGEMM README ("Kernels"): x [M, K] holds expert-grouped
+rows, w [E, N, K] the per-expert weights, and a cumulative row-offset array
+with a leading zero, offsets [E + 1], says that expert e owns rows
+offsets[e] <= i < offsets[e+1].  Rows at or past offsets[E] belong to no
+expert; the oracle marks them NaN in fwd/dgrad results.
+
+Inputs are float64 arrays (bf16 inputs decoded exactly).  Each function is
+the definition written out: one dense float64 matmul per expert.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .bf16 import bf16_bits_to_f64
+
+
+def _check_offsets(offsets, E: int, M: int) -> np.ndarray:
+    o = np.asarray(offsets, dtype=np.int64)
+    if o.shape != (E + 1,):
+        raise ValueError(f"offsets must have E+1={E + 1} entries, got {o.shape}")
+    if o[0] != 0 or (np.diff(o) < 0).any() or o[-1] > M:
+        raise ValueError("offsets must start at 0, be non-decreasing and end <= M")
+    return o
+
+
+def grouped_fwd(x: np.ndarray, w: np.ndarray, offsets) -> np.ndarray:
+    """Y[i, :] = x[i, :] @ w[e].T for offsets[e] <= i < offsets[e+1]  (fp64)."""
+    M, K = x.shape
+    E, N, K2 = w.shape
+    assert K == K2
+    o = _check_offsets(offsets, E, M)
+    y = np.full((M, N), np.nan)
+    for e in range(E):
+        lo, hi = o[e], o[e + 1]
+        if hi > lo:
+            y[lo:hi] = x[lo:hi] @ w[e].T
+    return y
+
+
+def grouped_dgrad(dy: np.ndarray, w: np.ndarray, offsets) -> np.ndarray:
+    """dX[i, :] = dy[i, :] @ w[e] for offsets[e] <= i < offsets[e+1]  (fp64)."""
+    M, N = dy.shape
+    E, N2, K = w.shape
+    assert N == N2
+    o = _check_offsets(offsets, E, M)
+    dx = np.full((M, K), np.nan)
+    for e in range(E):
+        lo, hi = o[e], o[e + 1]
+        if hi > lo:
+            dx[lo:hi] = dy[lo:hi] @ w[e]
+    return dx
+
+
+def grouped_wgrad(dy: np.ndarray, x: np.ndarray, offsets, E: int,
+                  prior: np.ndarray | None = None) -> np.ndarray:
+    """dW[e] = dy[rows_e].T @ x[rows_e]  (fp64, [E, N, K]); empty e gives 0.
+
+    With `prior`, the result is prior + that (the accumulate-into-fp32 form of
+    the TransformerEngine PR #2045 discussion of fuse_wgrad_accumulation)."""
+    M, N = dy.shape
+    M2, K = x.shape
+    assert M == M2
+    o = _check_offsets(offsets, E, M)
+    dw = np.zeros((E, N, K))
+    for e in range(E):
+        lo, hi = o[e], o[e + 1]
+        if hi > lo:
+            dw[e] = dy[lo:hi].T @ x[lo:hi]
+    if prior is not None:
+        dw = dw + prior
+    return dw
+
+
+def expert_of_rows(offsets, rows: np.ndarray) -> np.ndarray:
+    """Expert index owning each row (rows past offsets[E] give -1)."""
+    o = np.asarray(offsets, dtype=np.int64)
+    e = np.searchsorted(o, rows, side="right") - 1
+    return np.where(np.asarray(rows) < o[-1], e, -1)
+
+
+def _f64(a: np.ndarray) -> np.ndarray:
+    """Gathered operand pieces: bf16 bit patterns are decoded exactly."""
+    return bf16_bits_to_f64(a) if a.dtype == np.uint16 else np.asarray(a, np.float64)
+
+
+def sample_fwd(x: np.ndarray, w: np.ndarray, offsets, rows, cols):
+    """Y[rows[j], cols[j]] one element at a time (vectorised over j), fp64.
+
+    x, w may be float64 arrays or bf16 bit patterns (only the gathered rows are
+    decoded).  Returns (value, sum of |products|); the second feeds the
+    accumulation-error floor of the parity gate.  Rows must lie below
+    offsets[E]."""
+    rows = np.asarray(rows); cols = np.asarray(cols)
+    e = expert_of_rows(offsets, rows)
+    assert (e >= 0).all()
+    p = _f64(x[rows]) * _f64(w[e, cols])        # [S, K]
+    return p.sum(axis=1), np.abs(p).sum(axis=1)
+
+
+def sample_dgrad(dy: np.ndarray, w: np.ndarray, offsets, rows, cols):
+    """dX[rows[j], cols[j]] = sum_n dy[r, n] w[e, n, c], fp64, with sum |.|."""
+    rows = np.asarray(rows); cols = np.asarray(cols)
+    e = expert_of_rows(offsets, rows)
+    assert (e >= 0).all()
+    p = _f64(dy[rows]) * _f64(w[e, :, cols])    # [S, N]
+    return p.sum(axis=1), np.abs(p).sum(axis=1)
+
+
+def sample_wgrad(dy: np.ndarray, x: np.ndarray, offsets, experts, ns, ks):
+    """dW[experts[j], ns[j], ks[j]] = sum over the expert's rows, fp64,
+    with sum |.|; an empty expert gives exactly (0, 0)."""
+    o = np.asarray(offsets, dtype=np.int64)
+    val = np.zeros(len(experts)); mag = np.zeros(len(experts))
+    for j, (e, n, k) in enumerate(zip(experts, ns, ks)):
+        lo, hi = o[e], o[e + 1]
+        p = _f64(dy[lo:hi, n]) * _f64(x[lo:hi, k])
+        val[j] = p.sum(); mag[j] = np.abs(p).sum()
+    return val, mag
