@@ -1,0 +1,111 @@
+/* mgemm.h -- C ABI of the MoE grouped GEMM library for AMD Instinct MI355X
+ * (gfx950).  Library: libmgemm.so.
+ *
+ * The operations follow the problem statement of the RapidGEMM README
+ * ("Kernels"): an M-grouped GEMM that computes the grouped forward or
+ * input-gradient product from expert-grouped rows x [M, K], per-expert
+ * weights w [E, N, K] and a cumulative row-offset array with a leading zero;
+ * and a K-grouped GEMM that computes the grouped FP32 weight gradient from the
+ * same expert-grouped rows.  The backward of a GEMM is two GEMMs, dgrad and
+ * wgrad (DeepGEMM issue #10).  One C entry point per operation serves every
+ * front end, as the TransformerEngine PR #2045 review asks of its grouped-GEMM
+ * API.
+ *
+ * Conventions shared by all calls
+ *   - (M, N, K, E) always describe the FORWARD problem: X [M, K],
+ *     W [E, N, K], Y [M, N].  All tensors are dense, row-major, contiguous.
+ *   - bf16 tensors are passed as pointers to 16-bit bf16 bit patterns.
+ *   - offsets: int32 DEVICE array of E + 1 entries, offsets[0] == 0,
+ *     non-decreasing, offsets[E] <= M.  Expert e owns rows
+ *     offsets[e] <= i < offsets[e+1]; experts may be empty and row counts are
+ *     arbitrary (no multiple-of-tile requirement).  The library never reads
+ *     the offsets on the host: this is a precondition, checked only when the
+ *     environment variable MGEMM_VALIDATE=1 (debug; it copies the offsets to
+ *     the host and synchronises the stream).
+ *   - All data pointers are DEVICE pointers, 16-byte aligned; N and K must be
+ *     multiples of 8 (every row starts 16-byte aligned).  1 <= E <= 1024.
+ *     M, N, K < 2^31.  Outputs must not alias inputs.
+ *   - stream: a hipStream_t (NULL = the null stream).  Each call only
+ *     enqueues work on that stream and returns; it never synchronises,
+ *     allocates, or keeps a pointer after returning.  The caller owns every
+ *     buffer and must keep it alive until the stream has run the work.
+ *   - Host-detectable errors are returned before anything is enqueued.
+ *     Launch failures return MG_ERR_LAUNCH.  Faults during execution surface
+ *     at the caller's next synchronisation, like any stream work.  Nothing
+ *     throws across this ABI.
+ *   - Thread safety: calls may be made concurrently from several threads; the
+ *     only shared state is a per-device architecture check done once.
+ */
+#ifndef MGEMM_H
+#define MGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mg_status {
+  MG_OK = 0,
+  MG_ERR_NULL = 1,     /* a required pointer is NULL                          */
+  MG_ERR_SHAPE = 2,    /* E < 1 or > 1024, negative or too large sizes, N or K
+                          not a multiple of 8                                 */
+  MG_ERR_ALIGN = 3,    /* a data pointer is not 16-byte aligned               */
+  MG_ERR_DEVICE = 4,   /* current device is not gfx950, or HIP query failed   */
+  MG_ERR_LAUNCH = 5,   /* the kernel launch was rejected                      */
+  MG_ERR_OFFSETS = 6   /* offsets violate the precondition (validation only)  */
+} mg_status;
+
+/* M-grouped forward (RapidGEMM README, "Kernels", Mgemm forward form):
+ *   y[i, n] = sum_k x[i, k] * w[e, n, k]   for offsets[e] <= i < offsets[e+1]
+ * x: bf16 [M, K]; w: bf16 [E, N, K]; y: bf16 [M, N] (written).
+ * Products accumulate in fp32; y is the fp32 sum rounded to nearest even.
+ * Rows i >= offsets[E] of y are not touched.  M == 0 or N == 0 is a no-op;
+ * K == 0 writes zeros to the owned rows.
+ * max_m_per_e: optional hint, an upper bound on any expert's row count, used
+ * only to size the launch (0 = unknown).  Results never depend on it: with a
+ * hint that is too small each workgroup simply processes more tiles.  A
+ * negative value gives MG_ERR_SHAPE. */
+mg_status mgemm_fwd(const void* x, const void* w, const int32_t* offsets, void* y,
+                    int64_t M, int64_t N, int64_t K, int32_t E, int64_t max_m_per_e,
+                    void* stream);
+
+/* M-grouped input gradient (the same call's input-gradient form):
+ *   dx[i, k] = sum_n dy[i, n] * w[e, n, k]   for offsets[e] <= i < offsets[e+1]
+ * dy: bf16 [M, N]; w: bf16 [E, N, K]; dx: bf16 [M, K] (written).
+ * fp32 accumulation, round to nearest even.  Rows i >= offsets[E] of dx are
+ * not touched.  M == 0 or K == 0 is a no-op; N == 0 writes zeros.
+ * max_m_per_e: launch-size hint, as for mgemm_fwd. */
+mg_status mgemm_dgrad(const void* dy, const void* w, const int32_t* offsets, void* dx,
+                      int64_t M, int64_t N, int64_t K, int32_t E, int64_t max_m_per_e,
+                      void* stream);
+
+/* K-grouped weight gradient in FP32 (RapidGEMM README, "Kernels", Kgemm;
+ * wgrad is x^T dy, DeepGEMM issue #10, laid out like w so it can update w):
+ *   dw[e, n, k] (= or +=) sum_{offsets[e] <= i < offsets[e+1]} dy[i, n] * x[i, k]
+ * dy: bf16 [M, N]; x: bf16 [M, K]; dw: fp32 [E, N, K].
+ * accumulate == 0: dw is overwritten, and an expert with no rows gets zeros.
+ * accumulate != 0: the sum is added to dw's contents (fp32 gradient
+ * accumulation, as in the TransformerEngine PR #2045 review of
+ * fuse_wgrad_accumulation), and an empty expert's block is left as it was.
+ * Rows i >= offsets[E] do not contribute.  N == 0 or K == 0 is a no-op. */
+mg_status kgemm_wgrad(const void* dy, const void* x, const int32_t* offsets, float* dw,
+                      int64_t M, int64_t N, int64_t K, int32_t E, int32_t accumulate,
+                      void* stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* mg_status_str(int32_t status);
+
+/* Version of this ABI; bumped on any incompatible change. */
+int32_t mg_abi_version(void);
+
+/* Host-side check of an offsets array held in HOST memory (no device use):
+ * MG_OK if offsets[0] == 0, non-decreasing, offsets[E] <= M; MG_ERR_OFFSETS
+ * otherwise; MG_ERR_NULL / MG_ERR_SHAPE for a NULL pointer or bad E / M. */
+mg_status mg_check_offsets_host(const int32_t* offsets_host, int32_t E, int64_t M);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MGEMM_H */

@@ -1,0 +1,152 @@
+"""MoE grouped GEMM for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI of libmgemm.so (include/mgemm.h): argument
+checks and marshalling only.  Every step of the computation runs in the HIP
+kernels; PyTorch provides device memory and the current stream.
+
+  fwd(x, w, offsets)      Y[i] = x[i] W[e]^T          M-grouped forward
+  dgrad(dy, w, offsets)   dX[i] = dy[i] W[e]          M-grouped input gradient
+  wgrad(dy, x, offsets)   dW[e] = sum_i dy[i]^T x[i]  K-grouped fp32 weight gradient
+
+Page-shaped aliases follow the RapidGEMM README ("Kernels"):
+  Mgemm(x, w, cnt, max_M_per_E, transpose_B) and Kgemm(grad, X, cnt, descriptor).
+"""
+from __future__ import annotations
+
+import torch
+
+from ._lib import LIB, MgemmError, check, status_str  # noqa: F401
+
+__all__ = ["fwd", "dgrad", "wgrad", "Mgemm", "Kgemm", "MgemmError", "status_str", "LIB"]
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _offsets(offsets: torch.Tensor, E: int, dev) -> torch.Tensor:
+    _need(offsets, "offsets", torch.int32, 1)
+    if offsets.numel() != E + 1:
+        raise ValueError(f"offsets must have E+1 = {E + 1} entries, got {offsets.numel()}")
+    if offsets.device != dev:
+        raise ValueError("offsets must be on the same device as the data")
+    return offsets
+
+
+def fwd(x: torch.Tensor, w: torch.Tensor, offsets: torch.Tensor, max_m_per_e: int = 0,
+        out: torch.Tensor | None = None) -> torch.Tensor:
+    """M-grouped forward: out[i] = x[i] @ w[e].T for offsets[e] <= i < offsets[e+1].
+
+    x bf16 [M, K], w bf16 [E, N, K], offsets int32 [E+1] (device).  Rows past
+    offsets[E] of `out` are left untouched (uninitialised when `out` is None)."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(w, "w", torch.bfloat16, 3)
+    M, K = x.shape
+    E, N, K2 = w.shape
+    if K2 != K:
+        raise ValueError(f"x is [M, {K}] but w is [E, N, {K2}]")
+    _offsets(offsets, E, x.device)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    else:
+        _need(out, "out", torch.bfloat16, 2)
+        if tuple(out.shape) != (M, N):
+            raise ValueError(f"out must be [{M}, {N}]")
+    with torch.cuda.device(x.device):
+        st = LIB.mgemm_fwd(x.data_ptr(), w.data_ptr(), offsets.data_ptr(), out.data_ptr(),
+                           M, N, K, E, int(max_m_per_e), _stream(x))
+    check(st, "mgemm_fwd")
+    return out
+
+
+def dgrad(dy: torch.Tensor, w: torch.Tensor, offsets: torch.Tensor, max_m_per_e: int = 0,
+          out: torch.Tensor | None = None) -> torch.Tensor:
+    """M-grouped input gradient: out[i] = dy[i] @ w[e] for the rows of expert e.
+
+    dy bf16 [M, N], w bf16 [E, N, K]; returns bf16 [M, K]."""
+    _need(dy, "dy", torch.bfloat16, 2)
+    _need(w, "w", torch.bfloat16, 3)
+    M, N = dy.shape
+    E, N2, K = w.shape
+    if N2 != N:
+        raise ValueError(f"dy is [M, {N}] but w is [E, {N2}, K]")
+    _offsets(offsets, E, dy.device)
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.bfloat16, device=dy.device)
+    else:
+        _need(out, "out", torch.bfloat16, 2)
+        if tuple(out.shape) != (M, K):
+            raise ValueError(f"out must be [{M}, {K}]")
+    with torch.cuda.device(dy.device):
+        st = LIB.mgemm_dgrad(dy.data_ptr(), w.data_ptr(), offsets.data_ptr(), out.data_ptr(),
+                             M, N, K, E, int(max_m_per_e), _stream(dy))
+    check(st, "mgemm_dgrad")
+    return out
+
+
+def wgrad(dy: torch.Tensor, x: torch.Tensor, offsets: torch.Tensor, E: int | None = None,
+          out: torch.Tensor | None = None, accumulate: bool = False) -> torch.Tensor:
+    """K-grouped fp32 weight gradient: out[e] (=|+=) dy[rows_e].T @ x[rows_e].
+
+    dy bf16 [M, N], x bf16 [M, K]; returns fp32 [E, N, K].  E defaults to
+    offsets.numel() - 1.  With accumulate=True the sum is added into `out`."""
+    _need(dy, "dy", torch.bfloat16, 2)
+    _need(x, "x", torch.bfloat16, 2)
+    M, N = dy.shape
+    M2, K = x.shape
+    if M2 != M:
+        raise ValueError(f"dy has {M} rows but x has {M2}")
+    if E is None:
+        E = offsets.numel() - 1
+    _offsets(offsets, E, dy.device)
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs `out`")
+        out = torch.empty((E, N, K), dtype=torch.float32, device=dy.device)
+    else:
+        _need(out, "out", torch.float32, 3)
+        if tuple(out.shape) != (E, N, K):
+            raise ValueError(f"out must be [{E}, {N}, {K}]")
+    with torch.cuda.device(dy.device):
+        st = LIB.kgemm_wgrad(dy.data_ptr(), x.data_ptr(), offsets.data_ptr(), out.data_ptr(),
+                             M, N, K, E, 1 if accumulate else 0, _stream(dy))
+    check(st, "kgemm_wgrad")
+    return out
+
+
+def Mgemm(x: torch.Tensor, w: torch.Tensor, cnt: torch.Tensor, max_M_per_E: int = 0,
+          transpose_B: bool = True) -> torch.Tensor:
+    """RapidGEMM-shaped M-grouped GEMM (README, "Kernels").
+
+    w is stored [E, N, K].  transpose_B=True uses it transposed (the forward,
+    x [M, K] -> [M, N]); transpose_B=False uses it as stored (the input
+    gradient, x [M, N] -> [M, K]).  cnt: cumulative row offsets with a leading
+    zero."""
+    if transpose_B:
+        return fwd(x, w, cnt, max_M_per_E)
+    return dgrad(x, w, cnt, max_M_per_E)
+
+
+def Kgemm(grad: torch.Tensor, X: torch.Tensor, cnt: torch.Tensor,
+          descriptor: str | None = None) -> torch.Tensor:
+    """RapidGEMM-shaped K-grouped fp32 weight gradient (README, "Kernels").
+
+    descriptor names which weight is differentiated ("gw13": fused gate/up
+    projection, "gw2": down projection); shapes come from the tensors, so it
+    is only a label here."""
+    if descriptor not in (None, "gw13", "gw2"):
+        raise ValueError(f"descriptor must be 'gw13', 'gw2' or None, got {descriptor!r}")
+    return wgrad(grad, X, cnt)

@@ -1,0 +1,58 @@
+"""ctypes view of libmgemm.so (the C ABI declared in include/mgemm.h).
+
+Loading never falls back to anything: if the library is missing or broken,
+importing raises, naming the file and how to build it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmgemm.so")
+
+# status codes of mg_status
+MG_OK, MG_ERR_NULL, MG_ERR_SHAPE, MG_ERR_ALIGN, MG_ERR_DEVICE, MG_ERR_LAUNCH, MG_ERR_OFFSETS = range(7)
+
+# name -> (restype, argtypes); the exported symbols of include/mgemm.h
+_vp, _i32, _i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+SIGNATURES = {
+    "mgemm_fwd": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i64, _vp]),
+    "mgemm_dgrad": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i64, _vp]),
+    "kgemm_wgrad": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp]),
+    "mg_status_str": (ctypes.c_char_p, [_i32]),
+    "mg_abi_version": (_i32, []),
+    "mg_check_offsets_host": (_i32, [_vp, _i32, _i64]),
+}
+
+
+class MgemmError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_str(status)} (status {status})")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m moe_grouped_gemm_bf16_amd.build` "
+            "(hipcc, gfx950). There is no fallback implementation.")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if lib.mg_abi_version() != 1:
+        raise ImportError(f"{LIB_PATH}: unexpected ABI version {lib.mg_abi_version()}")
+    return lib
+
+
+LIB = _load()
+
+
+def status_str(status: int) -> str:
+    return LIB.mg_status_str(int(status)).decode()
+
+
+def check(status: int, what: str) -> None:
+    if status != MG_OK:
+        raise MgemmError(status, what)

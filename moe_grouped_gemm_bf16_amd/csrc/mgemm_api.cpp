@@ -1,0 +1,161 @@
+// C-ABI entry points of libmgemm.so: argument validation, device check and
+// dispatch to the gfx950 kernels.  No allocation, no host workspace, no
+// host<->device copy and no synchronisation on the normal path: the offsets
+// stay on the device and are read by the kernels' own tile scheduler (a host
+// workspace copied to the device per call, freed before the asynchronous copy
+// has run, is the lifetime race discussed in the TransformerEngine PR #2045
+// review; this design has no such buffer).
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "mgemm.h"
+#include "mgemm_launch.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 22;     // N, K: 256-row tile offsets fit int32
+constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
+constexpr int kMaxDevices = 64;
+
+std::atomic<int> g_arch_state[kMaxDevices];       // 0 unknown, 1 gfx950, 2 other
+
+mg_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MG_ERR_DEVICE;
+  int st = g_arch_state[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MG_ERR_DEVICE;
+    st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch_state[dev].store(st, std::memory_order_release);
+  }
+  return st == 1 ? MG_OK : MG_ERR_DEVICE;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+mg_status check_sizes(int64_t M, int64_t N, int64_t K, int32_t E) {
+  if (E < 1 || E > mg::kMaxExperts) return MG_ERR_SHAPE;
+  if (M < 0 || N < 0 || K < 0 || M > kMaxRows || N > kMaxDim || K > kMaxDim) return MG_ERR_SHAPE;
+  if ((N & 7) || (K & 7)) return MG_ERR_SHAPE;
+  return MG_OK;
+}
+
+// Optional debug validation of the device offsets (MGEMM_VALIDATE=1): copies
+// them to the host on the caller's stream and synchronises it.
+mg_status maybe_validate(const int32_t* offsets, int32_t E, int64_t M, hipStream_t s) {
+  static const bool on = [] {
+    const char* v = std::getenv("MGEMM_VALIDATE");
+    return v != nullptr && v[0] == '1';
+  }();
+  if (!on) return MG_OK;
+  std::vector<int32_t> h(static_cast<size_t>(E) + 1);
+  if (hipMemcpyAsync(h.data(), offsets, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost, s) !=
+          hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return MG_ERR_DEVICE;
+  return mg_check_offsets_host(h.data(), E, M);
+}
+
+mg_status launch(int mode, const mg::KernelArgs& a, int64_t max_m_per_e, hipStream_t s) {
+  int err = mg::launch_grouped(mode, a, max_m_per_e, s);
+  return err == hipSuccess ? MG_OK : MG_ERR_LAUNCH;
+}
+
+// Shared body of the two M-grouped calls.  `a_in` is x (fwd) or dy (dgrad).
+mg_status mgrouped(int mode, const void* a_in, const void* w, const int32_t* offsets, void* out,
+                   int64_t M, int64_t N, int64_t K, int32_t E, int64_t max_m_per_e,
+                   void* stream) {
+  mg_status st = check_sizes(M, N, K, E);
+  if (st != MG_OK) return st;
+  if (max_m_per_e < 0) return MG_ERR_SHAPE;
+  const int64_t pdim = mode == mg::kFwd ? N : K;
+  // tile-count bound used by the scheduler must fit in int32
+  if (((M + 255) / 256 + E) * ((pdim + 255) / 256) > kMaxRows) return MG_ERR_SHAPE;
+  if (M == 0 || pdim == 0) return MG_OK;
+  const int64_t red = mode == mg::kFwd ? K : N;   // an empty reduction reads no input
+  if (!offsets || !out || (red > 0 && (!a_in || !w))) return MG_ERR_NULL;
+  if ((red > 0 && (!aligned16(a_in) || !aligned16(w))) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(offsets) & 3u))
+    return MG_ERR_ALIGN;
+  if ((st = check_device()) != MG_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = maybe_validate(offsets, E, M, s)) != MG_OK) return st;
+  mg::KernelArgs a{};
+  a.p_src = w;
+  a.q_src = a_in;
+  a.offsets = offsets;
+  a.out = out;
+  a.M = M; a.N = N; a.K = K; a.E = E;
+  a.accumulate = 0;
+  return launch(mode, a, max_m_per_e, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+mg_status mgemm_fwd(const void* x, const void* w, const int32_t* offsets, void* y, int64_t M,
+                    int64_t N, int64_t K, int32_t E, int64_t max_m_per_e, void* stream) {
+  return mgrouped(mg::kFwd, x, w, offsets, y, M, N, K, E, max_m_per_e, stream);
+}
+
+mg_status mgemm_dgrad(const void* dy, const void* w, const int32_t* offsets, void* dx, int64_t M,
+                      int64_t N, int64_t K, int32_t E, int64_t max_m_per_e, void* stream) {
+  return mgrouped(mg::kDgrad, dy, w, offsets, dx, M, N, K, E, max_m_per_e, stream);
+}
+
+mg_status kgemm_wgrad(const void* dy, const void* x, const int32_t* offsets, float* dw,
+                      int64_t M, int64_t N, int64_t K, int32_t E, int32_t accumulate,
+                      void* stream) {
+  mg_status st = check_sizes(M, N, K, E);
+  if (st != MG_OK) return st;
+  if ((int64_t)E * ((N + 255) / 256) * ((K + 255) / 256) > kMaxRows) return MG_ERR_SHAPE;
+  if (N == 0 || K == 0) return MG_OK;
+  if (!offsets || !dw || (M > 0 && (!dy || !x))) return MG_ERR_NULL;
+  if ((M > 0 && (!aligned16(dy) || !aligned16(x))) || !aligned16(dw) ||
+      (reinterpret_cast<uintptr_t>(offsets) & 3u))
+    return MG_ERR_ALIGN;
+  if ((st = check_device()) != MG_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = maybe_validate(offsets, E, M, s)) != MG_OK) return st;
+  mg::KernelArgs a{};
+  a.p_src = x;
+  a.q_src = dy;
+  a.offsets = offsets;
+  a.out = dw;
+  a.M = M; a.N = N; a.K = K; a.E = E;
+  a.accumulate = accumulate ? 1 : 0;
+  return launch(mg::kWgrad, a, 0, s);
+}
+
+const char* mg_status_str(int32_t status) {
+  switch (status) {
+    case MG_OK: return "MG_OK";
+    case MG_ERR_NULL: return "MG_ERR_NULL: a required pointer is NULL";
+    case MG_ERR_SHAPE: return "MG_ERR_SHAPE: unsupported sizes (E in [1,1024], N,K multiples of 8)";
+    case MG_ERR_ALIGN: return "MG_ERR_ALIGN: data pointers must be 16-byte aligned";
+    case MG_ERR_DEVICE: return "MG_ERR_DEVICE: current device is not gfx950 (or HIP failed)";
+    case MG_ERR_LAUNCH: return "MG_ERR_LAUNCH: kernel launch failed";
+    case MG_ERR_OFFSETS: return "MG_ERR_OFFSETS: offsets must start at 0, not decrease, end <= M";
+    default: return "unknown mg_status";
+  }
+}
+
+int32_t mg_abi_version(void) { return 1; }
+
+mg_status mg_check_offsets_host(const int32_t* offsets_host, int32_t E, int64_t M) {
+  if (!offsets_host) return MG_ERR_NULL;
+  if (E < 1 || E > mg::kMaxExperts || M < 0 || M > kMaxRows) return MG_ERR_SHAPE;
+  if (offsets_host[0] != 0) return MG_ERR_OFFSETS;
+  for (int32_t e = 0; e < E; ++e)
+    if (offsets_host[e + 1] < offsets_host[e]) return MG_ERR_OFFSETS;
+  if (offsets_host[E] > M) return MG_ERR_OFFSETS;
+  return MG_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,27 @@
+// Internal interface between the C-ABI layer and the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mg {
+
+enum { kFwd = 0, kDgrad = 1, kWgrad = 2 };
+
+// Largest expert count a launch accepts: the device-side scheduler keeps the
+// per-expert tile prefix in LDS, two entries per thread of a 512-thread block.
+constexpr int kMaxExperts = 1024;
+
+struct KernelArgs {
+  const void* p_src;        // FWD/DGRAD: W [E,N,K]; WGRAD: X [M,K]
+  const void* q_src;        // FWD: X [M,K]; DGRAD/WGRAD: dY [M,N]
+  const int32_t* offsets;   // [E+1], device
+  void* out;                // FWD: Y [M,N] bf16; DGRAD: dX [M,K] bf16; WGRAD: dW [E,N,K] fp32
+  int64_t M, N, K;
+  int32_t E;
+  int32_t accumulate;       // WGRAD only: add into `out`
+};
+
+// Enqueue one grouped GEMM on stream `s`.  Returns a hipError_t value.
+int launch_grouped(int mode, const KernelArgs& a, int64_t max_m_per_e, hipStream_t s);
+
+}  // namespace mg

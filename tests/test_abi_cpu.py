@@ -1,0 +1,113 @@
+"""The C-ABI library loads and exports every symbol include/mgemm.h declares,
+and its host-side checks reject bad arguments before touching a device (CPU).
+
+No call here reaches the device: every call either fails validation or is a
+no-op (M == 0), which the ABI returns from before any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mgemm.h")
+
+from moe_grouped_gemm_bf16_amd import _lib  # noqa: E402
+
+L = _lib.LIB
+OK, NUL, SHAPE, ALIGN, DEV, LAUNCH, OFFS = range(7)
+A = 0x10000          # a 16-byte-aligned fake address, never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"if", "defined"})
+
+
+def test_header_declares_expected_api():
+    assert declared_functions() == sorted(_lib.SIGNATURES)
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert L.mg_abi_version() == 1
+
+
+def test_status_strings():
+    for s in range(7):
+        assert _lib.status_str(s).startswith("MG_")
+    assert "unknown" in _lib.status_str(99)
+
+
+def _host_check(off, E, M):
+    arr = np.ascontiguousarray(off, dtype=np.int32)
+    return L.mg_check_offsets_host(arr.ctypes.data, E, M)
+
+
+def test_host_offsets_check():
+    assert _host_check([0, 200, 200, 384, 512], 4, 512) == OK
+    assert _host_check([0, 200, 200, 384, 500], 4, 512) == OK      # trailing rows
+    assert _host_check([1, 200, 200, 384, 512], 4, 512) == OFFS    # no leading zero
+    assert _host_check([0, 200, 100, 384, 512], 4, 512) == OFFS    # decreasing
+    assert _host_check([0, 200, 200, 384, 513], 4, 512) == OFFS    # past M
+    assert _host_check([0, 0], 1, 0) == OK
+    assert L.mg_check_offsets_host(None, 4, 512) == NUL
+    assert _host_check([0], 0, 0) == SHAPE
+    assert _host_check([0] * 1026, 1025, 0) == SHAPE
+
+
+@pytest.mark.parametrize("fn", ["mgemm_fwd", "mgemm_dgrad"])
+def test_mgrouped_argument_errors(fn):
+    f = getattr(L, fn)
+    # (x, w, offsets, out, M, N, K, E, max_m_per_e, stream)
+    assert f(A, A, A, A, 512, 128, 256, 0, 0, None) == SHAPE            # E < 1
+    assert f(A, A, A, A, 512, 128, 256, 1025, 0, None) == SHAPE         # E too large
+    assert f(A, A, A, A, -1, 128, 256, 4, 0, None) == SHAPE             # M < 0
+    assert f(A, A, A, A, 512, 100, 256, 4, 0, None) == SHAPE            # N % 8
+    assert f(A, A, A, A, 512, 128, 252, 4, 0, None) == SHAPE            # K % 8
+    assert f(A, A, A, A, 512, 128, 1 << 23, 4, 0, None) == SHAPE        # K too large
+    assert f(A, A, A, A, 512, 128, 256, 4, -1, None) == SHAPE           # bad hint
+    assert f(None, A, A, A, 512, 128, 256, 4, 0, None) == NUL
+    assert f(A, None, A, A, 512, 128, 256, 4, 0, None) == NUL
+    assert f(A, A, None, A, 512, 128, 256, 4, 0, None) == NUL
+    assert f(A, A, A, None, 512, 128, 256, 4, 0, None) == NUL
+    assert f(A + 8, A, A, A, 512, 128, 256, 4, 0, None) == ALIGN
+    assert f(A, A + 2, A, A, 512, 128, 256, 4, 0, None) == ALIGN
+    assert f(A, A, A + 2, A, 512, 128, 256, 4, 0, None) == ALIGN
+    assert f(A, A, A, A + 4, 512, 128, 256, 4, 0, None) == ALIGN
+    # no rows: a valid no-op that never touches the (NULL) buffers or device
+    assert f(None, None, None, None, 0, 128, 256, 4, 0, None) == OK
+
+
+def test_wgrad_argument_errors():
+    f = L.kgemm_wgrad
+    # (dy, x, offsets, dw, M, N, K, E, accumulate, stream)
+    assert f(A, A, A, A, 512, 128, 256, 0, 0, None) == SHAPE
+    assert f(A, A, A, A, 512, 120, 252, 4, 0, None) == SHAPE
+    assert f(A, A, None, A, 512, 128, 256, 4, 0, None) == NUL
+    assert f(A, A, A, None, 512, 128, 256, 4, 0, None) == NUL
+    assert f(None, A, A, A, 512, 128, 256, 4, 0, None) == NUL
+    assert f(A, A, A, A + 8, 512, 128, 256, 4, 0, None) == ALIGN
+    assert f(A + 8, A, A, A, 512, 128, 256, 4, 0, None) == ALIGN
+    assert f(None, None, None, None, 0, 0, 256, 4, 0, None) == OK       # empty dw
+
+
+def test_python_binding_rejects_bad_tensors_on_host():
+    torch = pytest.importorskip("torch")
+    import moe_grouped_gemm_bf16_amd as mg
+    x = torch.zeros(8, 16, dtype=torch.bfloat16)
+    w = torch.zeros(2, 8, 16, dtype=torch.bfloat16)
+    off = torch.tensor([0, 4, 8], dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU"):
+        mg.fwd(x, w, off)
+    with pytest.raises(TypeError):
+        mg.fwd(x.float(), w, off)
+    with pytest.raises(ValueError):
+        mg.fwd(x, w[:, :, :8].contiguous(), off)
+    with pytest.raises(ValueError):
+        mg.Kgemm(x, x, off, descriptor="gw9")

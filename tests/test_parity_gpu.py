@@ -1,0 +1,225 @@
+"""GPU parity of the HIP path against the fp64 oracle (needs an MI355X).
+
+Every case calls the C ABI (through the thin binding) on seeded inputs and
+compares with the oracle on the same bits:
+  * bf16 outputs (fwd, dgrad): within one bf16 ulp of the oracle rounded to
+    bf16, or consistent with fp32 accumulation on cancelling sums (the gate
+    in oracle/gate.py);
+  * fp32 outputs (wgrad): relative Frobenius <= 1e-4 per expert and overall,
+    element-wise accumulation bound, empty experts exactly zero (or exactly
+    the prior contents when accumulating).
+Sizes span several 256-wide tiles with ragged tails; the full-size workloads
+are checked on sampled elements plus properties (determinism, untouched
+rows).
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_grouped_gemm_bf16_amd as mg
+from parity import (SENTINEL, dev_bf16, dev_i32, gate_dgrad_full, gate_dgrad_sampled,
+                    gate_fwd_full, gate_fwd_sampled, gate_wgrad_full, gate_wgrad_sampled,
+                    host_bits, sentinel_bf16)
+from workloads import make_workload, normal_bf16_bits, offsets_from_sizes
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _inputs(sizes, N, K, seed, extra_rows=0, x_scale=None, w_scale=None):
+    off = offsets_from_sizes(sizes)
+    M = int(off[-1]) + extra_rows
+    E = len(sizes)
+    xs = K ** -0.5 if x_scale is None else x_scale
+    ws = K ** -0.5 if w_scale is None else w_scale
+    xb = normal_bf16_bits((M, K), xs, 7000, seed, 1)
+    wb = normal_bf16_bits((E, N, K), ws, 7000, seed, 2)
+    dyb = normal_bf16_bits((M, N), 1.0, 7000, seed, 3)
+    return off, M, E, xb, wb, dyb
+
+
+def _run_mgrouped(off, M, xb, wb, dyb, N, K, hint=0):
+    x, w, dy, o = dev_bf16(xb), dev_bf16(wb), dev_bf16(dyb), dev_i32(off)
+    y = mg.fwd(x, w, o, hint, out=sentinel_bf16((M, N)))
+    dx = mg.dgrad(dy, w, o, hint, out=sentinel_bf16((M, K)))
+    torch.cuda.synchronize()
+    return host_bits(y), host_bits(dx)
+
+
+def _check_untouched(bits, off):
+    assert (bits[int(off[-1]):] == SENTINEL).all(), "rows past offsets[E] were written"
+
+
+# --------------------------------------------------------------- tiny config --
+
+def test_tiny_config_all_three():
+    (wl,) = make_workload(1)
+    _say("tiny", wl.offsets.tolist())
+    xb, wb, dyb = wl.x_bits(), wl.w_bits(), wl.dy_bits()
+    yb, dxb = _run_mgrouped(wl.offsets, wl.M, xb, wb, dyb, wl.N, wl.K)
+    r = gate_fwd_full(xb, wb, wl.offsets, yb); assert r.passed, str(r)
+    r = gate_dgrad_full(dyb, wb, wl.offsets, dxb); assert r.passed, str(r)
+    dw = mg.wgrad(dev_bf16(dyb), dev_bf16(xb), dev_i32(wl.offsets))
+    torch.cuda.synchronize()
+    r = gate_wgrad_full(dyb, xb, wl.offsets, dw.cpu().numpy()); assert r.passed, str(r)
+    assert (dw[1] == 0).all()
+
+
+# --------------------------------------------------------------- fuzz cases --
+
+MG_CASES = [
+    # sizes, N, K, extra rows past offsets[E]
+    ([256], 256, 256, 0),
+    ([1, 255, 256, 257], 264, 136, 5),
+    ([0, 513, 0, 1, 300], 520, 200, 17),
+    ([700, 0, 0], 72, 1032, 3),
+    ([3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14], 8, 8, 0),
+    ([64] * 9, 768, 64, 0),
+]
+
+
+@pytest.mark.parametrize("case", range(len(MG_CASES)))
+def test_mgrouped_fuzz(case):
+    sizes, N, K, extra = MG_CASES[case]
+    _say("mgrouped", sizes, N, K, extra)
+    off, M, E, xb, wb, dyb = _inputs(sizes, N, K, 100 + case, extra)
+    yb, dxb = _run_mgrouped(off, M, xb, wb, dyb, N, K)
+    r = gate_fwd_full(xb, wb, off, yb); assert r.passed, "fwd " + str(r)
+    r = gate_dgrad_full(dyb, wb, off, dxb); assert r.passed, "dgrad " + str(r)
+    _check_untouched(yb, off)
+    _check_untouched(dxb, off)
+
+
+WG_CASES = [
+    ([300, 0, 17, 1, 120], 264, 136),
+    ([64, 63, 65, 128, 0], 256, 256),
+    ([1000], 8, 520),
+    ([0, 0, 2], 136, 8),
+]
+
+
+@pytest.mark.parametrize("case", range(len(WG_CASES)))
+@pytest.mark.parametrize("accumulate", [False, True])
+def test_wgrad_fuzz(case, accumulate):
+    sizes, N, K = WG_CASES[case]
+    _say("wgrad", sizes, N, K, "accumulate" if accumulate else "")
+    off, M, E, xb, wb, dyb = _inputs(sizes, N, K, 200 + case, extra_rows=9,
+                                     x_scale=1.0, w_scale=1.0)
+    prior = None
+    out = None
+    if accumulate:
+        prior = np.random.default_rng(case).standard_normal((E, N, K)).astype(np.float32)
+        out = torch.from_numpy(prior.copy()).cuda()
+    dw = mg.wgrad(dev_bf16(dyb), dev_bf16(xb), dev_i32(off), out=out, accumulate=accumulate)
+    torch.cuda.synchronize()
+    r = gate_wgrad_full(dyb, xb, off, dw.cpu().numpy(),
+                        prior=None if prior is None else prior.astype(np.float64))
+    assert r.passed, str(r)
+
+
+def test_single_expert_is_plain_gemm():
+    off, M, E, xb, wb, dyb = _inputs([777], 392, 328, 300)
+    _say("E=1", M)
+    yb, dxb = _run_mgrouped(off, M, xb, wb, dyb, 392, 328)
+    assert gate_fwd_full(xb, wb, off, yb).passed
+    assert gate_dgrad_full(dyb, wb, off, dxb).passed
+    # and against torch's own fp32 GEMM of the same bf16 values
+    y = dev_bf16(yb).float()
+    ref = dev_bf16(xb).float() @ dev_bf16(wb)[0].float().t()
+    assert torch.allclose(y, ref, rtol=2 ** -7, atol=1e-2)
+
+
+def test_all_experts_empty_and_zero_reduction():
+    off = offsets_from_sizes([0, 0, 0])
+    M, N, K = 40, 64, 64
+    xb = normal_bf16_bits((M, K), 0.1, 1, 1); wb = normal_bf16_bits((3, N, K), 0.1, 1, 2)
+    _say("all empty")
+    yb, dxb = _run_mgrouped(off, M, xb, wb, normal_bf16_bits((M, N), 1.0, 1, 3), N, K)
+    assert (yb == SENTINEL).all() and (dxb == SENTINEL).all()
+    dw = mg.wgrad(dev_bf16(normal_bf16_bits((M, N), 1.0, 1, 3)), dev_bf16(xb), dev_i32(off))
+    prior = torch.full((3, N, K), 2.5, device="cuda")
+    mg.wgrad(dev_bf16(normal_bf16_bits((M, N), 1.0, 1, 3)), dev_bf16(xb), dev_i32(off),
+             out=prior, accumulate=True)
+    torch.cuda.synchronize()
+    assert (dw == 0).all() and (prior == 2.5).all()
+    # K == 0: the forward is an empty sum, the owned rows become zero
+    off2 = offsets_from_sizes([5, 3])
+    x0 = torch.empty((8, 0), dtype=torch.bfloat16, device="cuda")
+    w0 = torch.empty((2, 16, 0), dtype=torch.bfloat16, device="cuda")
+    y0 = mg.fwd(x0, w0, dev_i32(off2), out=sentinel_bf16((10, 16))[:8])
+    torch.cuda.synchronize()
+    assert (y0.float() == 0).all()
+
+
+def test_launch_hint_too_small_is_still_correct():
+    off, M, E, xb, wb, dyb = _inputs([600, 1, 900], 520, 136, 400)
+    _say("hint=1")
+    yb, dxb = _run_mgrouped(off, M, xb, wb, dyb, 520, 136, hint=1)
+    assert gate_fwd_full(xb, wb, off, yb).passed
+    assert gate_dgrad_full(dyb, wb, off, dxb).passed
+
+
+def test_side_stream_and_aliases():
+    off, M, E, xb, wb, dyb = _inputs([130, 0, 260], 264, 264, 500)
+    _say("side stream")
+    x, w, dy, o = dev_bf16(xb), dev_bf16(wb), dev_bf16(dyb), dev_i32(off)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        y = mg.Mgemm(x, w, o, 260, transpose_B=True)
+        dx = mg.Mgemm(dy, w, o, 260, transpose_B=False)
+        dw = mg.Kgemm(dy, x, o, "gw13")
+    s.synchronize()
+    assert gate_fwd_full(xb, wb, off, host_bits(y)).passed
+    assert gate_dgrad_full(dyb, wb, off, host_bits(dx)).passed
+    assert gate_wgrad_full(dyb, xb, off, dw.cpu().numpy()).passed
+
+
+# ------------------------------------------------------ full-size workloads --
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_uniform_workloads_sampled(cfg):
+    (wl,) = make_workload(cfg)
+    _say(wl.name)
+    xb, wb, dyb = wl.x_bits(), wl.w_bits(), wl.dy_bits()
+    x, w, dy, o = dev_bf16(xb), dev_bf16(wb), dev_bf16(dyb), dev_i32(wl.offsets)
+    y1 = host_bits(mg.fwd(x, w, o, 4096))
+    y2 = host_bits(mg.fwd(x, w, o, 4096))
+    dx = host_bits(mg.dgrad(dy, w, o, 4096))
+    dw = mg.wgrad(dy, x, o).cpu().numpy()
+    assert np.array_equal(y1, y2), "fwd is not bitwise reproducible"
+    r = gate_fwd_sampled(xb, wb, wl.offsets, y1); assert r.passed, "fwd " + str(r)
+    r = gate_dgrad_sampled(dyb, wb, wl.offsets, dx); assert r.passed, "dgrad " + str(r)
+    r = gate_wgrad_sampled(dyb, xb, wl.offsets, dw); assert r.passed, "wgrad " + str(r)
+
+
+@pytest.mark.parametrize("name", ["a3b_gate_up", "a3b_down"])
+def test_a3b_router_workload_sampled(name):
+    (wl,) = make_workload(4, name)
+    _say(wl.name, wl.rows)
+    xb, wb, dyb = wl.x_bits(), wl.w_bits(), wl.dy_bits()
+    x, w, dy, o = dev_bf16(xb), dev_bf16(wb), dev_bf16(dyb), dev_i32(wl.offsets)
+    y = host_bits(mg.fwd(x, w, o))
+    dx1 = mg.dgrad(dy, w, o)
+    dx2 = mg.dgrad(dy, w, o)
+    assert torch.equal(dx1.view(torch.int16), dx2.view(torch.int16))
+    r = gate_fwd_sampled(xb, wb, wl.offsets, y); assert r.passed, "fwd " + str(r)
+    r = gate_dgrad_sampled(dyb, wb, wl.offsets, host_bits(dx1)); assert r.passed, "dgrad " + str(r)
+
+
+@pytest.mark.parametrize("name", ["a3b_zipf_gw13", "a3b_zipf_gw2"])
+def test_a3b_zipf_wgrad_sampled(name):
+    (wl,) = make_workload(5, name)
+    _say(wl.name, wl.sizes().tolist())
+    xb, dyb = wl.x_bits(), wl.dy_bits()
+    x, dy, o = dev_bf16(xb), dev_bf16(dyb), dev_i32(wl.offsets)
+    dw = mg.wgrad(dy, x, o)
+    dw2 = mg.wgrad(dy, x, o)
+    assert torch.equal(dw, dw2), "wgrad is not bitwise reproducible"
+    got = dw.cpu().numpy()
+    r = gate_wgrad_sampled(dyb, xb, wl.offsets, got); assert r.passed, str(r)
+    empty = np.flatnonzero(wl.sizes() == 0)
+    assert len(empty) == 4 and (got[empty] == 0).all()
