@@ -1,0 +1,302 @@
+"""Benchmark of the MoE grouped GEMM hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one pass of the whole path over one batch of seeded synthetic
+input: the M-grouped forward Y = X W_e^T, the M-grouped input gradient
+dX = dY W_e and the K-grouped fp32 weight gradient dW_e = dY_e^T X_e, each one
+launch of libmgemm.so.  The default workload is the grouped-GEMM shape of the
+TransformerEngine PR #2045 perf table, (g, m, n, k) = (8, 4096, 768, 2048);
+`--workload a3b` runs one GPU's expert share of the 30B-A3B layout instead
+(router-assigned rows for fwd/dgrad of the gate-up and down GEMMs, the Zipf
+split for both weight gradients).
+
+Prints ONE JSON line: whole-step TFLOP/s (algorithmic flops 2*M*N*K per op,
+M = rows owned by experts), the fraction of the bf16 dense matrix-core peak,
+per-op HIP-event timings, the roofline entry of the dominant kernel and the
+oracle's CPU time on the host's cores.  Inputs are resident in HBM before
+the timed region; nothing is skipped inside it.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0        # MI355X published dense bf16 matrix-core peak
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
+KERNEL_SRC = os.path.join(ROOT, "moe_grouped_gemm_bf16_amd", "csrc", "mgemm_kernels.hip")
+KERNEL_NAMES = {"fwd": "grouped_gemm_kernel<0>", "dgrad": "grouped_gemm_kernel<1>",
+                "wgrad": "grouped_gemm_kernel<2>"}
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="uniform_g8", choices=["uniform_g8", "uniform_g16", "a3b"])
+    p.add_argument("--no-cpu-baseline", action="store_true",
+                   help="skip the oracle timing (used for profiler passes)")
+    p.add_argument("--cold", type=int, default=0,
+                   help="also time each op N times after flushing the caches")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run one plain 1 GiB device copy (for HBM counter calibration)")
+    return p.parse_args()
+
+
+# ------------------------------------------------------------------ workload --
+
+class Op:
+    """One launch of the path: a name, its workload, a launcher and its flops."""
+
+    def __init__(self, name, kind, wl, launch, flops, bytes_):
+        self.name, self.kind, self.wl, self.launch = name, kind, wl, launch
+        self.flops, self.bytes = flops, bytes_
+        self.times_ms = []
+
+
+def build_ops(workload: str, torch, mg):
+    from workloads import make_workload
+
+    def up(bits):
+        import numpy as np
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+    ops, inputs = [], []
+    if workload == "a3b":
+        mg_wls = make_workload(4)          # gate-up and down, router-assigned rows
+        wg_wls = make_workload(5)          # gw13 and gw2, Zipf split
+    else:
+        cfg = 2 if workload == "uniform_g8" else 3
+        mg_wls = make_workload(cfg)
+        wg_wls = mg_wls
+    for wl in mg_wls:
+        x, w, dy = up(wl.x_bits()), up(wl.w_bits()), up(wl.dy_bits())
+        off = torch.from_numpy(wl.offsets).cuda()
+        y = torch.empty((wl.M, wl.N), dtype=torch.bfloat16, device="cuda")
+        dx = torch.empty((wl.M, wl.K), dtype=torch.bfloat16, device="cuda")
+        hint = int(wl.sizes().max())
+        rows = wl.rows
+        ab = 2 * (rows * wl.K + wl.E * wl.N * wl.K + rows * wl.N)   # read X, W; write Y
+        ops.append(Op(f"fwd:{wl.name}", "fwd", wl,
+                      (lambda x=x, w=w, off=off, y=y, h=hint: mg.fwd(x, w, off, h, out=y)),
+                      wl.flops(), ab))
+        ops.append(Op(f"dgrad:{wl.name}", "dgrad", wl,
+                      (lambda dy=dy, w=w, off=off, dx=dx, h=hint: mg.dgrad(dy, w, off, h, out=dx)),
+                      wl.flops(), ab))
+        inputs.append((x, w, dy, off, y, dx))
+    for wl in wg_wls:
+        if workload == "a3b" or "wgrad" in wl.ops:
+            if workload == "a3b":
+                x, dy = up(wl.x_bits()), up(wl.dy_bits())
+                off = torch.from_numpy(wl.offsets).cuda()
+            else:
+                x, _, dy, off, _, _ = inputs[0]
+            dw = torch.empty((wl.E, wl.N, wl.K), dtype=torch.float32, device="cuda")
+            rows = wl.rows
+            ab = 2 * rows * (wl.N + wl.K) + 4 * wl.E * wl.N * wl.K        # read dY, X; write fp32 dW
+            ops.append(Op(f"wgrad:{wl.name}", "wgrad", wl,
+                          (lambda dy=dy, x=x, off=off, dw=dw: mg.wgrad(dy, x, off, out=dw)),
+                          wl.flops(), ab))
+            inputs.append((x, dy, off, dw))
+    return ops, inputs
+
+
+# ------------------------------------------------------------- CPU baseline --
+
+def cpu_baseline(workload: str):
+    """The oracle as it stands, timed on this host's cores over one whole step
+    of the default workload (all three ops, all experts); for the a3b
+    workload, over the gate-up fwd + dgrad of 4 of the 32 experts and the
+    gw13 weight gradient of those experts (a bounded sample)."""
+    import numpy as np
+    from oracle import (bf16_bits_to_f64, f64_to_bf16_bits, grouped_dgrad, grouped_fwd,
+                        grouped_wgrad)
+    from workloads import make_workload
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max(i.get("num_threads", 1) for i in threadpool_info()) if threadpool_info() else 1
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    flops, secs = 0, 0.0
+    if workload == "a3b":
+        wl = make_workload(4, "a3b_gate_up")[0]
+        sel = 4
+        o = wl.offsets
+        rows = int(o[sel])
+        X = bf16_bits_to_f64(wl.x_bits()[:rows]); W = bf16_bits_to_f64(wl.w_bits()[:sel])
+        DY = bf16_bits_to_f64(wl.dy_bits()[:rows]); off = o[:sel + 1]
+        sample = f"gate-up fwd+dgrad+wgrad of experts 0-3 ({rows} rows) of the 30B-A3B share"
+    else:
+        wl = make_workload(2 if workload == "uniform_g8" else 3)[0]
+        X, W, DY = (bf16_bits_to_f64(b) for b in (wl.x_bits(), wl.w_bits(), wl.dy_bits()))
+        off = wl.offsets
+        rows = int(off[-1])
+        sample = f"one whole step (fwd+dgrad+wgrad, all {wl.E} experts) of {wl.name}"
+    E = len(off) - 1
+    t = time.perf_counter()
+    f64_to_bf16_bits(grouped_fwd(X, W, off))
+    f64_to_bf16_bits(grouped_dgrad(DY, W, off))
+    grouped_wgrad(DY, X, off, E).astype(np.float32)
+    secs = time.perf_counter() - t
+    flops = 3 * 2 * rows * wl.N * wl.K
+    return {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle", "sample": sample, "seconds": round(secs, 3)}
+
+
+# -------------------------------------------------------------------- traffic --
+
+def load_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"```json\s*(\{.*?\})\s*```", text, re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("kernel_src_sha256_16") != kernel_hash():
+        return None
+    return rec.get("bytes_per_launch", {}).get(kernel)
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import moe_grouped_gemm_bf16_amd as mg
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    ops, _keep = build_ops(args.workload, torch, mg)
+    print(f"[bench] {args.workload}: {len(ops)} launches per step", file=sys.stderr, flush=True)
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 29, dtype=torch.int16, device="cuda")   # 1 GiB
+        b = torch.empty_like(a)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        for op in ops:
+            op.launch()
+    torch.cuda.synchronize()
+
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in ops] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        for i, op in enumerate(ops):
+            ev[s][i][0].record(stream)
+            op.launch()
+            ev[s][i][1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for s in range(args.steps):
+        for i, op in enumerate(ops):
+            op.times_ms.append(ev[s][i][0].elapsed_time(ev[s][i][1]))
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    step_flops = sum(op.flops for op in ops)
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+
+    per_op = {}
+    for op in ops:
+        avg = statistics.fmean(op.times_ms)
+        per_op[op.name] = {
+            "avg_us": round(avg * 1e3, 2),
+            "median_us": round(statistics.median(op.times_ms) * 1e3, 2),
+            "min_us": round(min(op.times_ms) * 1e3, 2),
+            "tflops": round(op.flops / (avg * 1e-3) / 1e12, 1),
+            "pct_peak": round(100 * op.flops / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 1),
+            "algo_GBps": round(op.bytes / (avg * 1e-3) / 1e9, 1),
+        }
+
+    if args.cold > 0:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        for op in ops:
+            ts = []
+            for _ in range(args.cold):
+                flush.fill_(1)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                op.launch()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            per_op[op.name]["cold_median_us"] = round(statistics.median(ts) * 1e3, 2)
+        del flush
+
+    dom = max(ops, key=lambda o: statistics.fmean(o.times_ms))
+    dom_avg_s = statistics.fmean(dom.times_ms) * 1e-3
+    achieved = dom.flops / dom_avg_s / 1e12
+    traffic = load_traffic(args.workload, dom.name)
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic, "kernel": f"{KERNEL_NAMES[dom.kind]} ({dom.name})",
+                "algorithmic_bytes": dom.bytes}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(args.workload)
+
+    wl0 = ops[0].wl
+    if args.workload == "a3b":
+        config = {"workload": "a3b_expert_share", "experts": 32, "d_model": 3072,
+                  "expert_ffn": 1280, "fwd_dgrad_rows": ops[0].wl.rows,
+                  "wgrad_rows": ops[-1].wl.rows, "ops": [o.name for o in ops]}
+    else:
+        config = {"workload": wl0.name, "g": wl0.E, "m": int(wl0.sizes()[0]), "n": wl0.N,
+                  "k": wl0.K, "ops": [o.name for o in ops]}
+    line = {
+        "metric": "grouped-GEMM TFLOP/s + % bf16 MFMA peak (fwd, dgrad, wgrad), 1 MI355X",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1)-scaled bf16 inputs, see workloads/synth.py)",
+        "config": config,
+        "per_op": per_op,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernel_src_sha256_16": kernel_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
