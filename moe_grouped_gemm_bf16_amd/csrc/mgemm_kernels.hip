@@ -18,17 +18,24 @@
 //   FWD      n  from W[e] [n][k]           m from X [m][k]   k  (both R-contiguous)
 //   DGRAD    k  from W[e] [n][k]           m from dY[m][n]   n  (P is R-strided)
 //   WGRAD    k  from X  [i][k]             n from dY[i][n]   i  (both R-strided)
-// Both operands are staged in LDS as [outer][R] with R contiguous, so a single
-// matrix-core loop serves all three; R-strided operands are transposed in
-// registers (8x8 blocks of bf16) on the way from HBM to LDS.
 //
-// Scheduling: one workgroup per output tile, all experts in one launch.  Each
-// workgroup reads the offsets, derives per-expert tile counts and their prefix
-// sums on the device (no host synchronisation, empty experts give no M-tiles),
-// and decodes its own tile.  M-grouped tiles all cost the same, so they are
-// laid out XCD by XCD (the dispatcher deals workgroups round-robin over the 8
-// XCDs) to keep operand panels in one XCD's L2.  K-grouped tiles cost in
-// proportion to the expert's rows, so they are ordered heaviest expert first.
+// Operand staging: HBM -> LDS by direct-to-LDS buffer loads (no registers),
+// in 4 LDS stages of 32 reduction steps, 3 of them in flight while one is
+// consumed.  R-contiguous operands are staged as [outer][32] rows and read
+// with 128-bit LDS loads; R-strided operands are staged as they lie in HBM,
+// [32][outer], and read with the LDS transpose load (ds_read_b64_tr_b16),
+// which hands each lane 4 consecutive reduction values of one outer index --
+// the transposes wgrad and dgrad need are done by the LDS read, not by a pass.
+// Buffer descriptors whose range ends at the last valid byte make ragged
+// rows, reduction tails and out-of-range columns arrive in LDS as zeros.
+//
+// Scheduling: all experts in one launch.  Each workgroup reads the offsets,
+// derives per-expert tile counts and their prefix sums on the device (no host
+// synchronisation, empty experts give no M-tiles) and loops over its tiles.
+// M-grouped tiles all cost the same, so they are laid out XCD by XCD (the
+// dispatcher deals workgroups round-robin over the 8 XCDs) to keep operand
+// panels in one XCD's L2.  K-grouped tiles cost in proportion to the expert's
+// rows, so they are ordered heaviest expert first.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -37,132 +44,93 @@
 namespace mg {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int kBP = 256;           // tile extent along P
-constexpr int kBQ = 256;           // tile extent along Q
-constexpr int kBK = 64;            // reduction slice per stage
-constexpr int kThreads = 512;      // 8 waves: 2 along P x 4 along Q
-constexpr int kWavesP = 2;
-constexpr int kWavesQ = 4;
-constexpr int kWaveP = kBP / kWavesP;   // 128
-constexpr int kWaveQ = kBQ / kWavesQ;   // 64
-constexpr int kBlkP = kWaveP / 32;      // 4 matrix-core blocks of 32 along P
-constexpr int kBlkQ = kWaveQ / 32;      // 2 along Q
-constexpr int kTileBytes = kBP * kBK * 2;          // one operand stage: 32 KiB
-constexpr int kLdsBytes = 4 * kTileBytes;          // 2 operands x 2 stages
-constexpr uint32_t kOOB = 0x80000000u;             // offset bit past any range
+constexpr int kBK = 32;                  // reduction steps per LDS stage
+constexpr int kStages = 4;               // LDS stages (kStages - 1 in flight)
+constexpr uint32_t kOOB = 0x80000000u;   // offset bit past any buffer range
 
-static_assert(kBP == 256 && kBQ == 256 && kBK == 64, "loaders assume 256x256x64");
+// Tile configuration: BP x BQ output tile, WP x WQ waves, each wave owning a
+// (BP/WP) x (BQ/WQ) sub-tile of 32x32 matrix-core blocks.
+template <int BP_, int BQ_, int WP_, int WQ_>
+struct TileCfg {
+  static constexpr int BP = BP_, BQ = BQ_, WP = WP_, WQ = WQ_;
+  static constexpr int NW = WP * WQ, NT = 64 * NW;
+  static constexpr int WTP = BP / WP, WTQ = BQ / WQ;
+  static constexpr int MP = WTP / 32, MQ = WTQ / 32;
+  static constexpr int P_BYTES = BP * kBK * 2, Q_BYTES = BQ * kBK * 2;
+  static constexpr int STAGE = P_BYTES + Q_BYTES;
+  static constexpr int LDS = kStages * STAGE;
+  static constexpr int SEGS = STAGE / 1024;          // 1 KiB direct-to-LDS loads per stage
+  static constexpr int SEGS_P = P_BYTES / 1024;
+  static constexpr int SEGS_PER_WAVE = SEGS / NW;
+  static_assert(WTP % 32 == 0 && WTQ % 32 == 0, "wave tile must be 32-aligned");
+  static_assert(SEGS % NW == 0 && SEGS_P % SEGS_PER_WAVE == 0, "segments per wave");
+  static_assert(LDS <= 160 * 1024 - 16 * 1024, "LDS budget");
+};
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  // raw buffer: stride 0, range `bytes`; loads past the range return zero.
-  // Base and range are wave-uniform; say so, so that the descriptor lives in
-  // scalar registers.
+// 128-bit raw buffer descriptor: base, stride 0, range `bytes`.  Loads past
+// the range return zero.  All inputs are wave-uniform.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
   const uint64_t b = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
-  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
-  void* p = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)n, 0x00020000);
+  i32x4 r;
+  r.x = (int32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  r.y = (int32_t)(__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) & 0xFFFFu);
+  r.z = (int32_t)__builtin_amdgcn_readfirstlane(bytes);
+  r.w = 0x00020000;
+  return r;
 }
 
-__device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+// Direct-to-LDS 16-byte load: lane l's 16 bytes land at LDS byte address
+// lds_addr + 16 l (lds_addr wave-uniform).  Issued as inline assembly so that
+// the compiler does not serialise it against the LDS reads of other stages;
+// completion is awaited explicitly with vmcnt before the stage's barrier.
+__device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t lds_addr, uint32_t voff) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "s"(lds_addr), "v"(voff), "s"(rsrc)
+      : "memory");
 }
 
-// LDS layout of one operand stage: 256 rows (outer index) x 64 bf16 (R), 128 B
-// per row, in 16-byte chunks whose position is XOR-swizzled by row bits 0-2
-// and 3-5.  Matrix-core reads (32 consecutive rows, one chunk) and the
-// transposed writes (rows 8 apart) both land on distinct banks.
-__device__ __forceinline__ uint32_t lds_off(int row, int chunk) {
-  int sw = (row ^ (row >> 3)) & 7;
-  return (uint32_t)(row * 128 + ((chunk ^ sw) << 4));
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// ---------------------------------------------------------------- loaders --
-// Each loader is run by 256 threads (one half of the workgroup, `lt` in
-// 0..255) and fetches one 256 x 64 operand stage into 8 x 16 bytes/thread.
-
-// R-contiguous source: rows 0..255 from `base` (row stride ld elements), R
-// columns [r0, r0 + 64).  Rows >= nrows and columns >= r_end read as zero.
-__device__ __forceinline__ void load_rc(u32x4 (&v)[8], const uint16_t* base, int ld, int nrows,
-                                        int r0, int r_end, int lt) {
-  const int rows = nrows < kBP ? (nrows > 0 ? nrows : 0) : kBP;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, (uint32_t)rows * (uint32_t)ld * 2u);
-  const int c = lt & 7;
-  const int rc = r0 + c * 8;
-  // a chunk past the reduction end gets an offset past any range (bit 31 set;
-  // ranges are below 2^31 bytes), so it reads as zero
-  const uint32_t oob = rc < r_end ? 0u : kOOB;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int row = (lt >> 3) + 32 * j;
-    v[j] = bload(rs, ((uint32_t)(row * ld + rc) * 2u) | oob);
-  }
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(
+      (const __attribute__((address_space(3))) void*)p);
 }
 
-__device__ __forceinline__ void store_rc(char* lds, const u32x4 (&v)[8], int lt) {
-  const int c = lt & 7;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int row = (lt >> 3) + 32 * j;
-    *reinterpret_cast<u32x4*>(lds + lds_off(row, c)) = v[j];
-  }
-}
-
-// R-strided source: R rows [0, 64) from `base` (row stride ld elements), outer
-// columns 0..255.  R rows >= nred and outer columns >= nouter read as zero;
-// the buffer range ends exactly at the last valid element, so no byte outside
-// the rows' valid columns is ever addressed.  Thread lt owns the 8x8 block
-// (R rows 8*(lt>>5) .. +7) x (outer 8*(lt&31) .. +7).
-__device__ __forceinline__ void load_rs(u32x4 (&v)[8], const uint16_t* base, int ld, int nred,
-                                        int nouter, int lt) {
-  const int rr = nred < kBK ? (nred > 0 ? nred : 0) : kBK;
-  const int oc = nouter < kBP ? nouter : kBP;
-  const uint32_t bytes = rr > 0 && oc > 0 ? ((uint32_t)(rr - 1) * (uint32_t)ld + (uint32_t)oc) * 2u : 0u;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, bytes);
-  const int ob = lt & 31, rb = lt >> 5;
-  const uint32_t oob = ob * 8 < oc ? 0u : kOOB;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t off = ((uint32_t)((rb * 8 + j) * ld + ob * 8) * 2u) | oob;
-    v[j] = bload(rs, off);
-  }
-}
-
-// Transpose the 8x8 bf16 block in registers and write it as 8 LDS rows
-// (outer 8*ob + c) holding R chunk rb.
-__device__ __forceinline__ void store_rs(char* lds, const u32x4 (&v)[8], int lt) {
-  const int ob = lt & 31, rb = lt >> 5;
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const int d = c >> 1;
-    u32x4 o;
-    if ((c & 1) == 0) {
-      o.x = __builtin_amdgcn_perm(v[1][d], v[0][d], 0x05040100u);
-      o.y = __builtin_amdgcn_perm(v[3][d], v[2][d], 0x05040100u);
-      o.z = __builtin_amdgcn_perm(v[5][d], v[4][d], 0x05040100u);
-      o.w = __builtin_amdgcn_perm(v[7][d], v[6][d], 0x05040100u);
-    } else {
-      o.x = __builtin_amdgcn_perm(v[1][d], v[0][d], 0x07060302u);
-      o.y = __builtin_amdgcn_perm(v[3][d], v[2][d], 0x07060302u);
-      o.z = __builtin_amdgcn_perm(v[5][d], v[4][d], 0x07060302u);
-      o.w = __builtin_amdgcn_perm(v[7][d], v[6][d], 0x07060302u);
-    }
-    *reinterpret_cast<u32x4*>(lds + lds_off(ob * 8 + c, rb)) = o;
-  }
-}
+// LDS layouts of one stage (byte offsets within an operand tile):
+//  R-contiguous tile [outer][32]: 64 B rows of 4 chunks of 16 B; chunk c of
+//    row r sits at chunk c ^ rc_swz(r).  32 consecutive rows read at one chunk
+//    hit distinct banks in groups of 8 or 16 lanes.
+//  R-strided tile [32][outer]: rows of outer*2 bytes in 16-B chunks; chunk c
+//    of reduction row r sits at c ^ rs_swz(r % 4).  A transpose load touches
+//    4 rows x 2 chunks per 16 lanes (4 chunks per 32 lanes), all distinct.
+__device__ __forceinline__ int rc_swz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
+__device__ __forceinline__ int rs_swz(int r4) { return (0xCA60 >> (4 * r4)) & 15; }  // 0,6,10,12
 
 // ------------------------------------------------------------- scheduler --
 
 // Exclusive prefix sum over the block of per-thread values; returns the
 // thread's exclusive prefix and writes the block total to *total.
+template <int NT>
 __device__ __forceinline__ int block_exclusive_scan(int x, int* scratch, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int incl = x;
@@ -175,7 +143,7 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int* scratch, int* to
   __syncthreads();
   int before = 0, all = 0;
 #pragma unroll
-  for (int w = 0; w < kThreads / 64; ++w) {
+  for (int w = 0; w < NT / 64; ++w) {
     int s = scratch[w];
     before += (w < wave) ? s : 0;
     all += s;
@@ -202,8 +170,6 @@ struct Sched {
   int total;    // number of tiles
 };
 
-// M-grouped set-up: tiles are, for every expert, ceil(m_e / BQ) M-tiles times
-// tilesP P-tiles; empty experts contribute none.
 // Offsets are read clamped to [0, M] and made non-decreasing per expert, so
 // that even offsets breaking the documented precondition cannot move any read
 // or write outside the tensors (the results are then meaningless, not unsafe).
@@ -212,9 +178,12 @@ __device__ __forceinline__ int clamp_off(const int32_t* offsets, int i, int M) {
   return o < 0 ? 0 : (o > M ? M : o);
 }
 
+// M-grouped set-up: tiles are, for every expert, ceil(m_e / BQ) M-tiles times
+// tilesP P-tiles; empty experts contribute none.
+template <int NT, int BQ>
 __device__ void setup_mgrouped(const int32_t* __restrict__ offsets, int E, int M, int tilesP,
                                Sched& S) {
-  constexpr int kPer = kMaxExperts / kThreads;
+  constexpr int kPer = (kMaxExperts + NT - 1) / NT;
   const int e0 = threadIdx.x * kPer;
   int cnt[kPer];
   int mine = 0;
@@ -228,12 +197,12 @@ __device__ void setup_mgrouped(const int32_t* __restrict__ offsets, int E, int M
       S.offs[e] = lo;
       if (e == E - 1) S.offs[E] = hi;
       const int m = hi - lo;
-      cnt[j] = m > 0 ? (m + kBQ - 1) / kBQ : 0;
+      cnt[j] = m > 0 ? (m + BQ - 1) / BQ : 0;
       mine += cnt[j];
     }
   }
   int mtiles;
-  int run = block_exclusive_scan(mine, S.scan, &mtiles);
+  int run = block_exclusive_scan<NT>(mine, S.scan, &mtiles);
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int e = e0 + j;
@@ -250,6 +219,7 @@ __device__ void setup_mgrouped(const int32_t* __restrict__ offsets, int E, int M
 // XCD by XCD: XCD x owns a contiguous range of tile ids, so tiles that run
 // together on one XCD share operand panels in its L2.  Within the range, the
 // P-tile index runs fastest.  Returns false once v is past this XCD's range.
+template <int BP, int BQ>
 __device__ __forceinline__ bool tile_mgrouped(int v, int E, int tilesP, int red,
                                               const Sched& S, Tile& t) {
   const int T = S.total;
@@ -266,9 +236,9 @@ __device__ __forceinline__ bool tile_mgrouped(int v, int E, int tilesP, int red,
     if (S.pref[mid] <= mt) lo = mid; else hi = mid - 1;
   }
   t.e = lo;
-  t.q0 = S.offs[lo] + (mt - S.pref[lo]) * kBQ;
+  t.q0 = S.offs[lo] + (mt - S.pref[lo]) * BQ;
   t.q_end = max(S.offs[lo + 1], S.offs[lo]);
-  t.p0 = tp * kBP;
+  t.p0 = tp * BP;
   t.r_begin = 0;
   t.r_end = red;
   return true;
@@ -277,11 +247,12 @@ __device__ __forceinline__ bool tile_mgrouped(int v, int E, int tilesP, int red,
 // K-grouped set-up: every expert has tilesQ x tilesP tiles whose cost grows
 // with its row count; experts are ranked heaviest first (ties: lower index
 // first) so that long reductions start early and short ones fill the tail.
+template <int NT>
 __device__ void setup_kgrouped(const int32_t* __restrict__ offsets, int E, int M, int per,
                                Sched& S) {
-  for (int e = threadIdx.x; e <= E; e += kThreads) S.offs[e] = clamp_off(offsets, e, M);
+  for (int e = threadIdx.x; e <= E; e += NT) S.offs[e] = clamp_off(offsets, e, M);
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kThreads) {
+  for (int e = threadIdx.x; e < E; e += NT) {
     const int me = max(S.offs[e + 1] - S.offs[e], 0);
     int rank = 0;
     for (int f = 0; f < E; ++f) {
@@ -294,6 +265,7 @@ __device__ void setup_kgrouped(const int32_t* __restrict__ offsets, int E, int M
   S.total = E * per;
 }
 
+template <int BP, int BQ>
 __device__ __forceinline__ bool tile_kgrouped(int v, int tilesP, int per, const Sched& S,
                                               Tile& t) {
   if (v >= S.total) return false;
@@ -301,8 +273,8 @@ __device__ __forceinline__ bool tile_kgrouped(int v, int tilesP, int per, const 
   const int e = S.inv[rank];
   const int tq = w / tilesP, tp = w - tq * tilesP;
   t.e = e;
-  t.q0 = tq * kBQ;
-  t.p0 = tp * kBP;
+  t.q0 = tq * BQ;
+  t.p0 = tp * BP;
   t.r_begin = S.offs[e];
   t.r_end = max(S.offs[e + 1], S.offs[e]);
   t.q_end = 0x7FFFFFFF;
@@ -311,9 +283,38 @@ __device__ __forceinline__ bool tile_kgrouped(int v, int tilesP, int per, const 
 
 // ------------------------------------------------------------------ kernel --
 
-template <int MODE>
+// Fragment reads.  A 32x32x16 matrix-core operand gives lane l the 8
+// reduction values 8*(l/32) + 0..7 of outer index l % 32 (within one k-slice
+// of 16).  Both operands use the same assignment, so the products pair up.
+
+// R-contiguous tile [outer][32] (64-byte rows): one 128-bit read.
+__device__ __forceinline__ bf16x8 frag_rc(const char* tile, uint32_t off) {
+  return *reinterpret_cast<const bf16x8*>(tile + off);
+}
+
+// R-strided tile [32][outer]: two transpose loads of 4 reduction rows each.
+// Within each 16-lane group, lane i's element j comes from the 8-byte word
+// addressed by lane 4j + i/4, element i % 4; so lane i addresses row
+// R0 + i/4, outer columns o0 + 4 (i % 4) .. +3, and receives column o0 + i of
+// rows R0 .. R0 + 3.
+__device__ __forceinline__ bf16x8 frag_rs(const char* tile, uint32_t off, uint32_t off4) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)((__attribute__((address_space(3))) char*)(
+                       (__attribute__((address_space(3))) void*)tile) + off));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)((__attribute__((address_space(3))) char*)(
+                       (__attribute__((address_space(3))) void*)tile) + off + off4));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+template <int MODE, class C>
 __device__ __forceinline__ void run_tile(const KernelArgs& a, const Tile& t, char* lds,
                                          int Pdim, int Qdim) {
+  constexpr bool P_RS = MODE != kFwd;      // P is R-strided for dgrad and wgrad
+  constexpr bool Q_RS = MODE == kWgrad;    // Q is R-strided for wgrad
+  constexpr int SPW = C::SEGS_PER_WAVE;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
 
@@ -336,86 +337,149 @@ __device__ __forceinline__ void run_tile(const KernelArgs& a, const Tile& t, cha
   }
   const int red_len = t.r_end - t.r_begin;
   const int nk = (red_len + kBK - 1) / kBK;
-  const int nrowsP = Pdim - t.p0;              // valid P rows (R-contiguous) or columns
-  const int nrowsQ = t.q_end - t.q0;           // for R-contiguous Q (M-grouped)
+  const int nP = Pdim - t.p0;                  // valid P rows (R-contiguous) or columns
+  const int nQ = MODE == kWgrad ? Qdim - t.q0 : t.q_end - t.q0;
 
-  const bool loadsP = wave < 4;                // waves 0-3 stage P, 4-7 stage Q
-  const int lt = tid & 255;
-  // stage s: P at s * 2 * kTileBytes, Q right after it
+  // ---- direct-to-LDS plan: each stage is C::SEGS 1-KiB segments (the P tile
+  // first, then the Q tile); wave w loads segments w*SPW .. w*SPW + SPW - 1.
+  const bool wP = wave * SPW < C::SEGS_P;                    // wave-uniform
+  const bool rs = wP ? P_RS : Q_RS;
+  const int outer = wP ? C::BP : C::BQ;
+  const int nouter = wP ? nP : nQ;
+  const int ld = wP ? ldP : ldQ;
+  const uint16_t* src = wP ? P : Q;
+  const int seg0 = wP ? wave * SPW : wave * SPW - C::SEGS_P;
+  const uint32_t lds_base = lds_u32(lds) + (wP ? 0u : (uint32_t)C::P_BYTES) + seg0 * 1024u;
+  uint32_t voff[SPW];
+  int col[SPW];
+#pragma unroll
+  for (int j = 0; j < SPW; ++j) {
+    const int p = (seg0 + j) * 1024 + lane * 16;             // byte within the tile
+    if (rs) {                                                // [32][outer]
+      const int r = p / (outer * 2), pc = (p >> 4) % (outer / 8);
+      const int c = pc ^ rs_swz(r & 3);
+      voff[j] = ((uint32_t)(r * ld + 8 * c) * 2u) | (8 * c < nouter ? 0u : kOOB);
+      col[j] = 0;
+    } else {                                                 // [outer][32]
+      const int row = p >> 6, pc = (p >> 4) & 3;
+      const int c = pc ^ rc_swz(row);
+      voff[j] = (uint32_t)(row * ld + 8 * c) * 2u;
+      col[j] = 8 * c;
+    }
+  }
+  const i32x4 rc_rsrc =
+      make_rsrc(src, (uint32_t)(nouter < outer ? (nouter > 0 ? nouter : 0) : outer) * (uint32_t)ld * 2u);
 
-  u32x4 v[8];
-  auto gload = [&](int kt) {
+  auto issue = [&](int stage, int kt) {
     const int r0 = kt * kBK;
-    if (loadsP) {
-      if (MODE == kFwd) load_rc(v, P, ldP, nrowsP, r0, red_len, lt);
-      else load_rs(v, P + (int64_t)r0 * ldP, ldP, red_len - r0, nrowsP, lt);
+    const uint32_t dst = lds_base + (uint32_t)(stage * C::STAGE);
+    if (rs) {
+      const int rr = min(red_len - r0, kBK), oc = min(nouter, outer);
+      const uint32_t bytes = rr > 0 && oc > 0 ? ((uint32_t)(rr - 1) * ld + oc) * 2u : 0u;
+      const i32x4 rsrc = make_rsrc(src + (int64_t)r0 * ld, bytes);
+#pragma unroll
+      for (int j = 0; j < SPW; ++j) dma16(rsrc, dst + j * 1024u, voff[j]);
     } else {
-      if (MODE == kWgrad) load_rs(v, Q + (int64_t)r0 * ldQ, ldQ, red_len - r0, Qdim - t.q0, lt);
-      else load_rc(v, Q, ldQ, nrowsQ, r0, red_len, lt);
+#pragma unroll
+      for (int j = 0; j < SPW; ++j)
+        dma16(rc_rsrc, dst + j * 1024u,
+              (voff[j] + (uint32_t)r0 * 2u) | (r0 + col[j] < red_len ? 0u : kOOB));
     }
   };
-  auto lstore = [&](int buf) {
-    char* base = lds + buf * (2 * kTileBytes) + (loadsP ? 0 : kTileBytes);
-    if (loadsP ? MODE == kFwd : MODE != kWgrad) store_rc(base, v, lt);
-    else store_rs(base, v, lt);
+
+  // ---- fragment addresses (byte offsets within an operand tile)
+  const int wp = wave / C::WQ, wq = wave % C::WQ;
+  const int l32 = lane & 31, h = lane >> 5, L = lane & 15, g16 = (lane >> 4) & 1;
+  uint32_t offP[P_RS ? C::MP : 2], offQ[Q_RS ? C::MQ : 2];
+  // R-contiguous: row = base + 32 i + l32 (swizzle depends on l32 only),
+  // chunk 2 kk + h; entry kk, then + 2048 i.
+  // R-strided: row 8 h + L/4 (+ 16 kk + 4 t), outer base + 32 i + 16 g16 + 4 (L % 4).
+  auto rs_off = [&](int obase, int i, int outer_) {
+    const int o = obase + 32 * i + 16 * g16 + 4 * (L & 3);
+    const int r = 8 * h + (L >> 2);
+    return (uint32_t)(r * outer_ * 2 + (((o >> 3) ^ rs_swz(L >> 2)) << 4) + 8 * (L & 1));
   };
-
-  f32x16 acc[kBlkP][kBlkQ];
+  auto rc_off = [&](int obase, int kk) {
+    const int row = obase + l32;
+    return (uint32_t)(row * 64 + (((2 * kk + h) ^ rc_swz(l32)) << 4));
+  };
+  if (P_RS) {
 #pragma unroll
-  for (int i = 0; i < kBlkP; ++i)
-#pragma unroll
-    for (int j = 0; j < kBlkQ; ++j) acc[i][j] = f32x16{};
-
-  const int wp = wave / kWavesQ, wq = wave % kWavesQ;
-  const int lrow = lane & 31, lhalf = lane >> 5;
-
-  if (nk > 0) {
-    gload(0);
-    lstore(0);
-    __syncthreads();
+    for (int i = 0; i < C::MP; ++i) offP[i] = rs_off(wp * C::WTP, i, C::BP);
+  } else {
+    offP[0] = rc_off(wp * C::WTP, 0); offP[1] = rc_off(wp * C::WTP, 1);
   }
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const char* sp = lds + cur * (2 * kTileBytes);
-    const char* sq = sp + kTileBytes;
+  if (Q_RS) {
+#pragma unroll
+    for (int j = 0; j < C::MQ; ++j) offQ[j] = rs_off(wq * C::WTQ, j, C::BQ);
+  } else {
+    offQ[0] = rc_off(wq * C::WTQ, 0); offQ[1] = rc_off(wq * C::WTQ, 1);
+  }
+
+  f32x16 acc[C::MP][C::MQ];
+#pragma unroll
+  for (int i = 0; i < C::MP; ++i)
+#pragma unroll
+    for (int j = 0; j < C::MQ; ++j) acc[i][j] = f32x16{};
+
+  auto compute = [&](int stage) {
+    const char* tp = lds + stage * C::STAGE;
+    const char* tq = tp + C::P_BYTES;
+    bf16x8 fp[2][C::MP], fq[2][C::MQ];
 #pragma unroll
     for (int kk = 0; kk < kBK / 16; ++kk) {
-      const int chunk = kk * 2 + lhalf;
-      bf16x8 fp[kBlkP], fq[kBlkQ];
 #pragma unroll
-      for (int i = 0; i < kBlkP; ++i)
-        fp[i] = *reinterpret_cast<const bf16x8*>(sp + lds_off(wp * kWaveP + i * 32 + lrow, chunk));
+      for (int i = 0; i < C::MP; ++i)
+        fp[kk][i] = P_RS ? frag_rs(tp, offP[i] + kk * 16 * C::BP * 2, 4 * C::BP * 2)
+                         : frag_rc(tp, offP[kk] + i * 2048);
 #pragma unroll
-      for (int j = 0; j < kBlkQ; ++j)
-        fq[j] = *reinterpret_cast<const bf16x8*>(sq + lds_off(wq * kWaveQ + j * 32 + lrow, chunk));
-#pragma unroll
-      for (int i = 0; i < kBlkP; ++i)
-#pragma unroll
-        for (int j = 0; j < kBlkQ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp[i], fq[j], acc[i][j], 0, 0, 0);
-      // keep each k-slice's fragment reads next to its own products (bounds
-      // the fragment registers live at once)
-      __builtin_amdgcn_sched_barrier(0);
+      for (int j = 0; j < C::MQ; ++j)
+        fq[kk][j] = Q_RS ? frag_rs(tq, offQ[j] + kk * 16 * C::BQ * 2, 4 * C::BQ * 2)
+                         : frag_rc(tq, offQ[kk] + j * 2048);
     }
-    if (kt + 1 < nk) lstore(cur ^ 1);
-    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk)
+#pragma unroll
+      for (int i = 0; i < C::MP; ++i)
+#pragma unroll
+        for (int j = 0; j < C::MQ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp[kk][i], fq[kk][j], acc[i][j],
+                                                              0, 0, 0);
+  };
+
+  // ---- pipeline: stage kt lives in LDS buffer kt % kStages; while it is
+  // consumed, stages kt+1 .. kt+kStages-1 are in flight.
+  __syncthreads();                     // the previous tile's readers are done
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s)
+    if (s < nk) issue(s, s);
+  for (int kt = 0; kt < nk; ++kt) {
+    // this wave's loads of stage kt are done once at most the loads of the
+    // stages issued after it are outstanding
+    const int after = min(kStages - 2, nk - 1 - kt);
+    if (after >= 2) wait_vmcnt<2 * SPW>();
+    else if (after == 1) wait_vmcnt<SPW>();
+    else wait_vmcnt<0>();
+    __syncthreads();                   // every wave's part of stage kt is in LDS,
+                                       // and stage kt-1's buffer is free
+    if (kt + kStages - 1 < nk) issue((kt + kStages - 1) % kStages, kt + kStages - 1);
+    compute(kt % kStages);
   }
 
-  // ---- epilogue.  Result block (i, j): lane holds Q index lrow and P indices
-  // 8*g + 4*lhalf + 0..3 for g = 0..3 (accumulator registers 4g..4g+3).
+  // ---- epilogue.  Result block (i, j): lane holds Q index l32 and P indices
+  // 8*g + 4*h + 0..3 for g = 0..3 (accumulator registers 4g..4g+3).
   if (MODE == kWgrad) {
     float* out = reinterpret_cast<float*>(a.out) + (int64_t)t.e * a.N * a.K;
 #pragma unroll
-    for (int j = 0; j < kBlkQ; ++j) {
-      const int n = t.q0 + wq * kWaveQ + j * 32 + lrow;
+    for (int j = 0; j < C::MQ; ++j) {
+      const int n = t.q0 + wq * C::WTQ + j * 32 + l32;
       if (n >= Qdim) continue;
       float* orow = out + (int64_t)n * a.K;
 #pragma unroll
-      for (int i = 0; i < kBlkP; ++i) {
+      for (int i = 0; i < C::MP; ++i) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int k = t.p0 + wp * kWaveP + i * 32 + g * 8 + lhalf * 4;
+          const int k = t.p0 + wp * C::WTP + i * 32 + g * 8 + h * 4;
           if (k >= Pdim) continue;
           f32x4 r = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
                      acc[i][j][4 * g + 3]};
@@ -429,15 +493,15 @@ __device__ __forceinline__ void run_tile(const KernelArgs& a, const Tile& t, cha
     uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
     const int ldo = Pdim;
 #pragma unroll
-    for (int j = 0; j < kBlkQ; ++j) {
-      const int m = t.q0 + wq * kWaveQ + j * 32 + lrow;
+    for (int j = 0; j < C::MQ; ++j) {
+      const int m = t.q0 + wq * C::WTQ + j * 32 + l32;
       if (m >= t.q_end) continue;
       uint16_t* orow = out + (int64_t)m * ldo;
 #pragma unroll
-      for (int i = 0; i < kBlkP; ++i) {
+      for (int i = 0; i < C::MP; ++i) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int c = t.p0 + wp * kWaveP + i * 32 + g * 8 + lhalf * 4;
+          const int c = t.p0 + wp * C::WTP + i * 32 + g * 8 + h * 4;
           if (c >= Pdim) continue;
           bf16x2 lo = __builtin_convertvector(
               (f32x2){acc[i][j][4 * g], acc[i][j][4 * g + 1]}, bf16x2);
@@ -451,9 +515,10 @@ __device__ __forceinline__ void run_tile(const KernelArgs& a, const Tile& t, cha
   }
 }
 
-template <int MODE>
-__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+template <int MODE, class C>
+__global__ __launch_bounds__(C::NT)
+void grouped_gemm_kernel(KernelArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[C::LDS];
   __shared__ int sched[16 + 2 * (kMaxExperts + 1) + kMaxExperts];
 
   int Pdim, Qdim;
@@ -464,22 +529,23 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs a)
   } else {
     Pdim = (int)a.K; Qdim = (int)a.N;
   }
-  const int tilesP = (Pdim + kBP - 1) / kBP;
-  const int tilesQ = (Qdim + kBQ - 1) / kBQ;
+  const int tilesP = (Pdim + C::BP - 1) / C::BP;
+  const int tilesQ = (Qdim + C::BQ - 1) / C::BQ;
   const int E = a.E;
   Sched S;
   S.scan = sched;
   S.pref = sched + 16;
   S.offs = S.pref + (E + 1);
   S.inv = S.offs + (E + 1);
-  if (MODE == kWgrad) setup_kgrouped(a.offsets, E, (int)a.M, tilesQ * tilesP, S);
-  else setup_mgrouped(a.offsets, E, (int)a.M, tilesP, S);
+  if (MODE == kWgrad) setup_kgrouped<C::NT>(a.offsets, E, (int)a.M, tilesQ * tilesP, S);
+  else setup_mgrouped<C::NT, C::BQ>(a.offsets, E, (int)a.M, tilesP, S);
   const int red = MODE == kFwd ? (int)a.K : (int)a.N;
 
   for (int v = blockIdx.x;; v += gridDim.x) {
     Tile t;
-    const bool have = MODE == kWgrad ? tile_kgrouped(v, tilesP, tilesQ * tilesP, S, t)
-                                     : tile_mgrouped(v, E, tilesP, red, S, t);
+    const bool have = MODE == kWgrad
+                          ? tile_kgrouped<C::BP, C::BQ>(v, tilesP, tilesQ * tilesP, S, t)
+                          : tile_mgrouped<C::BP, C::BQ>(v, E, tilesP, red, S, t);
     if (!have) break;
     t.e = __builtin_amdgcn_readfirstlane(t.e);
     t.q0 = __builtin_amdgcn_readfirstlane(t.q0);
@@ -487,39 +553,38 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs a)
     t.p0 = __builtin_amdgcn_readfirstlane(t.p0);
     t.r_begin = __builtin_amdgcn_readfirstlane(t.r_begin);
     t.r_end = __builtin_amdgcn_readfirstlane(t.r_end);
-    run_tile<MODE>(a, t, lds, Pdim, Qdim);
+    run_tile<MODE, C>(a, t, lds, Pdim, Qdim);
   }
 }
+
 
 // ------------------------------------------------------------ host launch --
 
-static int tiles_upper_bound_m(int64_t M, int E, int64_t max_m_per_e, int tilesP) {
-  int64_t mt = (M + kBQ - 1) / kBQ + E;             // sum_e ceil(m_e/BQ) <= this
-  if (max_m_per_e > 0) {
-    int64_t alt = (int64_t)E * ((max_m_per_e + kBQ - 1) / kBQ);
-    if (alt < mt) mt = alt;
-  }
-  return (int)(mt * tilesP);
-}
+using Cfg = TileCfg<256, 256, 2, 4>;    // 8 waves (2 per SIMD), 128x64 per wave
 
 int launch_grouped(int mode, const KernelArgs& a, int64_t max_m_per_e, hipStream_t s) {
   int grid;
   if (mode == kWgrad) {
-    const int tilesP = (int)((a.K + kBP - 1) / kBP), tilesQ = (int)((a.N + kBQ - 1) / kBQ);
+    const int tilesP = (int)((a.K + Cfg::BP - 1) / Cfg::BP);
+    const int tilesQ = (int)((a.N + Cfg::BQ - 1) / Cfg::BQ);
     grid = a.E * tilesQ * tilesP;
   } else {
-    // a multiple of 8 so that every virtual id a workgroup visits stays on its XCD
     const int64_t Pdim = mode == kFwd ? a.N : a.K;
-    const int tilesP = (int)((Pdim + kBP - 1) / kBP);
-    grid = tiles_upper_bound_m(a.M, a.E, max_m_per_e, tilesP);
-    grid = (grid + 7) & ~7;
+    const int tilesP = (int)((Pdim + Cfg::BP - 1) / Cfg::BP);
+    int64_t mt = (a.M + Cfg::BQ - 1) / Cfg::BQ + a.E;       // sum_e ceil(m_e/BQ) <= this
+    if (max_m_per_e > 0) {
+      const int64_t alt = (int64_t)a.E * ((max_m_per_e + Cfg::BQ - 1) / Cfg::BQ);
+      if (alt < mt) mt = alt;
+    }
+    // a multiple of 8 so that every virtual id a workgroup visits stays on its XCD
+    grid = (int)((mt * tilesP + 7) & ~int64_t(7));
   }
   if (grid <= 0) return 0;
-  dim3 g(grid), b(kThreads);
+  dim3 g(grid), b(Cfg::NT);
   switch (mode) {
-    case kFwd: hipLaunchKernelGGL(grouped_gemm_kernel<kFwd>, g, b, 0, s, a); break;
-    case kDgrad: hipLaunchKernelGGL(grouped_gemm_kernel<kDgrad>, g, b, 0, s, a); break;
-    default: hipLaunchKernelGGL(grouped_gemm_kernel<kWgrad>, g, b, 0, s, a); break;
+    case kFwd: hipLaunchKernelGGL((grouped_gemm_kernel<kFwd, Cfg>), g, b, 0, s, a); break;
+    case kDgrad: hipLaunchKernelGGL((grouped_gemm_kernel<kDgrad, Cfg>), g, b, 0, s, a); break;
+    default: hipLaunchKernelGGL((grouped_gemm_kernel<kWgrad, Cfg>), g, b, 0, s, a); break;
   }
   return (int)hipGetLastError();
 }
