@@ -54,8 +54,22 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int kBK = 32;                  // reduction steps per LDS stage
-constexpr int kStages = 4;               // LDS stages (kStages - 1 in flight)
+#ifndef MG_BK
+#define MG_BK 64
+#endif
+#ifndef MG_DMA_SLOTS
+#define MG_DMA_SLOTS 1
+#endif
+// Reduction steps per LDS stage.  64 makes every R-contiguous row of a stage
+// one full 128-byte line, so each L2 request carries 128 bytes.
+constexpr int kBK = MG_BK;
+constexpr int kStages = kBK == 32 ? 4 : 2;   // LDS stages (256x256 tile: 128 KiB)
+constexpr int kRowB = kBK * 2;               // bytes per R-contiguous staged row
+constexpr int kRowChunks = kBK / 8;          // 16-byte chunks per such row
+
+#ifndef MG_WAVES
+#define MG_WAVES 8
+#endif
 constexpr uint32_t kOOB = 0x80000000u;   // offset bit past any buffer range
 
 // Tile configuration: BP x BQ output tile, WP x WQ waves, each wave owning a
@@ -117,13 +131,16 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
 }
 
 // LDS layouts of one stage (byte offsets within an operand tile):
-//  R-contiguous tile [outer][32]: 64 B rows of 4 chunks of 16 B; chunk c of
-//    row r sits at chunk c ^ rc_swz(r).  32 consecutive rows read at one chunk
-//    hit distinct banks in groups of 8 or 16 lanes.
+//  R-contiguous tile [outer][kBK]: rows of kRowB bytes in 16-B chunks; chunk c
+//    of row r sits at chunk c ^ rc_swz(r), which uses row bits 0-4 only.  32
+//    consecutive rows read at one chunk hit distinct banks in groups of 8 or
+//    16 lanes.
 //  R-strided tile [32][outer]: rows of outer*2 bytes in 16-B chunks; chunk c
 //    of reduction row r sits at c ^ rs_swz(r % 4).  A transpose load touches
 //    4 rows x 2 chunks per 16 lanes (4 chunks per 32 lanes), all distinct.
-__device__ __forceinline__ int rc_swz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
+__device__ __forceinline__ int rc_swz(int row) {
+  return kRowChunks == 4 ? (((row >> 1) ^ (row >> 2)) & 3) : ((row & 7) ^ ((row >> 3) & 3));
+}
 __device__ __forceinline__ int rs_swz(int r4) { return (0xCA60 >> (4 * r4)) & 15; }  // 0,6,10,12
 
 // ------------------------------------------------------------- scheduler --
@@ -361,22 +378,33 @@ __device__ __forceinline__ void run_tile(const KernelArgs& a, const Tile& t, cha
       voff[j] = ((uint32_t)(r * ld + 8 * c) * 2u) | (8 * c < nouter ? 0u : kOOB);
       col[j] = 0;
     } else {                                                 // [outer][32]
-      const int row = p >> 6, pc = (p >> 4) & 3;
+      const int row = p / kRowB, pc = (p >> 4) % kRowChunks;
       const int c = pc ^ rc_swz(row);
       voff[j] = (uint32_t)(row * ld + 8 * c) * 2u;
       col[j] = 8 * c;
     }
   }
-  const i32x4 rc_rsrc =
-      make_rsrc(src, (uint32_t)(nouter < outer ? (nouter > 0 ? nouter : 0) : outer) * (uint32_t)ld * 2u);
+  const int rc_rows = nouter < outer ? (nouter > 0 ? nouter : 0) : outer;
+  const i32x4 rc_rsrc = make_rsrc(src, (uint32_t)rc_rows * (uint32_t)ld * 2u);
+  auto rs_rsrc = [&](int r0) {
+    const int rr = min(red_len - r0, kBK), oc = min(nouter, outer);
+    const uint32_t bytes = rr > 0 && oc > 0 ? ((uint32_t)(rr - 1) * ld + oc) * 2u : 0u;
+    return make_rsrc(src + (int64_t)r0 * ld, bytes);
+  };
 
-  auto issue = [&](int stage, int kt) {
+  // Vector-memory operations this wave has issued (uniform), and the count
+  // right after each stage's loads: the loads of stage s are complete once at
+  // most `issued - after[s % kStages]` operations are outstanding.
+  int issued = 0;
+  int after[kStages];
+#pragma unroll
+  for (int s = 0; s < kStages; ++s) after[s] = 0;
+
+  auto issue = [&](int kt) {
     const int r0 = kt * kBK;
-    const uint32_t dst = lds_base + (uint32_t)(stage * C::STAGE);
+    const uint32_t dst = lds_base + (uint32_t)((kt % kStages) * C::STAGE);
     if (rs) {
-      const int rr = min(red_len - r0, kBK), oc = min(nouter, outer);
-      const uint32_t bytes = rr > 0 && oc > 0 ? ((uint32_t)(rr - 1) * ld + oc) * 2u : 0u;
-      const i32x4 rsrc = make_rsrc(src + (int64_t)r0 * ld, bytes);
+      const i32x4 rsrc = rs_rsrc(r0);
 #pragma unroll
       for (int j = 0; j < SPW; ++j) dma16(rsrc, dst + j * 1024u, voff[j]);
     } else {
@@ -385,14 +413,17 @@ __device__ __forceinline__ void run_tile(const KernelArgs& a, const Tile& t, cha
         dma16(rc_rsrc, dst + j * 1024u,
               (voff[j] + (uint32_t)r0 * 2u) | (r0 + col[j] < red_len ? 0u : kOOB));
     }
+    issued += SPW;
+    after[kt % kStages] = issued;
   };
 
   // ---- fragment addresses (byte offsets within an operand tile)
   const int wp = wave / C::WQ, wq = wave % C::WQ;
   const int l32 = lane & 31, h = lane >> 5, L = lane & 15, g16 = (lane >> 4) & 1;
-  uint32_t offP[P_RS ? C::MP : 2], offQ[Q_RS ? C::MQ : 2];
+  constexpr int KK = kBK / 16;                 // 16-wide k-slices per stage
+  uint32_t offP[P_RS ? C::MP : KK], offQ[Q_RS ? C::MQ : KK];
   // R-contiguous: row = base + 32 i + l32 (swizzle depends on l32 only),
-  // chunk 2 kk + h; entry kk, then + 2048 i.
+  // chunk 2 kk + h; entry kk, then + 32 kRowB i.
   // R-strided: row 8 h + L/4 (+ 16 kk + 4 t), outer base + 32 i + 16 g16 + 4 (L % 4).
   auto rs_off = [&](int obase, int i, int outer_) {
     const int o = obase + 32 * i + 16 * g16 + 4 * (L & 3);
@@ -401,19 +432,21 @@ __device__ __forceinline__ void run_tile(const KernelArgs& a, const Tile& t, cha
   };
   auto rc_off = [&](int obase, int kk) {
     const int row = obase + l32;
-    return (uint32_t)(row * 64 + (((2 * kk + h) ^ rc_swz(l32)) << 4));
+    return (uint32_t)(row * kRowB + (((2 * kk + h) ^ rc_swz(l32)) << 4));
   };
   if (P_RS) {
 #pragma unroll
     for (int i = 0; i < C::MP; ++i) offP[i] = rs_off(wp * C::WTP, i, C::BP);
   } else {
-    offP[0] = rc_off(wp * C::WTP, 0); offP[1] = rc_off(wp * C::WTP, 1);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) offP[kk] = rc_off(wp * C::WTP, kk);
   }
   if (Q_RS) {
 #pragma unroll
     for (int j = 0; j < C::MQ; ++j) offQ[j] = rs_off(wq * C::WTQ, j, C::BQ);
   } else {
-    offQ[0] = rc_off(wq * C::WTQ, 0); offQ[1] = rc_off(wq * C::WTQ, 1);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) offQ[kk] = rc_off(wq * C::WTQ, kk);
   }
 
   f32x16 acc[C::MP][C::MQ];
@@ -422,48 +455,134 @@ __device__ __forceinline__ void run_tile(const KernelArgs& a, const Tile& t, cha
 #pragma unroll
     for (int j = 0; j < C::MQ; ++j) acc[i][j] = f32x16{};
 
-  auto compute = [&](int stage) {
-    const char* tp = lds + stage * C::STAGE;
+  struct Frags {
+    bf16x8 p[C::MP], q[C::MQ];
+  };
+  auto read = [&](int kt, int kk, Frags& f) {
+    const char* tp = lds + (kt % kStages) * C::STAGE;
     const char* tq = tp + C::P_BYTES;
-    bf16x8 fp[2][C::MP], fq[2][C::MQ];
 #pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
+    for (int i = 0; i < C::MP; ++i)
+      f.p[i] = P_RS ? frag_rs(tp, offP[i] + kk * 16 * C::BP * 2, 4 * C::BP * 2)
+                    : frag_rc(tp, offP[kk] + i * 32 * kRowB);
 #pragma unroll
-      for (int i = 0; i < C::MP; ++i)
-        fp[kk][i] = P_RS ? frag_rs(tp, offP[i] + kk * 16 * C::BP * 2, 4 * C::BP * 2)
-                         : frag_rc(tp, offP[kk] + i * 2048);
+    for (int j = 0; j < C::MQ; ++j)
+      f.q[j] = Q_RS ? frag_rs(tq, offQ[j] + kk * 16 * C::BQ * 2, 4 * C::BQ * 2)
+                    : frag_rc(tq, offQ[kk] + j * 32 * kRowB);
+  };
+  auto mma = [&](const Frags& f) {
+#pragma unroll
+    for (int i = 0; i < C::MP; ++i)
 #pragma unroll
       for (int j = 0; j < C::MQ; ++j)
-        fq[kk][j] = Q_RS ? frag_rs(tq, offQ[j] + kk * 16 * C::BQ * 2, 4 * C::BQ * 2)
-                         : frag_rc(tq, offQ[kk] + j * 2048);
-    }
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk)
-#pragma unroll
-      for (int i = 0; i < C::MP; ++i)
-#pragma unroll
-        for (int j = 0; j < C::MQ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp[kk][i], fq[kk][j], acc[i][j],
-                                                              0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.p[i], f.q[j], acc[i][j], 0, 0, 0);
+  };
+  // wait until this wave's loads of stage s have landed
+  auto wait_stage = [&](int s) {
+    int n = issued - after[s % kStages];
+    n = n < 0 ? 0 : n;
+    if (n >= 24) wait_vmcnt<24>();
+    else if (n >= 16) { if (n >= 20) wait_vmcnt<20>(); else wait_vmcnt<16>(); }
+    else if (n >= 8) { if (n >= 12) wait_vmcnt<12>(); else wait_vmcnt<8>(); }
+    else if (n >= 4) { if (n >= 6) wait_vmcnt<6>(); else wait_vmcnt<4>(); }
+    else if (n >= 2) wait_vmcnt<2>();
+    else wait_vmcnt<0>();
   };
 
-  // ---- pipeline: stage kt lives in LDS buffer kt % kStages; while it is
-  // consumed, stages kt+1 .. kt+kStages-1 are in flight.
+  // ---- pipeline.  Stage s lives in LDS buffer s % kStages and is consumed
+  // in KK k-slices.  While slice kk's products run, slice kk+1 is read; the
+  // last slice's products run while the barrier that publishes stage kt+1
+  // is crossed and stage kt+1's first slice is read, so the matrix cores
+  // stay busy across it.  That barrier also releases stage kt's buffer for
+  // every wave (each wave waits for its own LDS reads before arriving), so
+  // the loads of stage kt+kStages start right after it, spread between the
+  // products of the following MG_DMA_SLOTS slices (a burst of loads would
+  // stall on the memory queue).
+  constexpr int kMM = C::MP * C::MQ;
+  constexpr int kSlots = MG_DMA_SLOTS < KK ? MG_DMA_SLOTS : KK;
+  constexpr int kPer = (SPW + kSlots - 1) / kSlots;   // loads per slot
+  // Products of one k-slice, with loads [d0, d0 + nd) of stage dma_kt spread
+  // evenly between them.
+  auto mma_dma = [&](const Frags& f, int dma_kt, int d0, int nd) {
+    const bool doit = nd > 0 && dma_kt < nk;
+    const int r0 = dma_kt * kBK;
+    const uint32_t dst = lds_base + (uint32_t)((dma_kt % kStages) * C::STAGE);
+    i32x4 rsrc = rc_rsrc;
+    if (rs && doit) rsrc = rs_rsrc(r0);
+    const int every = nd > 0 && kMM / nd > 0 ? kMM / nd : 1;
+    int d = d0;
+#pragma unroll
+    for (int x = 0; x < kMM; ++x) {
+      const int i = x / C::MQ, j = x % C::MQ;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.p[i], f.q[j], acc[i][j], 0, 0, 0);
+      if ((x + 1) % every == 0 && d < d0 + nd) {
+        if (doit) {
+          __builtin_amdgcn_sched_barrier(0);
+          const uint32_t off = rs ? voff[d]
+                                  : (voff[d] + (uint32_t)r0 * 2u) | (r0 + col[d] < red_len ? 0u : kOOB);
+          dma16(rsrc, dst + d * 1024u, off);
+          ++issued;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        ++d;
+      }
+    }
+    if (doit && d0 + nd == SPW) after[dma_kt % kStages] = issued;
+  };
+  auto slot_lo = [&](int slot) { return min(slot * kPer, SPW); };
+  auto slot_n = [&](int slot) { return min((slot + 1) * kPer, SPW) - min(slot * kPer, SPW); };
+
   __syncthreads();                     // the previous tile's readers are done
 #pragma unroll
   for (int s = 0; s < kStages - 1; ++s)
-    if (s < nk) issue(s, s);
+    if (s < nk) issue(s);
+  Frags fr[2];
+  if (nk > 0) {
+    wait_stage(0);
+    __syncthreads();
+    read(0, 0, fr[0]);
+  }
+  // slot 0 of stage kStages-1 (its buffer is still untouched)
+  {
+    const int s0 = kStages - 1;
+    if (s0 < nk) {
+      const int r0 = s0 * kBK;
+      const uint32_t dst = lds_base + (uint32_t)((s0 % kStages) * C::STAGE);
+      const i32x4 rsrc = rs ? rs_rsrc(r0) : rc_rsrc;
+      for (int d = slot_lo(0); d < slot_lo(0) + slot_n(0); ++d) {
+        const uint32_t off = rs ? voff[d]
+                                : (voff[d] + (uint32_t)r0 * 2u) | (r0 + col[d] < red_len ? 0u : kOOB);
+        dma16(rsrc, dst + d * 1024u, off);
+        ++issued;
+      }
+      if (slot_n(0) == SPW) after[s0 % kStages] = issued;
+    }
+  }
   for (int kt = 0; kt < nk; ++kt) {
-    // this wave's loads of stage kt are done once at most the loads of the
-    // stages issued after it are outstanding
-    const int after = min(kStages - 2, nk - 1 - kt);
-    if (after >= 2) wait_vmcnt<2 * SPW>();
-    else if (after == 1) wait_vmcnt<SPW>();
-    else wait_vmcnt<0>();
-    __syncthreads();                   // every wave's part of stage kt is in LDS,
-                                       // and stage kt-1's buffer is free
-    if (kt + kStages - 1 < nk) issue((kt + kStages - 1) % kStages, kt + kStages - 1);
-    compute(kt % kStages);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      Frags& cur = fr[kk & 1];
+      Frags& nxt = fr[(kk + 1) & 1];
+      int dma_kt, slot;
+      if (kk + 1 < KK) {
+        read(kt, kk + 1, nxt);
+        dma_kt = kt + kStages - 1;      // slots 1.. of the stage begun after the last barrier
+        slot = kk + 1;
+      } else {
+        if (kt + 1 < nk) {
+          wait_stage(kt + 1);
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          __syncthreads();
+          read(kt + 1, 0, nxt);
+        }
+        dma_kt = kt + kStages;          // its buffer (stage kt's) was just released
+        slot = 0;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (slot < kSlots) mma_dma(cur, dma_kt, slot_lo(slot), slot_n(slot));
+      else mma_dma(cur, dma_kt, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   // ---- epilogue.  Result block (i, j): lane holds Q index l32 and P indices
@@ -560,7 +679,11 @@ void grouped_gemm_kernel(KernelArgs a) {
 
 // ------------------------------------------------------------ host launch --
 
+#if MG_WAVES == 8
 using Cfg = TileCfg<256, 256, 2, 4>;    // 8 waves (2 per SIMD), 128x64 per wave
+#else
+using Cfg = TileCfg<256, 256, 2, 2>;    // 4 waves (1 per SIMD), 128x128 per wave
+#endif
 
 int launch_grouped(int mode, const KernelArgs& a, int64_t max_m_per_e, hipStream_t s) {
   int grid;
