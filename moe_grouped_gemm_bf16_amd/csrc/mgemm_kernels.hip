@@ -20,31 +20,42 @@
 //   WGRAD    k  from X  [i][k]             n from dY[i][n]   i  (both R-strided)
 //
 // Operand staging: HBM -> LDS by direct-to-LDS buffer loads (no registers),
-// in 4 LDS stages of 32 reduction steps, 3 of them in flight while one is
-// consumed.  R-contiguous operands are staged as [outer][32] rows and read
+// in LDS stages of kBK reduction steps, the next stage in flight while one is
+// consumed.  R-contiguous operands are staged as [outer][kBK] rows and read
 // with 128-bit LDS loads; R-strided operands are staged as they lie in HBM,
-// [32][outer], and read with the LDS transpose load (ds_read_b64_tr_b16),
+// [kBK][outer], and read with the LDS transpose load (ds_read_b64_tr_b16),
 // which hands each lane 4 consecutive reduction values of one outer index --
 // the transposes wgrad and dgrad need are done by the LDS read, not by a pass.
 // Buffer descriptors whose range ends at the last valid byte make ragged
 // rows, reduction tails and out-of-range columns arrive in LDS as zeros.
 //
-// Scheduling: all experts in one launch.  Each workgroup reads the offsets,
-// derives per-expert tile counts and their prefix sums on the device (no host
-// synchronisation, empty experts give no M-tiles) and loops over its tiles.
-// M-grouped tiles all cost the same, so they are laid out XCD by XCD (the
-// dispatcher deals workgroups round-robin over the 8 XCDs) to keep operand
-// panels in one XCD's L2.  K-grouped tiles cost in proportion to the expert's
-// rows, so they are ordered heaviest expert first.
+// Scheduling: all experts in one persistent launch, one workgroup per compute
+// unit.  Each workgroup reads the offsets once, derives per-expert tile counts
+// and their prefix sums on the device (no host synchronisation; empty experts
+// give no M-tiles) and walks its own list of tiles.  The LDS stage ring runs
+// on across tile boundaries: the first stages of the next tile load while the
+// current tile's last products and its stores run.  Workgroup b runs on XCD
+// b % 8 (the dispatcher deals workgroups to the XCDs round-robin), and every
+// XCD owns a part of the tile space chosen so that the tiles it runs at the
+// same time share operand panels in its L2:
+//   M-grouped: a contiguous range of tile ids in a grouped raster order
+//     (groups of gm M-tiles of one expert, M-tile fastest), so the tiles in
+//     flight on an XCD cover ~gm M-tiles x a few P-tiles of one expert.
+//   K-grouped: for every expert, one of 8 compact chunks of its tile grid
+//     (P-bands of bw P-tiles, P-tile fastest within a band); experts are taken
+//     heaviest first and the workgroups of an XCD share its list longest-
+//     processing-time first, which balances tiles whose cost is the expert's
+//     row count.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <atomic>
 
 #include "mgemm_launch.h"
 
 namespace mg {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -56,9 +67,6 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 #ifndef MG_BK
 #define MG_BK 64
-#endif
-#ifndef MG_DMA_SLOTS
-#define MG_DMA_SLOTS 1
 #endif
 // Reduction steps per LDS stage.  64 makes every R-contiguous row of a stage
 // one full 128-byte line, so each L2 request carries 128 bytes.
@@ -135,7 +143,7 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
 //    of row r sits at chunk c ^ rc_swz(r), which uses row bits 0-4 only.  32
 //    consecutive rows read at one chunk hit distinct banks in groups of 8 or
 //    16 lanes.
-//  R-strided tile [32][outer]: rows of outer*2 bytes in 16-B chunks; chunk c
+//  R-strided tile [kBK][outer]: rows of outer*2 bytes in 16-B chunks; chunk c
 //    of reduction row r sits at c ^ rs_swz(r % 4).  A transpose load touches
 //    4 rows x 2 chunks per 16 lanes (4 chunks per 32 lanes), all distinct.
 __device__ __forceinline__ int rc_swz(int row) {
@@ -178,13 +186,20 @@ struct Tile {
   int r_end;
 };
 
-// Scheduler state kept in LDS for the whole launch.
+// Scheduler state kept in LDS / registers for the whole launch.
 struct Sched {
   int* scan;    // [16] scan scratch
   int* pref;    // [E+1] M-grouped: exclusive prefix of M-tiles per expert
   int* offs;    // [E+1] copy of the offsets
   int* inv;     // [E]   K-grouped: rank (heaviest first) -> expert
+  int* mine;    // [2E]  K-grouped: this workgroup's (rank | rho << 16, count) entries
+  int* keys;    // [64]  K-grouped: balancing scratch
+  int nmine;    // K-grouped: entries in `mine`
   int total;    // number of tiles
+  int E, tilesP, tilesQ, red;
+  int gm;       // M-grouped: M-tiles per raster group
+  int bw;       // K-grouped: P-tiles per band
+  int per;      // K-grouped: tiles per expert
 };
 
 // Offsets are read clamped to [0, M] and made non-decreasing per expert, so
@@ -198,8 +213,7 @@ __device__ __forceinline__ int clamp_off(const int32_t* offsets, int i, int M) {
 // M-grouped set-up: tiles are, for every expert, ceil(m_e / BQ) M-tiles times
 // tilesP P-tiles; empty experts contribute none.
 template <int NT, int BQ>
-__device__ void setup_mgrouped(const int32_t* __restrict__ offsets, int E, int M, int tilesP,
-                               Sched& S) {
+__device__ void setup_mgrouped(const int32_t* __restrict__ offsets, int E, int M, Sched& S) {
   constexpr int kPer = (kMaxExperts + NT - 1) / NT;
   const int e0 = threadIdx.x * kPer;
   int cnt[kPer];
@@ -228,75 +242,271 @@ __device__ void setup_mgrouped(const int32_t* __restrict__ offsets, int E, int M
   }
   if (threadIdx.x == 0) S.pref[E] = mtiles;
   __syncthreads();
-  S.total = mtiles * tilesP;
+  S.total = mtiles * S.tilesP;
 }
 
-// Tile of virtual workgroup id v (v = blockIdx.x + j * gridDim.x; gridDim.x is
-// a multiple of 8, so v stays on blockIdx.x's XCD).  The tiles are laid out
-// XCD by XCD: XCD x owns a contiguous range of tile ids, so tiles that run
-// together on one XCD share operand panels in its L2.  Within the range, the
-// P-tile index runs fastest.  Returns false once v is past this XCD's range.
-template <int BP, int BQ>
-__device__ __forceinline__ bool tile_mgrouped(int v, int E, int tilesP, int red,
-                                              const Sched& S, Tile& t) {
-  const int T = S.total;
-  const int x = v & 7, s = v >> 3;
-  const int q8 = T >> 3, r8 = T & 7;
-  if (s >= q8 + (x < r8 ? 1 : 0)) return false;
-  const int L = x * q8 + (x < r8 ? x : r8) + s;
-  const int mt = L / tilesP, tp = L - mt * tilesP;
-  // the expert whose M-tile range [pref[e], pref[e+1]) holds mt: the largest e
-  // with pref[e] <= mt (empty experts share their successor's prefix)
-  int lo = 0, hi = E - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (S.pref[mid] <= mt) lo = mid; else hi = mid - 1;
-  }
-  t.e = lo;
-  t.q0 = S.offs[lo] + (mt - S.pref[lo]) * BQ;
-  t.q_end = max(S.offs[lo + 1], S.offs[lo]);
-  t.p0 = tp * BP;
-  t.r_begin = 0;
-  t.r_end = red;
-  return true;
+// K-grouped: chunk k (0..7) of an expert's tile grid is the band-order index
+// range [k per / 8, (k+1) per / 8).
+__device__ __forceinline__ int kchunk_start(int k, int per) { return (k * per) >> 3; }
+__device__ __forceinline__ int kchunk_size(int k, int per) {
+  return kchunk_start(k + 1, per) - kchunk_start(k, per);
 }
 
 // K-grouped set-up: every expert has tilesQ x tilesP tiles whose cost grows
 // with its row count; experts are ranked heaviest first (ties: lower index
 // first) so that long reductions start early and short ones fill the tail.
+// The row counts are staged in S.mine (free until the balancing below),
+// padded with -1 so that the rank loop reads them four at a time.
 template <int NT>
-__device__ void setup_kgrouped(const int32_t* __restrict__ offsets, int E, int M, int per,
-                               Sched& S) {
+__device__ void setup_kgrouped(const int32_t* __restrict__ offsets, int E, int M, Sched& S) {
   for (int e = threadIdx.x; e <= E; e += NT) S.offs[e] = clamp_off(offsets, e, M);
   __syncthreads();
+  int* sizes = S.mine;
+  for (int e = threadIdx.x; e < E + 4; e += NT)
+    sizes[e] = e < E ? max(S.offs[e + 1] - S.offs[e], 0) : -1;
+  __syncthreads();
+  const int4* s4 = reinterpret_cast<const int4*>(sizes);
   for (int e = threadIdx.x; e < E; e += NT) {
-    const int me = max(S.offs[e + 1] - S.offs[e], 0);
+    const int me = sizes[e];
     int rank = 0;
-    for (int f = 0; f < E; ++f) {
-      const int mf = max(S.offs[f + 1] - S.offs[f], 0);
-      rank += (mf > me || (mf == me && f < e)) ? 1 : 0;
+    for (int f4 = 0; f4 < (E + 3) / 4; ++f4) {
+      const int4 v = s4[f4];
+      const int f = 4 * f4;
+      rank += (v.x > me || (v.x == me && f < e)) ? 1 : 0;
+      rank += (v.y > me || (v.y == me && f + 1 < e)) ? 1 : 0;
+      rank += (v.z > me || (v.z == me && f + 2 < e)) ? 1 : 0;
+      rank += (v.w > me || (v.w == me && f + 3 < e)) ? 1 : 0;
     }
     S.inv[rank] = e;
   }
   __syncthreads();
-  S.total = E * per;
+  S.total = E * S.per;
 }
 
+// K-grouped balancing.  XCD x's list is chunk (x - r) mod 8 of expert inv[r]
+// for r = 0, 1, ...: runs of equal-cost tiles, heaviest first.  Its nx
+// workgroups take them longest-processing-time first: the c tiles of a chunk
+// go `full` = c / nx to every workgroup and one more to the `rem` = c % nx
+// least loaded ones (ties: lower workgroup index).  A workgroup whose load
+// has rank rho among them takes the chunk's tiles rho, rho + nx, ...; it
+// records (r, rho, count) for its own list.  Cost of a tile: its stages plus
+// three for the store, scaled so that every load fits 25 bits; the keys
+// (load, index) are ranked by comparing each with all the others.  When every
+// tile costs the same this is plain round-robin over the list, done without
+// ranking.  One wave does the work; the per-rank quantities are computed 64
+// ranks at a time, one per lane, and read back with readlane.
+template <int NT>
+__device__ void balance_kgrouped(int x, int me, int nx, Sched& S) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    uint64_t tot = 0;
+    int ntiles = 0;
+    uint32_t wlo = 0xFFFFFFFFu, whi = 0;
+    for (int r = lane; r < S.E; r += 64) {
+      const int e = S.inv[r];
+      const int m = max(S.offs[e + 1] - S.offs[e], 0);
+      const uint32_t w = (uint32_t)((m + kBK - 1) / kBK + 3);
+      const int c = kchunk_size((x - r) & 7, S.per);
+      tot += (uint64_t)c * w;
+      ntiles += c;
+      if (c > 0) { wlo = min(wlo, w); whi = max(whi, w); }
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+      tot += __shfl_xor(tot, d, 64);
+      ntiles += __shfl_xor(ntiles, d, 64);
+      wlo = min(wlo, (uint32_t)__shfl_xor((int)wlo, d, 64));
+      whi = max(whi, (uint32_t)__shfl_xor((int)whi, d, 64));
+    }
+    // (the reductions are wave-uniform; say so, so that what follows is scalar)
+    tot = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(tot >> 32)) << 32) |
+          __builtin_amdgcn_readfirstlane((uint32_t)tot);
+    ntiles = __builtin_amdgcn_readfirstlane(ntiles);
+    wlo = __builtin_amdgcn_readfirstlane(wlo);
+    whi = __builtin_amdgcn_readfirstlane(whi);
+    // scaled tile cost (c >> sh) + 1: a load never exceeds (tot >> sh) + ntiles;
+    // keys need loads below 2^25, else (only for lists of tens of millions of
+    // tiles) the round-robin below is used, which is balanced to one tile
+    int sh = 0;
+    while ((tot >> sh) >= (1ull << 15)) ++sh;
+    const uint64_t maxload = (tot >> sh) + (uint64_t)ntiles;
+    const bool equal = wlo >= whi || (maxload >> 25) != 0;
+    uint32_t load = 0;
+    int n = 0, pos = 0;       // pos: list position mod nx (equal costs)
+    for (int b0 = 0; b0 < S.E; b0 += 64) {
+      const int rl = b0 + lane;
+      int cl = 0, fl = 0, rl_rem = 0;
+      uint32_t wl = 0;
+      if (rl < S.E) {
+        const int e = S.inv[rl];
+        const int m = max(S.offs[e + 1] - S.offs[e], 0);
+        wl = (uint32_t)(((m + kBK - 1) / kBK + 3) >> sh) + 1u;
+        cl = kchunk_size((x - rl) & 7, S.per);
+        fl = cl / nx;
+        rl_rem = cl - fl * nx;
+      }
+      const int nb = min(64, S.E - b0);
+      for (int i = 0; i < nb; ++i) {
+        const int c = __builtin_amdgcn_readlane(cl, i);
+        if (c == 0) continue;
+        const int full = __builtin_amdgcn_readlane(fl, i);
+        const int rem = __builtin_amdgcn_readlane(rl_rem, i);
+        int rho;
+        if (equal) {
+          rho = me - pos;
+          rho += rho < 0 ? nx : 0;
+          pos += rem;
+          pos -= pos >= nx ? nx : 0;
+        } else {
+          const uint32_t w = (uint32_t)__builtin_amdgcn_readlane((int)wl, i);
+          int rank = lane;
+          if (rem > 0) {
+            // rank of each bin's key among the nx keys (all distinct)
+            const uint32_t key = lane < nx ? ((load << 6) | (uint32_t)lane) : 0xFFFFFFFFu;
+            S.keys[lane] = (int)key;
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            const uint4* kv = reinterpret_cast<const uint4*>(S.keys);
+            int r0 = 0, r1 = 0;
+            if (nx <= 32) {
+              uint4 q[8];
+#pragma unroll
+              for (int j = 0; j < 8; ++j) q[j] = kv[j];
+#pragma unroll
+              for (int j = 0; j < 8; j += 2) {
+                r0 += (q[j].x < key) + (q[j].y < key) + (q[j].z < key) + (q[j].w < key);
+                r1 += (q[j + 1].x < key) + (q[j + 1].y < key) + (q[j + 1].z < key) +
+                      (q[j + 1].w < key);
+              }
+            } else {
+              uint4 q[16];
+#pragma unroll
+              for (int j = 0; j < 16; ++j) q[j] = kv[j];
+#pragma unroll
+              for (int j = 0; j < 16; j += 2) {
+                r0 += (q[j].x < key) + (q[j].y < key) + (q[j].z < key) + (q[j].w < key);
+                r1 += (q[j + 1].x < key) + (q[j + 1].y < key) + (q[j + 1].z < key) +
+                      (q[j + 1].w < key);
+              }
+            }
+            rank = r0 + r1;
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            if (rank < rem) load += w;
+          }
+          load += (uint32_t)full * w;
+          rho = __builtin_amdgcn_readlane(rank, me);
+        }
+        const int cnt = full + (rho < rem ? 1 : 0);
+        if (cnt > 0) {
+          if (lane == 0) {
+            S.mine[2 * n] = (b0 + i) | (rho << 16);
+            S.mine[2 * n + 1] = cnt;
+          }
+          ++n;
+        }
+      }
+    }
+    if (lane == 0) S.keys[0] = n;
+  }
+  __syncthreads();
+  S.nmine = S.keys[0];
+}
+
+// M-grouped tile id L -> tile.  Ids run expert by expert; within an expert,
+// in groups of gm M-tiles (the last group may be shorter), M-tile fastest,
+// then P-tile.
 template <int BP, int BQ>
-__device__ __forceinline__ bool tile_kgrouped(int v, int tilesP, int per, const Sched& S,
-                                              Tile& t) {
-  if (v >= S.total) return false;
-  const int rank = v / per, w = v - rank * per;
-  const int e = S.inv[rank];
-  const int tq = w / tilesP, tp = w - tq * tilesP;
+__device__ __forceinline__ void decode_mgrouped(int L, const Sched& S, Tile& t) {
+  const int tilesP = S.tilesP;
+  // the expert whose id range [pref[e] tilesP, pref[e+1] tilesP) holds L: the
+  // largest e with pref[e] tilesP <= L (empty experts share their successor's
+  // prefix)
+  int lo = 0, hi = S.E - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (S.pref[mid] * tilesP <= L) lo = mid; else hi = mid - 1;
+  }
+  const int e = lo;
+  const int local = L - S.pref[e] * tilesP;
+  const int mt = S.pref[e + 1] - S.pref[e];
+  const int g = local / (S.gm * tilesP);
+  const int rem = local - g * S.gm * tilesP;
+  const int gh = min(S.gm, mt - g * S.gm);
+  const int tp = rem / gh;
+  const int m = g * S.gm + (rem - tp * gh);
+  t.e = e;
+  t.q0 = S.offs[e] + m * BQ;
+  t.q_end = max(S.offs[e + 1], S.offs[e]);
+  t.p0 = tp * BP;
+  t.r_begin = 0;
+  t.r_end = S.red;
+}
+
+// Tile u of chunk k of the expert with rank r -> tile.  Within the expert's
+// grid the tiles run in band order: P-bands of bw P-tiles each (the last may
+// be narrower); within a band, Q-tile slow and P-tile fast.
+template <int BP, int BQ>
+__device__ __forceinline__ void decode_kgrouped(int r, int k, int u_in_chunk, const Sched& S,
+                                                Tile& t) {
+  const int e = S.inv[r];
+  const int u = kchunk_start(k, S.per) + u_in_chunk;
+  const int nbw = S.bw * S.tilesQ;
+  const int b = min(u / nbw, (S.tilesP - 1) / S.bw);
+  const int local = u - b * nbw;
+  const int wb = min(S.bw, S.tilesP - b * S.bw);
+  const int tq = local / wb;
+  const int tp = b * S.bw + (local - tq * wb);
   t.e = e;
   t.q0 = tq * BQ;
   t.p0 = tp * BP;
   t.r_begin = S.offs[e];
   t.r_end = max(S.offs[e + 1], S.offs[e]);
   t.q_end = 0x7FFFFFFF;
-  return true;
 }
+
+// The tile list of one workgroup: XCD x = blockIdx % 8, index c = blockIdx / 8
+// among the nx = gridDim / 8 workgroups of that XCD (gridDim is a multiple
+// of 8).  M-grouped: ids lo + c, lo + c + nx, ... of the XCD's range.
+// K-grouped: the balanced entries of `mine`.
+template <int MODE, int BP, int BQ>
+struct TileSeq {
+  int x, c, nx, count, lo, j, ie;
+
+  __device__ __forceinline__ void init(const Sched& S) {
+    x = blockIdx.x & 7;
+    c = blockIdx.x >> 3;
+    nx = gridDim.x >> 3;
+    j = 0;
+    ie = 0;
+    if (MODE != kWgrad) {
+      const int q8 = S.total >> 3, r8 = S.total & 7;
+      count = q8 + (x < r8 ? 1 : 0);
+      lo = x * q8 + (x < r8 ? x : r8);
+    }
+  }
+
+  // Next tile of this workgroup; false once the list is exhausted.
+  __device__ __forceinline__ bool next(const Sched& S, Tile& t) {
+    if (MODE == kWgrad) {
+      if (ie >= S.nmine) return false;
+      const int rr = S.mine[2 * ie], cnt = S.mine[2 * ie + 1];
+      const int r = rr & 0xFFFF, rho = rr >> 16;
+      decode_kgrouped<BP, BQ>(r, (x - r) & 7, rho + j * nx, S, t);
+      if (++j == cnt) { j = 0; ++ie; }
+    } else {
+      const int s = c + j * nx;
+      if (s >= count) return false;
+      ++j;
+      decode_mgrouped<BP, BQ>(lo + s, S, t);
+    }
+    t.e = __builtin_amdgcn_readfirstlane(t.e);
+    t.q0 = __builtin_amdgcn_readfirstlane(t.q0);
+    t.q_end = __builtin_amdgcn_readfirstlane(t.q_end);
+    t.p0 = __builtin_amdgcn_readfirstlane(t.p0);
+    t.r_begin = __builtin_amdgcn_readfirstlane(t.r_begin);
+    t.r_end = __builtin_amdgcn_readfirstlane(t.r_end);
+    return true;
+  }
+};
 
 // ------------------------------------------------------------------ kernel --
 
@@ -304,12 +514,12 @@ __device__ __forceinline__ bool tile_kgrouped(int v, int tilesP, int per, const 
 // reduction values 8*(l/32) + 0..7 of outer index l % 32 (within one k-slice
 // of 16).  Both operands use the same assignment, so the products pair up.
 
-// R-contiguous tile [outer][32] (64-byte rows): one 128-bit read.
+// R-contiguous tile [outer][kBK]: one 128-bit read.
 __device__ __forceinline__ bf16x8 frag_rc(const char* tile, uint32_t off) {
   return *reinterpret_cast<const bf16x8*>(tile + off);
 }
 
-// R-strided tile [32][outer]: two transpose loads of 4 reduction rows each.
+// R-strided tile [kBK][outer]: two transpose loads of 4 reduction rows each.
 // Within each 16-lane group, lane i's element j comes from the 8-byte word
 // addressed by lane 4j + i/4, element i % 4; so lane i addresses row
 // R0 + i/4, outer columns o0 + 4 (i % 4) .. +3, and receives column o0 + i of
@@ -326,101 +536,140 @@ __device__ __forceinline__ bf16x8 frag_rs(const char* tile, uint32_t off, uint32
   return __builtin_bit_cast(bf16x8, w);
 }
 
+// The persistent body of one workgroup: a producer walks the tile list
+// issuing LDS stages (tiles with an empty reduction have none), a consumer
+// walks the same list consuming them and storing each tile's result.  Stage
+// g of the launch lives in LDS buffer g % kStages.
 template <int MODE, class C>
-__device__ __forceinline__ void run_tile(const KernelArgs& a, const Tile& t, char* lds,
-                                         int Pdim, int Qdim) {
+__device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, char* lds,
+                                          int Pdim, int Qdim) {
   constexpr bool P_RS = MODE != kFwd;      // P is R-strided for dgrad and wgrad
   constexpr bool Q_RS = MODE == kWgrad;    // Q is R-strided for wgrad
   constexpr int SPW = C::SEGS_PER_WAVE;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
 
-  // ---- operand sources for this tile
-  const uint16_t* P = reinterpret_cast<const uint16_t*>(a.p_src);
-  const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.q_src);
   int ldP, ldQ;
-  if (MODE == kFwd) {            // P = W[e] rows n (R = k), Q = X rows m (R = k)
-    ldP = (int)a.K; ldQ = (int)a.K;
-    P += ((int64_t)t.e * a.N + t.p0) * a.K;
-    Q += (int64_t)t.q0 * a.K;
-  } else if (MODE == kDgrad) {   // P = W[e] [n][k] R-strided, Q = dY rows m (R = n)
-    ldP = (int)a.K; ldQ = (int)a.N;
-    P += (int64_t)t.e * a.N * a.K + t.p0;
-    Q += (int64_t)t.q0 * a.N;
-  } else {                       // P = X [i][k] R-strided, Q = dY [i][n] R-strided
-    ldP = (int)a.K; ldQ = (int)a.N;
-    P += (int64_t)t.r_begin * a.K + t.p0;
-    Q += (int64_t)t.r_begin * a.N + t.q0;
-  }
-  const int red_len = t.r_end - t.r_begin;
-  const int nk = (red_len + kBK - 1) / kBK;
-  const int nP = Pdim - t.p0;                  // valid P rows (R-contiguous) or columns
-  const int nQ = MODE == kWgrad ? Qdim - t.q0 : t.q_end - t.q0;
+  if (MODE == kFwd) { ldP = (int)a.K; ldQ = (int)a.K; }
+  else if (MODE == kDgrad) { ldP = (int)a.K; ldQ = (int)a.N; }
+  else { ldP = (int)a.K; ldQ = (int)a.N; }
 
   // ---- direct-to-LDS plan: each stage is C::SEGS 1-KiB segments (the P tile
   // first, then the Q tile); wave w loads segments w*SPW .. w*SPW + SPW - 1.
+  // The per-lane part (offset within the tile, column) is the same for every
+  // tile; the base, the valid extents and the descriptor follow the tile.
   const bool wP = wave * SPW < C::SEGS_P;                    // wave-uniform
   const bool rs = wP ? P_RS : Q_RS;
   const int outer = wP ? C::BP : C::BQ;
-  const int nouter = wP ? nP : nQ;
   const int ld = wP ? ldP : ldQ;
-  const uint16_t* src = wP ? P : Q;
   const int seg0 = wP ? wave * SPW : wave * SPW - C::SEGS_P;
   const uint32_t lds_base = lds_u32(lds) + (wP ? 0u : (uint32_t)C::P_BYTES) + seg0 * 1024u;
   uint32_t voff[SPW];
-  int col[SPW];
+  int col[SPW];    // R-contiguous: reduction column; R-strided: outer column
 #pragma unroll
   for (int j = 0; j < SPW; ++j) {
     const int p = (seg0 + j) * 1024 + lane * 16;             // byte within the tile
-    if (rs) {                                                // [32][outer]
+    if (rs) {                                                // [kBK][outer]
       const int r = p / (outer * 2), pc = (p >> 4) % (outer / 8);
       const int c = pc ^ rs_swz(r & 3);
-      voff[j] = ((uint32_t)(r * ld + 8 * c) * 2u) | (8 * c < nouter ? 0u : kOOB);
-      col[j] = 0;
-    } else {                                                 // [outer][32]
+      voff[j] = (uint32_t)(r * ld + 8 * c) * 2u;
+      col[j] = 8 * c;
+    } else {                                                 // [outer][kBK]
       const int row = p / kRowB, pc = (p >> 4) % kRowChunks;
       const int c = pc ^ rc_swz(row);
       voff[j] = (uint32_t)(row * ld + 8 * c) * 2u;
       col[j] = 8 * c;
     }
   }
-  const int rc_rows = nouter < outer ? (nouter > 0 ? nouter : 0) : outer;
-  const i32x4 rc_rsrc = make_rsrc(src, (uint32_t)rc_rows * (uint32_t)ld * 2u);
-  auto rs_rsrc = [&](int r0) {
-    const int rr = min(red_len - r0, kBK), oc = min(nouter, outer);
-    const uint32_t bytes = rr > 0 && oc > 0 ? ((uint32_t)(rr - 1) * ld + oc) * 2u : 0u;
-    return make_rsrc(src + (int64_t)r0 * ld, bytes);
+
+  // Operand bases and valid extents of a tile.
+  auto tile_src = [&](const Tile& t, const uint16_t*& src, int& nouter) {
+    const uint16_t* P = reinterpret_cast<const uint16_t*>(a.p_src);
+    const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.q_src);
+    if (MODE == kFwd) {            // P = W[e] rows n (R = k), Q = X rows m (R = k)
+      P += ((int64_t)t.e * a.N + t.p0) * a.K;
+      Q += (int64_t)t.q0 * a.K;
+    } else if (MODE == kDgrad) {   // P = W[e] [n][k] R-strided, Q = dY rows m (R = n)
+      P += (int64_t)t.e * a.N * a.K + t.p0;
+      Q += (int64_t)t.q0 * a.N;
+    } else {                       // P = X [i][k] R-strided, Q = dY [i][n] R-strided
+      P += (int64_t)t.r_begin * a.K + t.p0;
+      Q += (int64_t)t.r_begin * a.N + t.q0;
+    }
+    const int nP = Pdim - t.p0;
+    const int nQ = MODE == kWgrad ? Qdim - t.q0 : t.q_end - t.q0;
+    src = wP ? P : Q;
+    nouter = wP ? nP : nQ;
   };
 
-  // Vector-memory operations this wave has issued (uniform), and the count
-  // right after each stage's loads: the loads of stage s are complete once at
-  // most `issued - after[s % kStages]` operations are outstanding.
-  int issued = 0;
+  // ---- producer state (wave-uniform)
+  TileSeq<MODE, C::BP, C::BQ> pseq;
+  pseq.init(S);
+  const uint16_t* p_src = nullptr;
+  int p_nouter = 0, p_red = 0, p_nk = 0, p_kt = 0;
+  i32x4 p_rc = {0, 0, 0, 0};
+  bool p_live = false;
+  auto p_next_tile = [&]() {
+    Tile t;
+    p_live = false;
+    while (pseq.next(S, t)) {
+      const int red = t.r_end - t.r_begin;
+      const int nk = (red + kBK - 1) / kBK;
+      if (nk <= 0) continue;                  // nothing to stage: the consumer stores zeros
+      tile_src(t, p_src, p_nouter);
+      p_red = red;
+      p_nk = nk;
+      p_kt = 0;
+      const int rows = p_nouter < outer ? (p_nouter > 0 ? p_nouter : 0) : outer;
+      p_rc = make_rsrc(p_src, (uint32_t)rows * (uint32_t)ld * 2u);
+      p_live = true;
+      return;
+    }
+  };
+  p_next_tile();
+
+  // Vector-memory loads this wave has issued (uniform), and the count right
+  // after each stage's loads: the loads of stage g are complete once at most
+  // `issued - after[g % kStages]` operations are outstanding (loads complete
+  // in order; stores are not counted, which only makes the wait stricter).
+  int issued = 0, gp = 0;
   int after[kStages];
 #pragma unroll
   for (int s = 0; s < kStages; ++s) after[s] = 0;
 
-  auto issue = [&](int kt) {
-    const int r0 = kt * kBK;
-    const uint32_t dst = lds_base + (uint32_t)((kt % kStages) * C::STAGE);
-    if (rs) {
-      const i32x4 rsrc = rs_rsrc(r0);
+  auto stage_rsrc = [&](int r0) {
+    if (!rs) return p_rc;
+    const int rr = min(p_red - r0, kBK), oc = min(p_nouter, outer);
+    const uint32_t bytes = rr > 0 && oc > 0 ? ((uint32_t)(rr - 1) * ld + oc) * 2u : 0u;
+    return make_rsrc(p_src + (int64_t)r0 * ld, bytes);
+  };
+  auto dma_one = [&](const i32x4& rsrc, uint32_t dst, int d, int r0) {
+    const uint32_t off = rs ? (voff[d] | (col[d] < p_nouter ? 0u : kOOB))
+                            : ((voff[d] + (uint32_t)r0 * 2u) | (r0 + col[d] < p_red ? 0u : kOOB));
+    dma16(rsrc, dst + d * 1024u, off);
+  };
+  auto p_advance = [&]() {
+    after[gp % kStages] = issued;
+    ++gp;
+    if (++p_kt == p_nk) p_next_tile();
+  };
+  // Issue the producer's next stage in one go.
+  auto produce = [&]() {
+    if (!p_live) return;
+    const int r0 = p_kt * kBK;
+    const uint32_t dst = lds_base + (uint32_t)((gp % kStages) * C::STAGE);
+    const i32x4 rsrc = stage_rsrc(r0);
 #pragma unroll
-      for (int j = 0; j < SPW; ++j) dma16(rsrc, dst + j * 1024u, voff[j]);
-    } else {
-#pragma unroll
-      for (int j = 0; j < SPW; ++j)
-        dma16(rc_rsrc, dst + j * 1024u,
-              (voff[j] + (uint32_t)r0 * 2u) | (r0 + col[j] < red_len ? 0u : kOOB));
-    }
+    for (int d = 0; d < SPW; ++d) dma_one(rsrc, dst, d, r0);
     issued += SPW;
-    after[kt % kStages] = issued;
+    p_advance();
   };
 
   // ---- fragment addresses (byte offsets within an operand tile)
   const int wp = wave / C::WQ, wq = wave % C::WQ;
   const int l32 = lane & 31, h = lane >> 5, L = lane & 15, g16 = (lane >> 4) & 1;
   constexpr int KK = kBK / 16;                 // 16-wide k-slices per stage
+  static_assert(KK % 2 == 0, "fragment double buffer parity");
   uint32_t offP[P_RS ? C::MP : KK], offQ[Q_RS ? C::MQ : KK];
   // R-contiguous: row = base + 32 i + l32 (swizzle depends on l32 only),
   // chunk 2 kk + h; entry kk, then + 32 kRowB i.
@@ -458,8 +707,8 @@ __device__ __forceinline__ void run_tile(const KernelArgs& a, const Tile& t, cha
   struct Frags {
     bf16x8 p[C::MP], q[C::MQ];
   };
-  auto read = [&](int kt, int kk, Frags& f) {
-    const char* tp = lds + (kt % kStages) * C::STAGE;
+  auto read = [&](int g, int kk, Frags& f) {
+    const char* tp = lds + (g % kStages) * C::STAGE;
     const char* tq = tp + C::P_BYTES;
 #pragma unroll
     for (int i = 0; i < C::MP; ++i)
@@ -470,16 +719,9 @@ __device__ __forceinline__ void run_tile(const KernelArgs& a, const Tile& t, cha
       f.q[j] = Q_RS ? frag_rs(tq, offQ[j] + kk * 16 * C::BQ * 2, 4 * C::BQ * 2)
                     : frag_rc(tq, offQ[kk] + j * 32 * kRowB);
   };
-  auto mma = [&](const Frags& f) {
-#pragma unroll
-    for (int i = 0; i < C::MP; ++i)
-#pragma unroll
-      for (int j = 0; j < C::MQ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.p[i], f.q[j], acc[i][j], 0, 0, 0);
-  };
-  // wait until this wave's loads of stage s have landed
-  auto wait_stage = [&](int s) {
-    int n = issued - after[s % kStages];
+  // wait until this wave's loads of stage g have landed
+  auto wait_stage = [&](int g) {
+    int n = issued - after[g % kStages];
     n = n < 0 ? 0 : n;
     if (n >= 24) wait_vmcnt<24>();
     else if (n >= 16) { if (n >= 20) wait_vmcnt<20>(); else wait_vmcnt<16>(); }
@@ -489,148 +731,144 @@ __device__ __forceinline__ void run_tile(const KernelArgs& a, const Tile& t, cha
     else wait_vmcnt<0>();
   };
 
-  // ---- pipeline.  Stage s lives in LDS buffer s % kStages and is consumed
-  // in KK k-slices.  While slice kk's products run, slice kk+1 is read; the
-  // last slice's products run while the barrier that publishes stage kt+1
-  // is crossed and stage kt+1's first slice is read, so the matrix cores
-  // stay busy across it.  That barrier also releases stage kt's buffer for
-  // every wave (each wave waits for its own LDS reads before arriving), so
-  // the loads of stage kt+kStages start right after it, spread between the
-  // products of the following MG_DMA_SLOTS slices (a burst of loads would
-  // stall on the memory queue).
+  // Products of one k-slice.  With `dma`, the producer's next stage is
+  // issued between them (a burst of loads would stall on the memory queue).
   constexpr int kMM = C::MP * C::MQ;
-  constexpr int kSlots = MG_DMA_SLOTS < KK ? MG_DMA_SLOTS : KK;
-  constexpr int kPer = (SPW + kSlots - 1) / kSlots;   // loads per slot
-  // Products of one k-slice, with loads [d0, d0 + nd) of stage dma_kt spread
-  // evenly between them.
-  auto mma_dma = [&](const Frags& f, int dma_kt, int d0, int nd) {
-    const bool doit = nd > 0 && dma_kt < nk;
-    const int r0 = dma_kt * kBK;
-    const uint32_t dst = lds_base + (uint32_t)((dma_kt % kStages) * C::STAGE);
-    i32x4 rsrc = rc_rsrc;
-    if (rs && doit) rsrc = rs_rsrc(r0);
-    const int every = nd > 0 && kMM / nd > 0 ? kMM / nd : 1;
-    int d = d0;
+  auto mma = [&](const Frags& f, bool dma) {
+    const bool doit = dma && p_live;
+    int r0 = 0;
+    uint32_t dst = 0;
+    i32x4 rsrc = p_rc;
+    if (doit) {
+      r0 = p_kt * kBK;
+      dst = lds_base + (uint32_t)((gp % kStages) * C::STAGE);
+      rsrc = stage_rsrc(r0);
+    }
+    constexpr int every = kMM / SPW > 0 ? kMM / SPW : 1;
+    int d = 0;
 #pragma unroll
     for (int x = 0; x < kMM; ++x) {
       const int i = x / C::MQ, j = x % C::MQ;
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.p[i], f.q[j], acc[i][j], 0, 0, 0);
-      if ((x + 1) % every == 0 && d < d0 + nd) {
+      if ((x + 1) % every == 0 && d < SPW) {
         if (doit) {
           __builtin_amdgcn_sched_barrier(0);
-          const uint32_t off = rs ? voff[d]
-                                  : (voff[d] + (uint32_t)r0 * 2u) | (r0 + col[d] < red_len ? 0u : kOOB);
-          dma16(rsrc, dst + d * 1024u, off);
+          dma_one(rsrc, dst, d, r0);
           ++issued;
           __builtin_amdgcn_sched_barrier(0);
         }
         ++d;
       }
     }
-    if (doit && d0 + nd == SPW) after[dma_kt % kStages] = issued;
-  };
-  auto slot_lo = [&](int slot) { return min(slot * kPer, SPW); };
-  auto slot_n = [&](int slot) { return min((slot + 1) * kPer, SPW) - min(slot * kPer, SPW); };
-
-  __syncthreads();                     // the previous tile's readers are done
+    if (doit) {
 #pragma unroll
-  for (int s = 0; s < kStages - 1; ++s)
-    if (s < nk) issue(s);
+      for (; d < SPW; ++d) {
+        dma_one(rsrc, dst, d, r0);
+        ++issued;
+      }
+      p_advance();
+    }
+  };
+
+  // Result block (i, j): lane holds Q index l32 and P indices 8*g + 4*h + 0..3
+  // for g = 0..3 (accumulator registers 4g..4g+3).
+  auto store_tile = [&](const Tile& t) {
+    if (MODE == kWgrad) {
+      if (a.accumulate && t.r_end <= t.r_begin) return;   // adds nothing
+      float* out = reinterpret_cast<float*>(a.out) + (int64_t)t.e * a.N * a.K;
+#pragma unroll
+      for (int j = 0; j < C::MQ; ++j) {
+        const int n = t.q0 + wq * C::WTQ + j * 32 + l32;
+        if (n >= Qdim) continue;
+        float* orow = out + (int64_t)n * a.K;
+#pragma unroll
+        for (int i = 0; i < C::MP; ++i) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int k = t.p0 + wp * C::WTP + i * 32 + g * 8 + h * 4;
+            if (k >= Pdim) continue;
+            f32x4 r = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                       acc[i][j][4 * g + 3]};
+            f32x4* dst = reinterpret_cast<f32x4*>(orow + k);
+            if (a.accumulate) r += *dst;
+            *dst = r;
+          }
+        }
+      }
+    } else {
+      uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+      const int ldo = Pdim;
+#pragma unroll
+      for (int j = 0; j < C::MQ; ++j) {
+        const int m = t.q0 + wq * C::WTQ + j * 32 + l32;
+        if (m >= t.q_end) continue;
+        uint16_t* orow = out + (int64_t)m * ldo;
+#pragma unroll
+        for (int i = 0; i < C::MP; ++i) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int c = t.p0 + wp * C::WTP + i * 32 + g * 8 + h * 4;
+            if (c >= Pdim) continue;
+            bf16x2 lo = __builtin_convertvector(
+                (f32x2){acc[i][j][4 * g], acc[i][j][4 * g + 1]}, bf16x2);
+            bf16x2 hi = __builtin_convertvector(
+                (f32x2){acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]}, bf16x2);
+            u32x2 pk = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+            *reinterpret_cast<u32x2*>(orow + c) = pk;
+          }
+        }
+      }
+    }
+  };
+
+  // ---- pipeline.  Stage g is consumed in KK k-slices.  While slice kk's
+  // products run, slice kk+1 is read; the last slice's products run after the
+  // barrier that publishes stage g+1 (its first slice is read before them),
+  // so the matrix cores stay busy across it.  That barrier also releases
+  // stage g's buffer for every wave (each wave waits for its own LDS reads
+  // before arriving), so the producer's next stage g + kStages is issued into
+  // it between those products.
+#pragma unroll
+  for (int s = 0; s < kStages; ++s) produce();   // every buffer is free at the start
+  TileSeq<MODE, C::BP, C::BQ> cseq;
+  cseq.init(S);
   Frags fr[2];
-  if (nk > 0) {
+  int g = 0;
+  if (gp > 0) {
     wait_stage(0);
     __syncthreads();
     read(0, 0, fr[0]);
   }
-  // slot 0 of stage kStages-1 (its buffer is still untouched)
-  {
-    const int s0 = kStages - 1;
-    if (s0 < nk) {
-      const int r0 = s0 * kBK;
-      const uint32_t dst = lds_base + (uint32_t)((s0 % kStages) * C::STAGE);
-      const i32x4 rsrc = rs ? rs_rsrc(r0) : rc_rsrc;
-      for (int d = slot_lo(0); d < slot_lo(0) + slot_n(0); ++d) {
-        const uint32_t off = rs ? voff[d]
-                                : (voff[d] + (uint32_t)r0 * 2u) | (r0 + col[d] < red_len ? 0u : kOOB);
-        dma16(rsrc, dst + d * 1024u, off);
-        ++issued;
-      }
-      if (slot_n(0) == SPW) after[s0 % kStages] = issued;
-    }
-  }
-  for (int kt = 0; kt < nk; ++kt) {
+  Tile ct;
+  while (cseq.next(S, ct)) {
+    const int nk = (ct.r_end - ct.r_begin + kBK - 1) / kBK;
+    for (int kt = 0; kt < nk; ++kt, ++g) {
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      Frags& cur = fr[kk & 1];
-      Frags& nxt = fr[(kk + 1) & 1];
-      int dma_kt, slot;
-      if (kk + 1 < KK) {
-        read(kt, kk + 1, nxt);
-        dma_kt = kt + kStages - 1;      // slots 1.. of the stage begun after the last barrier
-        slot = kk + 1;
-      } else {
-        if (kt + 1 < nk) {
-          wait_stage(kt + 1);
-          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-          __syncthreads();
-          read(kt + 1, 0, nxt);
+      for (int kk = 0; kk < KK; ++kk) {
+        Frags& cur = fr[kk & 1];
+        Frags& nxt = fr[(kk + 1) & 1];
+        bool dma = false;
+        if (kk + 1 < KK) {
+          read(g, kk + 1, nxt);
+        } else {
+          if (g + 1 < gp) {
+            wait_stage(g + 1);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __syncthreads();
+            read(g + 1, 0, nxt);
+          }
+          dma = true;
         }
-        dma_kt = kt + kStages;          // its buffer (stage kt's) was just released
-        slot = 0;
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      if (slot < kSlots) mma_dma(cur, dma_kt, slot_lo(slot), slot_n(slot));
-      else mma_dma(cur, dma_kt, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-
-  // ---- epilogue.  Result block (i, j): lane holds Q index l32 and P indices
-  // 8*g + 4*h + 0..3 for g = 0..3 (accumulator registers 4g..4g+3).
-  if (MODE == kWgrad) {
-    float* out = reinterpret_cast<float*>(a.out) + (int64_t)t.e * a.N * a.K;
-#pragma unroll
-    for (int j = 0; j < C::MQ; ++j) {
-      const int n = t.q0 + wq * C::WTQ + j * 32 + l32;
-      if (n >= Qdim) continue;
-      float* orow = out + (int64_t)n * a.K;
-#pragma unroll
-      for (int i = 0; i < C::MP; ++i) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int k = t.p0 + wp * C::WTP + i * 32 + g * 8 + h * 4;
-          if (k >= Pdim) continue;
-          f32x4 r = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                     acc[i][j][4 * g + 3]};
-          f32x4* dst = reinterpret_cast<f32x4*>(orow + k);
-          if (a.accumulate) r += *dst;
-          *dst = r;
-        }
+        __builtin_amdgcn_sched_barrier(0);
+        mma(cur, dma);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-  } else {
-    uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
-    const int ldo = Pdim;
+    store_tile(ct);
 #pragma unroll
-    for (int j = 0; j < C::MQ; ++j) {
-      const int m = t.q0 + wq * C::WTQ + j * 32 + l32;
-      if (m >= t.q_end) continue;
-      uint16_t* orow = out + (int64_t)m * ldo;
+    for (int i = 0; i < C::MP; ++i)
 #pragma unroll
-      for (int i = 0; i < C::MP; ++i) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int c = t.p0 + wp * C::WTP + i * 32 + g * 8 + h * 4;
-          if (c >= Pdim) continue;
-          bf16x2 lo = __builtin_convertvector(
-              (f32x2){acc[i][j][4 * g], acc[i][j][4 * g + 1]}, bf16x2);
-          bf16x2 hi = __builtin_convertvector(
-              (f32x2){acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]}, bf16x2);
-          u32x2 pk = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-          *reinterpret_cast<u32x2*>(orow + c) = pk;
-        }
-      }
-    }
+      for (int j = 0; j < C::MQ; ++j) acc[i][j] = f32x16{};
   }
 }
 
@@ -638,7 +876,10 @@ template <int MODE, class C>
 __global__ __launch_bounds__(C::NT)
 void grouped_gemm_kernel(KernelArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[C::LDS];
-  __shared__ int sched[16 + 2 * (kMaxExperts + 1) + kMaxExperts];
+  // keys [64] | scan [16] | mine [2 kMaxExperts + 8] | pref [E+1] | offs [E+1] | inv [E]
+  // (keys and mine 16-byte aligned: they are read four entries at a time)
+  __shared__ __attribute__((aligned(16))) int sched[64 + 16 + 2 * kMaxExperts + 8 +
+                                                   2 * (kMaxExperts + 1) + kMaxExperts];
 
   int Pdim, Qdim;
   if (MODE == kFwd) {
@@ -648,32 +889,37 @@ void grouped_gemm_kernel(KernelArgs a) {
   } else {
     Pdim = (int)a.K; Qdim = (int)a.N;
   }
-  const int tilesP = (Pdim + C::BP - 1) / C::BP;
-  const int tilesQ = (Qdim + C::BQ - 1) / C::BQ;
   const int E = a.E;
   Sched S;
-  S.scan = sched;
-  S.pref = sched + 16;
+  S.keys = sched;
+  S.scan = sched + 64;
+  S.mine = sched + 80;
+  S.pref = S.mine + 2 * kMaxExperts + 8;
   S.offs = S.pref + (E + 1);
   S.inv = S.offs + (E + 1);
-  if (MODE == kWgrad) setup_kgrouped<C::NT>(a.offsets, E, (int)a.M, tilesQ * tilesP, S);
-  else setup_mgrouped<C::NT, C::BQ>(a.offsets, E, (int)a.M, tilesP, S);
-  const int red = MODE == kFwd ? (int)a.K : (int)a.N;
-
-  for (int v = blockIdx.x;; v += gridDim.x) {
-    Tile t;
-    const bool have = MODE == kWgrad
-                          ? tile_kgrouped<C::BP, C::BQ>(v, tilesP, tilesQ * tilesP, S, t)
-                          : tile_mgrouped<C::BP, C::BQ>(v, E, tilesP, red, S, t);
-    if (!have) break;
-    t.e = __builtin_amdgcn_readfirstlane(t.e);
-    t.q0 = __builtin_amdgcn_readfirstlane(t.q0);
-    t.q_end = __builtin_amdgcn_readfirstlane(t.q_end);
-    t.p0 = __builtin_amdgcn_readfirstlane(t.p0);
-    t.r_begin = __builtin_amdgcn_readfirstlane(t.r_begin);
-    t.r_end = __builtin_amdgcn_readfirstlane(t.r_end);
-    run_tile<MODE, C>(a, t, lds, Pdim, Qdim);
+  S.nmine = 0;
+  S.E = E;
+  S.tilesP = (Pdim + C::BP - 1) / C::BP;
+  S.tilesQ = (Qdim + C::BQ - 1) / C::BQ;
+  S.red = MODE == kFwd ? (int)a.K : (int)a.N;
+  // raster group: about sqrt(nx) M-tiles, more when there are few P-tiles,
+  // so that the nx tiles an XCD runs at once span ~gm x (nx / gm) panels
+  const int nx = gridDim.x >> 3;
+  int gm = 1;
+  while (gm * gm < nx) ++gm;
+  S.gm = max(gm, (nx + S.tilesP - 1) / S.tilesP);
+  S.per = S.tilesQ * S.tilesP;
+  // band width ~ sqrt(per / 8): a chunk of per/8 tiles is then ~bw x bw
+  int bw = 1;
+  while (bw < S.tilesP && 2 * (2 * bw + 1) * (2 * bw + 1) <= S.per) ++bw;
+  S.bw = bw;
+  if (MODE == kWgrad) {
+    setup_kgrouped<C::NT>(a.offsets, E, (int)a.M, S);
+    balance_kgrouped<C::NT>(blockIdx.x & 7, blockIdx.x >> 3, nx, S);
+  } else {
+    setup_mgrouped<C::NT, C::BQ>(a.offsets, E, (int)a.M, S);
   }
+  run_tiles<MODE, C>(a, S, lds, Pdim, Qdim);
 }
 
 
@@ -685,25 +931,46 @@ using Cfg = TileCfg<256, 256, 2, 4>;    // 8 waves (2 per SIMD), 128x64 per wave
 using Cfg = TileCfg<256, 256, 2, 2>;    // 4 waves (1 per SIMD), 128x128 per wave
 #endif
 
+// Compute units of the current device (one resident workgroup each).
+static int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 int launch_grouped(int mode, const KernelArgs& a, int64_t max_m_per_e, hipStream_t s) {
-  int grid;
+  int64_t tiles;
   if (mode == kWgrad) {
-    const int tilesP = (int)((a.K + Cfg::BP - 1) / Cfg::BP);
-    const int tilesQ = (int)((a.N + Cfg::BQ - 1) / Cfg::BQ);
-    grid = a.E * tilesQ * tilesP;
+    const int64_t tilesP = (a.K + Cfg::BP - 1) / Cfg::BP;
+    const int64_t tilesQ = (a.N + Cfg::BQ - 1) / Cfg::BQ;
+    tiles = (int64_t)a.E * tilesQ * tilesP;
   } else {
     const int64_t Pdim = mode == kFwd ? a.N : a.K;
-    const int tilesP = (int)((Pdim + Cfg::BP - 1) / Cfg::BP);
+    const int64_t tilesP = (Pdim + Cfg::BP - 1) / Cfg::BP;
     int64_t mt = (a.M + Cfg::BQ - 1) / Cfg::BQ + a.E;       // sum_e ceil(m_e/BQ) <= this
     if (max_m_per_e > 0) {
       const int64_t alt = (int64_t)a.E * ((max_m_per_e + Cfg::BQ - 1) / Cfg::BQ);
       if (alt < mt) mt = alt;
     }
-    // a multiple of 8 so that every virtual id a workgroup visits stays on its XCD
-    grid = (int)((mt * tilesP + 7) & ~int64_t(7));
+    tiles = mt * tilesP;
   }
-  if (grid <= 0) return 0;
-  dim3 g(grid), b(Cfg::NT);
+  if (tiles <= 0) return 0;
+  // one workgroup per compute unit at most, and a multiple of 8 so that
+  // workgroup b stays on XCD b % 8's part of the tile space
+  // (at most 64 per XCD: the K-grouped balancing keeps one lane per workgroup)
+  const int cus = device_cus() & ~7;
+  const int64_t cap = cus < 8 ? 8 : (cus > 512 ? 512 : cus);
+  int64_t grid = (tiles + 7) & ~int64_t(7);
+  if (grid > cap) grid = cap;
+  dim3 g((unsigned)grid), b(Cfg::NT);
   switch (mode) {
     case kFwd: hipLaunchKernelGGL((grouped_gemm_kernel<kFwd, Cfg>), g, b, 0, s, a); break;
     case kDgrad: hipLaunchKernelGGL((grouped_gemm_kernel<kDgrad, Cfg>), g, b, 0, s, a); break;

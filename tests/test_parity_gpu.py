@@ -78,6 +78,8 @@ MG_CASES = [
     ([700, 0, 0], 72, 1032, 3),
     ([3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14], 8, 8, 0),
     ([64] * 9, 768, 64, 0),
+    # the largest expert count, mostly tiny and empty experts
+    ([int(v) for v in np.random.default_rng(7).integers(0, 6, 1024)], 8, 16, 2),
 ]
 
 
@@ -98,6 +100,12 @@ WG_CASES = [
     ([64, 63, 65, 128, 0], 256, 256),
     ([1000], 8, 520),
     ([0, 0, 2], 136, 8),
+    # many skewed experts, a few empty: chunks of a handful of tiles, ranked
+    ([int(v) for v in np.random.default_rng(8).zipf(1.3, 40) % 700] + [0, 0], 520, 264),
+    # 256 tiles per expert: every XCD chunk holds exactly one tile per workgroup
+    ([70, 0, 5], 4096, 4096),
+    # the largest expert count
+    ([int(v) for v in np.random.default_rng(9).integers(0, 9, 1024)], 8, 24),
 ]
 
 
