@@ -731,43 +731,46 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
     else wait_vmcnt<0>();
   };
 
-  // Products of one k-slice.  With `dma`, the producer's next stage is
-  // issued between them (a burst of loads would stall on the memory queue).
-  constexpr int kMM = C::MP * C::MQ;
-  auto mma = [&](const Frags& f, bool dma) {
-    const bool doit = dma && p_live;
-    int r0 = 0;
-    uint32_t dst = 0;
-    i32x4 rsrc = p_rc;
-    if (doit) {
-      r0 = p_kt * kBK;
-      dst = lds_base + (uint32_t)((gp % kStages) * C::STAGE);
-      rsrc = stage_rsrc(r0);
+  constexpr int kMM = C::MP * C::MQ;            // products per k-slice per wave
+  // Products x0 .. x1-1 of one k-slice with the producer's loads d0 .. d1-1
+  // (of the stage set up in `sd`) spread evenly between them.
+  struct StageDma {
+    int r0;
+    uint32_t dst;
+    i32x4 rsrc;
+    bool on;
+  };
+  auto dma_begin = [&]() {
+    StageDma sd;
+    sd.on = p_live;
+    sd.r0 = 0;
+    sd.dst = 0;
+    sd.rsrc = p_rc;
+    if (sd.on) {
+      sd.r0 = p_kt * kBK;
+      sd.dst = lds_base + (uint32_t)((gp % kStages) * C::STAGE);
+      sd.rsrc = stage_rsrc(sd.r0);
     }
-    constexpr int every = kMM / SPW > 0 ? kMM / SPW : 1;
-    int d = 0;
+    return sd;
+  };
+  auto mma_part = [&](const Frags& f, int x0, int x1, const StageDma& sd, int d0, int d1) {
+    int d = d0;
 #pragma unroll
-    for (int x = 0; x < kMM; ++x) {
+    for (int x = x0; x < x1; ++x) {
       const int i = x / C::MQ, j = x % C::MQ;
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.p[i], f.q[j], acc[i][j], 0, 0, 0);
-      if ((x + 1) % every == 0 && d < SPW) {
-        if (doit) {
+      // after product x, (x - x0 + 1) (d1 - d0) / (x1 - x0) loads are due
+      while (d < d1 && (d - d0) * (x1 - x0) < (x - x0 + 1) * (d1 - d0)) {
+        if (sd.on) {
           __builtin_amdgcn_sched_barrier(0);
-          dma_one(rsrc, dst, d, r0);
+          dma_one(sd.rsrc, sd.dst, d, sd.r0);
           ++issued;
           __builtin_amdgcn_sched_barrier(0);
         }
         ++d;
       }
     }
-    if (doit) {
-#pragma unroll
-      for (; d < SPW; ++d) {
-        dma_one(rsrc, dst, d, r0);
-        ++issued;
-      }
-      p_advance();
-    }
+    if (sd.on && d1 == SPW && d0 < d1) p_advance();   // this part issued the stage's last load
   };
 
   // Result block (i, j): lane holds Q index l32 and P indices 8*g + 4*h + 0..3
@@ -821,18 +824,21 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
     }
   };
 
-  // ---- pipeline.  Stage g is consumed in KK k-slices.  While slice kk's
-  // products run, slice kk+1 is read; the last slice's products run after the
-  // barrier that publishes stage g+1 (its first slice is read before them),
-  // so the matrix cores stay busy across it.  That barrier also releases
-  // stage g's buffer for every wave (each wave waits for its own LDS reads
-  // before arriving), so the producer's next stage g + kStages is issued into
-  // it between those products.
+  // ---- pipeline.  Stage g is consumed in KK k-slices; while slice kk's
+  // products run, slice kk+1 is read.  The last slice of a stage has two
+  // barriers.  The first comes as soon as every wave holds that slice (each
+  // waits for its own LDS reads before arriving): stage g's buffer is then
+  // free, and the producer's next stage g + kStages is issued into it during
+  // the first half of the slice's products -- it does not wait for stage g+1
+  // to land.  The second, in the middle of the products, publishes stage g+1
+  // once this wave's loads of it have landed, and its first slice is read
+  // while the second half of the products runs.
 #pragma unroll
   for (int s = 0; s < kStages; ++s) produce();   // every buffer is free at the start
   TileSeq<MODE, C::BP, C::BQ> cseq;
   cseq.init(S);
   Frags fr[2];
+  const StageDma sd_none = {0, 0u, p_rc, false};
   int g = 0;
   if (gp > 0) {
     wait_stage(0);
@@ -847,21 +853,28 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
       for (int kk = 0; kk < KK; ++kk) {
         Frags& cur = fr[kk & 1];
         Frags& nxt = fr[(kk + 1) & 1];
-        bool dma = false;
         if (kk + 1 < KK) {
           read(g, kk + 1, nxt);
+          __builtin_amdgcn_sched_barrier(0);
+          mma_part(cur, 0, kMM, sd_none, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
         } else {
-          if (g + 1 < gp) {
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          __syncthreads();
+          const bool more = g + 1 < gp;
+          const StageDma sd = dma_begin();
+          __builtin_amdgcn_sched_barrier(0);
+          mma_part(cur, 0, kMM / 2, sd, 0, SPW / 2);
+          __builtin_amdgcn_sched_barrier(0);
+          if (more) {
             wait_stage(g + 1);
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             __syncthreads();
             read(g + 1, 0, nxt);
           }
-          dma = true;
+          __builtin_amdgcn_sched_barrier(0);
+          mma_part(cur, kMM / 2, kMM, sd, SPW / 2, SPW);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        mma(cur, dma);
-        __builtin_amdgcn_sched_barrier(0);
       }
     }
     store_tile(ct);
