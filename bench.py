@@ -55,6 +55,8 @@ def parse_args():
                    help="also time each op N times after flushing the caches")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run one plain 1 GiB device copy (for HBM counter calibration)")
+    p.add_argument("--comparators", action="store_true",
+                   help="also time library baselines on the same inputs (reported only)")
     return p.parse_args()
 
 
@@ -63,9 +65,10 @@ def parse_args():
 class Op:
     """One launch of the path: a name, its workload, a launcher and its flops."""
 
-    def __init__(self, name, kind, wl, launch, flops, bytes_):
+    def __init__(self, name, kind, wl, launch, flops, bytes_, tensors=None):
         self.name, self.kind, self.wl, self.launch = name, kind, wl, launch
         self.flops, self.bytes = flops, bytes_
+        self.tensors = tensors or {}
         self.times_ms = []
 
 
@@ -94,10 +97,10 @@ def build_ops(workload: str, torch, mg):
         ab = 2 * (rows * wl.K + wl.E * wl.N * wl.K + rows * wl.N)   # read X, W; write Y
         ops.append(Op(f"fwd:{wl.name}", "fwd", wl,
                       (lambda x=x, w=w, off=off, y=y, h=hint: mg.fwd(x, w, off, h, out=y)),
-                      wl.flops(), ab))
+                      wl.flops(), ab, dict(a=x, w=w, off=off)))
         ops.append(Op(f"dgrad:{wl.name}", "dgrad", wl,
                       (lambda dy=dy, w=w, off=off, dx=dx, h=hint: mg.dgrad(dy, w, off, h, out=dx)),
-                      wl.flops(), ab))
+                      wl.flops(), ab, dict(a=dy, w=w, off=off)))
         inputs.append((x, w, dy, off, y, dx))
     for wl in wg_wls:
         if workload == "a3b" or "wgrad" in wl.ops:
@@ -111,9 +114,69 @@ def build_ops(workload: str, torch, mg):
             ab = 2 * rows * (wl.N + wl.K) + 4 * wl.E * wl.N * wl.K        # read dY, X; write fp32 dW
             ops.append(Op(f"wgrad:{wl.name}", "wgrad", wl,
                           (lambda dy=dy, x=x, off=off, dw=dw: mg.wgrad(dy, x, off, out=dw)),
-                          wl.flops(), ab))
+                          wl.flops(), ab, dict(dy=dy, x=x, off=off)))
             inputs.append((x, dy, off, dw))
     return ops, inputs
+
+
+# -------------------------------------------------------------- comparators --
+
+def comparators(ops, torch, reps=20):
+    """Library baselines on the same device inputs, reported beside the kernels
+    (never part of `value`): a loop of one hipBLASLt GEMM per expert (torch 2-D
+    matmul, the analogue of the multi-stream per-group baseline of the
+    TransformerEngine PR #2045 perf table) and torch._grouped_mm where this torch
+    has it.  Operands that the libraries want in the other orientation are made
+    contiguous before the timed region.  Both emit bf16 for wgrad (the kernel
+    under test writes fp32)."""
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return statistics.median(a.elapsed_time(b) for a, b in ev) * 1e3
+
+    out = {}
+    for op in ops:
+        t, o = op.tensors, [int(v) for v in op.wl.offsets]
+        E = len(o) - 1
+        spans = [(e, o[e], o[e + 1]) for e in range(E) if o[e + 1] > o[e]]
+        ends = t["off"][1:].contiguous()
+        rec = {}
+        if op.kind == "fwd":
+            wt = t["w"].transpose(1, 2).contiguous()          # [E, K, N]
+            a = t["a"]
+            loop = lambda: [torch.matmul(a[i:j], wt[e]) for e, i, j in spans]
+            grp = lambda: torch._grouped_mm(a, wt, offs=ends)
+        elif op.kind == "dgrad":
+            w, a = t["w"], t["a"]
+            loop = lambda: [torch.matmul(a[i:j], w[e]) for e, i, j in spans]
+            grp = lambda: torch._grouped_mm(a, w, offs=ends)
+        else:
+            dyt, x = t["dy"].t().contiguous(), t["x"]           # dY^T [N, M]
+            loop = lambda: [torch.matmul(dyt[:, i:j], x[i:j]) for e, i, j in spans]
+            grp = lambda: torch._grouped_mm(dyt, x, offs=ends)
+        us = timed(loop)
+        rec["hipblaslt_per_expert_loop"] = {"us": round(us, 1),
+                                            "tflops": round(op.flops / us / 1e6, 1)}
+        if hasattr(torch, "_grouped_mm"):
+            try:
+                us = timed(grp)
+                rec["torch_grouped_mm"] = {"us": round(us, 1),
+                                           "tflops": round(op.flops / us / 1e6, 1)}
+            except Exception as exc:                       # not supported on this build
+                rec["torch_grouped_mm"] = {"error": f"{type(exc).__name__}: {str(exc)[:120]}"}
+        if op.kind == "wgrad":
+            rec["note"] = "comparators write bf16 dW; the kernel writes fp32"
+        out[op.name] = rec
+        torch.cuda.empty_cache()
+    return out
 
 
 # ------------------------------------------------------------- CPU baseline --
@@ -262,6 +325,11 @@ def main():
                 "traffic": traffic, "kernel": f"{KERNEL_NAMES[dom.kind]} ({dom.name})",
                 "algorithmic_bytes": dom.bytes}
 
+    comp = None
+    if args.comparators:
+        print("[bench] timing library comparators", file=sys.stderr, flush=True)
+        comp = comparators(ops, torch)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
@@ -295,6 +363,8 @@ def main():
         "cpu_baseline": cpu,
         "kernel_src_sha256_16": kernel_hash(),
     }
+    if comp is not None:
+        line["comparators"] = comp
     print(json.dumps(line), flush=True)
 
 
