@@ -61,6 +61,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -773,26 +774,63 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
     if (sd.on && d1 == SPW && d0 < d1) p_advance();   // this part issued the stage's last load
   };
 
-  // Result block (i, j): lane holds Q index l32 and P indices 8*g + 4*h + 0..3
-  // for g = 0..3 (accumulator registers 4g..4g+3).
+  // Result block (i, j) of the matrix cores: lane l holds Q index l % 32 and,
+  // in accumulator registers 4g .. 4g+3, the four consecutive P indices of
+  // 16-byte chunk 2g + l/32 (P indices 8g + 4(l/32) + 0..3).  A store
+  // instruction then touches 32 output rows; the memory pipeline handles about
+  // one row per cycle, so the lanes are first regrouped with the lane-half
+  // swaps of gfx950 so that each store covers 16 rows x 64 contiguous bytes:
+  //  fp32: v_permlane16_swap between chunk pairs (2g', 2g'+1) leaves register
+  //    group g holding row (l % 16) + 16 (g % 2), chunk (l / 32) + 2 ((l / 16) % 2)
+  //    + 4 (g / 2): 4 stores of 16 B per block;
+  //  bf16: 8-byte chunks; v_permlane16_swap between groups (g, g+2) then
+  //    v_permlane32_swap between (2g', 2g'+1) leave lane l holding rows (l % 16)
+  //    and (l % 16) + 16, chunks c, c+1 with c = 4 ((l / 16) % 2) + 2 (l / 32):
+  //    2 stores of 16 B per block.
+  auto swap16 = [](uint32_t& x, uint32_t& y) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, y, false, false);
+    x = r[0];
+    y = r[1];
+  };
+  auto swap32 = [](uint32_t& x, uint32_t& y) {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+    x = r[0];
+    y = r[1];
+  };
+  const int l16 = lane & 15, pa = (lane >> 4) & 1, pb = lane >> 5;
   auto store_tile = [&](const Tile& t) {
     if (MODE == kWgrad) {
       if (a.accumulate && t.r_end <= t.r_begin) return;   // adds nothing
       float* out = reinterpret_cast<float*>(a.out) + (int64_t)t.e * a.N * a.K;
+      const int c = pb + 2 * pa;                          // chunk of groups 0 and 1
 #pragma unroll
       for (int j = 0; j < C::MQ; ++j) {
-        const int n = t.q0 + wq * C::WTQ + j * 32 + l32;
-        if (n >= Qdim) continue;
-        float* orow = out + (int64_t)n * a.K;
 #pragma unroll
         for (int i = 0; i < C::MP; ++i) {
+          // (each element goes through a named float: this compiler lowers
+          // __builtin_bit_cast of an ext_vector element as a copy of element 0)
+          uint32_t v[4][4];
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float f = acc[i][j][4 * g + e];
+              v[g][e] = __builtin_bit_cast(uint32_t, f);
+            }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            swap16(v[0][e], v[1][e]);
+            swap16(v[2][e], v[3][e]);
+          }
+          const int n0 = t.q0 + wq * C::WTQ + j * 32 + l16;
+          const int k0 = t.p0 + wp * C::WTP + i * 32 + 4 * c;
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const int k = t.p0 + wp * C::WTP + i * 32 + g * 8 + h * 4;
-            if (k >= Pdim) continue;
-            f32x4 r = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                       acc[i][j][4 * g + 3]};
-            f32x4* dst = reinterpret_cast<f32x4*>(orow + k);
+            const int n = n0 + 16 * (g & 1), k = k0 + 16 * (g >> 1);
+            if (n >= Qdim || k >= Pdim) continue;
+            f32x4 r = {__builtin_bit_cast(float, v[g][0]), __builtin_bit_cast(float, v[g][1]),
+                       __builtin_bit_cast(float, v[g][2]), __builtin_bit_cast(float, v[g][3])};
+            f32x4* dst = reinterpret_cast<f32x4*>(out + (int64_t)n * a.K + k);
             if (a.accumulate) r += *dst;
             *dst = r;
           }
@@ -801,23 +839,41 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
     } else {
       uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
       const int ldo = Pdim;
+      const int c = 4 * pa + 2 * pb;                      // first of the lane's two chunks
 #pragma unroll
       for (int j = 0; j < C::MQ; ++j) {
-        const int m = t.q0 + wq * C::WTQ + j * 32 + l32;
-        if (m >= t.q_end) continue;
-        uint16_t* orow = out + (int64_t)m * ldo;
 #pragma unroll
         for (int i = 0; i < C::MP; ++i) {
+          uint32_t v[4][2];
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const int c = t.p0 + wp * C::WTP + i * 32 + g * 8 + h * 4;
-            if (c >= Pdim) continue;
-            bf16x2 lo = __builtin_convertvector(
+            const bf16x2 lo = __builtin_convertvector(
                 (f32x2){acc[i][j][4 * g], acc[i][j][4 * g + 1]}, bf16x2);
-            bf16x2 hi = __builtin_convertvector(
+            const bf16x2 hi = __builtin_convertvector(
                 (f32x2){acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]}, bf16x2);
-            u32x2 pk = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-            *reinterpret_cast<u32x2*>(orow + c) = pk;
+            v[g][0] = __builtin_bit_cast(uint32_t, lo);
+            v[g][1] = __builtin_bit_cast(uint32_t, hi);
+          }
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            swap16(v[0][e], v[2][e]);
+            swap16(v[1][e], v[3][e]);
+          }
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            swap32(v[0][e], v[1][e]);
+            swap32(v[2][e], v[3][e]);
+          }
+          const int m0 = t.q0 + wq * C::WTQ + j * 32 + l16;
+          const int col = t.p0 + wp * C::WTP + i * 32 + 4 * c;
+          if (col >= Pdim) continue;
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const int m = m0 + 16 * half;
+            if (m >= t.q_end) continue;
+            const u32x4 pk = {v[2 * half][0], v[2 * half][1], v[2 * half + 1][0],
+                              v[2 * half + 1][1]};
+            *reinterpret_cast<u32x4*>(out + (int64_t)m * ldo + col) = pk;
           }
         }
       }
