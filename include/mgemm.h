@@ -26,15 +26,22 @@
  *     multiples of 8 (every row starts 16-byte aligned).  1 <= E <= 1024.
  *     M, N, K < 2^31.  Outputs must not alias inputs.
  *   - stream: a hipStream_t (NULL = the null stream).  Each call only
- *     enqueues work on that stream and returns; it never synchronises,
- *     allocates, or keeps a pointer after returning.  The caller owns every
- *     buffer and must keep it alive until the stream has run the work.
+ *     enqueues work on that stream and returns; it never synchronises or
+ *     keeps a caller pointer after returning.  The caller owns every buffer
+ *     and must keep it alive until the stream has run the work.  The one
+ *     allocation: the first kgemm_wgrad call on a (device, stream) pair
+ *     allocates a 64 MiB device workspace for that pair (hipMalloc, zeroing
+ *     its counters on the stream) and keeps it until the process ends; calls
+ *     on one stream share it in stream order, calls on different streams
+ *     never share one.  If that allocation fails the call still runs, without
+ *     the token split.  MGEMM_SPLIT=0 turns the split (and the workspace) off.
  *   - Host-detectable errors are returned before anything is enqueued.
  *     Launch failures return MG_ERR_LAUNCH.  Faults during execution surface
  *     at the caller's next synchronisation, like any stream work.  Nothing
  *     throws across this ABI.
  *   - Thread safety: calls may be made concurrently from several threads; the
- *     only shared state is a per-device architecture check done once.
+ *     shared state is a per-device architecture check done once and the
+ *     mutex-protected table of per-stream workspaces.
  */
 #ifndef MGEMM_H
 #define MGEMM_H
@@ -88,7 +95,11 @@ mg_status mgemm_dgrad(const void* dy, const void* w, const int32_t* offsets, voi
  * accumulate != 0: the sum is added to dw's contents (fp32 gradient
  * accumulation, as in the TransformerEngine PR #2045 review of
  * fuse_wgrad_accumulation), and an empty expert's block is left as it was.
- * Rows i >= offsets[E] do not contribute.  N == 0 or K == 0 is a no-op. */
+ * Rows i >= offsets[E] do not contribute.  N == 0 or K == 0 is a no-op.
+ * An expert much heavier than the rest may have its token range split in two
+ * halves whose fp32 partial sums are added as (half + half), then + dw when
+ * accumulating: results are bitwise reproducible from call to call.  This is
+ * the call that uses the per-stream workspace described above. */
 mg_status kgemm_wgrad(const void* dy, const void* x, const int32_t* offsets, float* dw,
                       int64_t M, int64_t N, int64_t K, int32_t E, int32_t accumulate,
                       void* stream);

@@ -1,10 +1,12 @@
 // C-ABI entry points of libmgemm.so: argument validation, device check and
-// dispatch to the gfx950 kernels.  No allocation, no host workspace, no
-// host<->device copy and no synchronisation on the normal path: the offsets
-// stay on the device and are read by the kernels' own tile scheduler (a host
-// workspace copied to the device per call, freed before the asynchronous copy
-// has run, is the lifetime race discussed in the TransformerEngine PR #2045
-// review; this design has no such buffer).
+// dispatch to the gfx950 kernels.  No host workspace, no host<->device copy
+// and no synchronisation on the normal path: the offsets stay on the device
+// and are read by the kernels' own tile scheduler (a host workspace copied to
+// the device per call, freed before the asynchronous copy has run, is the
+// lifetime race discussed in the TransformerEngine PR #2045 review; this
+// design has no such buffer).  The only allocation is the device workspace of
+// the weight gradient's token split, made once per (device, stream) by the
+// launch layer and kept for the life of the process.
 #include <hip/hip_runtime.h>
 
 #include <atomic>

@@ -45,11 +45,16 @@
 //     (P-bands of bw P-tiles, P-tile fastest within a band); experts are taken
 //     heaviest first and the workgroups of an XCD share its list longest-
 //     processing-time first, which balances tiles whose cost is the expert's
-//     row count.
+//     row count.  A tile too heavy to balance by placement (an expert holding
+//     a large share of the rows) is split into two halves of its token range
+//     whose fp32 partial sums are added by whichever half ends second.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include <atomic>
+#include <cstdlib>
+#include <mutex>
+#include <vector>
 
 #include "mgemm_launch.h"
 
@@ -59,6 +64,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -183,8 +189,9 @@ struct Tile {
   int q0;       // first Q index of the tile (global row for M-grouped, n for K-grouped)
   int q_end;    // one past the last valid Q index
   int p0;       // first P index
-  int r_begin;  // reduction range [r_begin, r_end)
+  int r_begin;  // reduction range [r_begin, r_end) of this work item
   int r_end;
+  int split;    // K-grouped: -1 for a whole tile, else 2 x split-tile id + half
 };
 
 // Scheduler state kept in LDS / registers for the whole launch.
@@ -201,6 +208,7 @@ struct Sched {
   int gm;       // M-grouped: M-tiles per raster group
   int bw;       // K-grouped: P-tiles per band
   int per;      // K-grouped: tiles per expert
+  bool split;   // K-grouped: heavy tiles may be split in two token halves
 };
 
 // Offsets are read clamped to [0, M] and made non-decreasing per expert, so
@@ -284,6 +292,17 @@ __device__ void setup_kgrouped(const int32_t* __restrict__ offsets, int E, int M
   S.total = E * S.per;
 }
 
+// K-grouped token split.  A tile of an expert whose cost exceeds the XCD's
+// average load per workgroup cannot be balanced by placement alone: it is
+// split into two halves of its token range when such tiles are few enough
+// (at most kSplitPerXcd and at most half the XCD's workgroups) for each half
+// to share a workgroup with lighter tiles.  The halves add their fp32
+// partial sums at the end (see the consumer's epilogue).  kSplitCost: extra
+// cost, in stages, charged to a half for writing and reading the partial.
+constexpr int kSplitPerXcd = 16;
+constexpr int kSplitMinStages = 16;
+constexpr int kSplitCost = 4;
+
 // K-grouped balancing.  XCD x's list is chunk (x - r) mod 8 of expert inv[r]
 // for r = 0, 1, ...: runs of equal-cost tiles, heaviest first.  Its nx
 // workgroups take them longest-processing-time first: the c tiles of a chunk
@@ -300,14 +319,50 @@ template <int NT>
 __device__ void balance_kgrouped(int x, int me, int nx, Sched& S) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
+    // pass 1: the XCD's total cost, for the split decision
+    uint64_t tot0 = 0;
+    for (int r = lane; r < S.E; r += 64) {
+      const int e = S.inv[r];
+      const int m = max(S.offs[e + 1] - S.offs[e], 0);
+      tot0 += (uint64_t)kchunk_size((x - r) & 7, S.per) * (uint64_t)((m + kBK - 1) / kBK + 3);
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) tot0 += __shfl_xor(tot0, d, 64);
+    tot0 = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(tot0 >> 32)) << 32) |
+           __builtin_amdgcn_readfirstlane((uint32_t)tot0);
+    const uint64_t avg = tot0 / (uint64_t)nx;
+    // tiles heavier than the average load (and long enough to halve)
+    auto heavy = [&](int m) {
+      const int st = (m + kBK - 1) / kBK;
+      return st >= kSplitMinStages && (uint64_t)(st + 3) > avg;
+    };
+    int nheavy = 0;
+    for (int r = lane; r < S.E; r += 64) {
+      const int e = S.inv[r];
+      if (heavy(max(S.offs[e + 1] - S.offs[e], 0))) nheavy += kchunk_size((x - r) & 7, S.per);
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) nheavy += __shfl_xor(nheavy, d, 64);
+    nheavy = __builtin_amdgcn_readfirstlane(nheavy);
+    const bool split_on = S.split && nheavy > 0 && nheavy <= kSplitPerXcd && 2 * nheavy <= nx;
+    // a run's pieces: c tiles of cost w, or 2c halves of cost about w / 2
+    auto piece = [&](int m, int c, int& np, uint32_t& w, bool& sp) {
+      const int st = (m + kBK - 1) / kBK;
+      sp = split_on && heavy(m);
+      np = sp ? 2 * c : c;
+      w = (uint32_t)(sp ? (st + 1) / 2 + 3 + kSplitCost : st + 3);
+    };
+    // pass 2: totals over the pieces
     uint64_t tot = 0;
     int ntiles = 0;
     uint32_t wlo = 0xFFFFFFFFu, whi = 0;
     for (int r = lane; r < S.E; r += 64) {
       const int e = S.inv[r];
       const int m = max(S.offs[e + 1] - S.offs[e], 0);
-      const uint32_t w = (uint32_t)((m + kBK - 1) / kBK + 3);
-      const int c = kchunk_size((x - r) & 7, S.per);
+      int c;
+      uint32_t w;
+      bool sp;
+      piece(m, kchunk_size((x - r) & 7, S.per), c, w, sp);
       tot += (uint64_t)c * w;
       ntiles += c;
       if (c > 0) { wlo = min(wlo, w); whi = max(whi, w); }
@@ -334,15 +389,20 @@ __device__ void balance_kgrouped(int x, int me, int nx, Sched& S) {
     const bool equal = wlo >= whi || (maxload >> 25) != 0;
     uint32_t load = 0;
     int n = 0, pos = 0;       // pos: list position mod nx (equal costs)
+    int sbase = 0;            // split tiles of this XCD so far
     for (int b0 = 0; b0 < S.E; b0 += 64) {
       const int rl = b0 + lane;
-      int cl = 0, fl = 0, rl_rem = 0;
+      int cl = 0, fl = 0, rl_rem = 0, spl = 0, ctl = 0;
       uint32_t wl = 0;
       if (rl < S.E) {
         const int e = S.inv[rl];
         const int m = max(S.offs[e + 1] - S.offs[e], 0);
-        wl = (uint32_t)(((m + kBK - 1) / kBK + 3) >> sh) + 1u;
-        cl = kchunk_size((x - rl) & 7, S.per);
+        uint32_t w;
+        bool sp;
+        ctl = kchunk_size((x - rl) & 7, S.per);
+        piece(m, ctl, cl, w, sp);
+        spl = sp ? 1 : 0;
+        wl = (w >> sh) + 1u;
         fl = cl / nx;
         rl_rem = cl - fl * nx;
       }
@@ -397,13 +457,15 @@ __device__ void balance_kgrouped(int x, int me, int nx, Sched& S) {
           rho = __builtin_amdgcn_readlane(rank, me);
         }
         const int cnt = full + (rho < rem ? 1 : 0);
+        const int sp = __builtin_amdgcn_readlane(spl, i);
         if (cnt > 0) {
           if (lane == 0) {
-            S.mine[2 * n] = (b0 + i) | (rho << 16);
+            S.mine[2 * n] = (b0 + i) | (rho << 16) | (sbase << 22) | (sp << 27);
             S.mine[2 * n + 1] = cnt;
           }
           ++n;
         }
+        if (sp) sbase += __builtin_amdgcn_readlane(ctl, i);
       }
     }
     if (lane == 0) S.keys[0] = n;
@@ -487,11 +549,24 @@ struct TileSeq {
 
   // Next tile of this workgroup; false once the list is exhausted.
   __device__ __forceinline__ bool next(const Sched& S, Tile& t) {
+    t.split = -1;
     if (MODE == kWgrad) {
       if (ie >= S.nmine) return false;
+      // entry: rank (bits 0-9), rho (16-21), first split-tile index (22-26), split (27)
       const int rr = S.mine[2 * ie], cnt = S.mine[2 * ie + 1];
-      const int r = rr & 0xFFFF, rho = rr >> 16;
-      decode_kgrouped<BP, BQ>(r, (x - r) & 7, rho + j * nx, S, t);
+      const int r = rr & 0x3FF, rho = (rr >> 16) & 63, sbase = (rr >> 22) & 31;
+      const bool sp = (rr >> 27) & 1;
+      const int v = rho + j * nx;                 // piece of the chunk
+      const int u = sp ? v >> 1 : v;
+      decode_kgrouped<BP, BQ>(r, (x - r) & 7, u, S, t);
+      if (sp) {
+        // halves of the token range, split at a stage boundary
+        const int st = (t.r_end - t.r_begin + kBK - 1) / kBK;
+        const int mid = t.r_begin + ((st + 1) / 2) * kBK;
+        if (v & 1) t.r_begin = mid;
+        else t.r_end = mid;
+        t.split = ((x * kSplitPerXcd + sbase + u) << 1) | (v & 1);
+      }
       if (++j == cnt) { j = 0; ++ie; }
     } else {
       const int s = c + j * nx;
@@ -505,6 +580,7 @@ struct TileSeq {
     t.p0 = __builtin_amdgcn_readfirstlane(t.p0);
     t.r_begin = __builtin_amdgcn_readfirstlane(t.r_begin);
     t.r_end = __builtin_amdgcn_readfirstlane(t.r_end);
+    t.split = __builtin_amdgcn_readfirstlane(t.split);
     return true;
   }
 };
@@ -798,86 +874,146 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
     y = r[1];
   };
   const int l16 = lane & 15, pa = (lane >> 4) & 1, pb = lane >> 5;
-  auto store_tile = [&](const Tile& t) {
+  // Result block (i, j) held in `blk` (the register layout of acc[i][j]).
+  auto store_block = [&](const Tile& t, int i, int j, const f32x16& blk) {
     if (MODE == kWgrad) {
-      if (a.accumulate && t.r_end <= t.r_begin) return;   // adds nothing
       float* out = reinterpret_cast<float*>(a.out) + (int64_t)t.e * a.N * a.K;
       const int c = pb + 2 * pa;                          // chunk of groups 0 and 1
+      // (each element goes through a named float: this compiler lowers
+      // __builtin_bit_cast of an ext_vector element as a copy of element 0)
+      uint32_t v[4][4];
 #pragma unroll
-      for (int j = 0; j < C::MQ; ++j) {
+      for (int g = 0; g < 4; ++g)
 #pragma unroll
-        for (int i = 0; i < C::MP; ++i) {
-          // (each element goes through a named float: this compiler lowers
-          // __builtin_bit_cast of an ext_vector element as a copy of element 0)
-          uint32_t v[4][4];
-#pragma unroll
-          for (int g = 0; g < 4; ++g)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float f = acc[i][j][4 * g + e];
-              v[g][e] = __builtin_bit_cast(uint32_t, f);
-            }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            swap16(v[0][e], v[1][e]);
-            swap16(v[2][e], v[3][e]);
-          }
-          const int n0 = t.q0 + wq * C::WTQ + j * 32 + l16;
-          const int k0 = t.p0 + wp * C::WTP + i * 32 + 4 * c;
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int n = n0 + 16 * (g & 1), k = k0 + 16 * (g >> 1);
-            if (n >= Qdim || k >= Pdim) continue;
-            f32x4 r = {__builtin_bit_cast(float, v[g][0]), __builtin_bit_cast(float, v[g][1]),
-                       __builtin_bit_cast(float, v[g][2]), __builtin_bit_cast(float, v[g][3])};
-            f32x4* dst = reinterpret_cast<f32x4*>(out + (int64_t)n * a.K + k);
-            if (a.accumulate) r += *dst;
-            *dst = r;
-          }
+        for (int e = 0; e < 4; ++e) {
+          const float f = blk[4 * g + e];
+          v[g][e] = __builtin_bit_cast(uint32_t, f);
         }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        swap16(v[0][e], v[1][e]);
+        swap16(v[2][e], v[3][e]);
+      }
+      const int n0 = t.q0 + wq * C::WTQ + j * 32 + l16;
+      const int k0 = t.p0 + wp * C::WTP + i * 32 + 4 * c;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + 16 * (g & 1), k = k0 + 16 * (g >> 1);
+        if (n >= Qdim || k >= Pdim) continue;
+        f32x4 r = {__builtin_bit_cast(float, v[g][0]), __builtin_bit_cast(float, v[g][1]),
+                   __builtin_bit_cast(float, v[g][2]), __builtin_bit_cast(float, v[g][3])};
+        f32x4* dst = reinterpret_cast<f32x4*>(out + (int64_t)n * a.K + k);
+        if (a.accumulate) r += *dst;
+        *dst = r;
       }
     } else {
       uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
       const int ldo = Pdim;
       const int c = 4 * pa + 2 * pb;                      // first of the lane's two chunks
+      uint32_t v[4][2];
 #pragma unroll
-      for (int j = 0; j < C::MQ; ++j) {
+      for (int g = 0; g < 4; ++g) {
+        const bf16x2 lo = __builtin_convertvector((f32x2){blk[4 * g], blk[4 * g + 1]}, bf16x2);
+        const bf16x2 hi =
+            __builtin_convertvector((f32x2){blk[4 * g + 2], blk[4 * g + 3]}, bf16x2);
+        v[g][0] = __builtin_bit_cast(uint32_t, lo);
+        v[g][1] = __builtin_bit_cast(uint32_t, hi);
+      }
 #pragma unroll
-        for (int i = 0; i < C::MP; ++i) {
-          uint32_t v[4][2];
+      for (int e = 0; e < 2; ++e) {
+        swap16(v[0][e], v[2][e]);
+        swap16(v[1][e], v[3][e]);
+      }
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const bf16x2 lo = __builtin_convertvector(
-                (f32x2){acc[i][j][4 * g], acc[i][j][4 * g + 1]}, bf16x2);
-            const bf16x2 hi = __builtin_convertvector(
-                (f32x2){acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]}, bf16x2);
-            v[g][0] = __builtin_bit_cast(uint32_t, lo);
-            v[g][1] = __builtin_bit_cast(uint32_t, hi);
-          }
+      for (int e = 0; e < 2; ++e) {
+        swap32(v[0][e], v[1][e]);
+        swap32(v[2][e], v[3][e]);
+      }
+      const int m0 = t.q0 + wq * C::WTQ + j * 32 + l16;
+      const int col = t.p0 + wp * C::WTP + i * 32 + 4 * c;
+      if (col >= Pdim) return;
 #pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            swap16(v[0][e], v[2][e]);
-            swap16(v[1][e], v[3][e]);
-          }
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            swap32(v[0][e], v[1][e]);
-            swap32(v[2][e], v[3][e]);
-          }
-          const int m0 = t.q0 + wq * C::WTQ + j * 32 + l16;
-          const int col = t.p0 + wp * C::WTP + i * 32 + 4 * c;
-          if (col >= Pdim) continue;
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const int m = m0 + 16 * half;
-            if (m >= t.q_end) continue;
-            const u32x4 pk = {v[2 * half][0], v[2 * half][1], v[2 * half + 1][0],
-                              v[2 * half + 1][1]};
-            *reinterpret_cast<u32x4*>(out + (int64_t)m * ldo + col) = pk;
-          }
-        }
+      for (int half = 0; half < 2; ++half) {
+        const int m = m0 + 16 * half;
+        if (m >= t.q_end) continue;
+        const u32x4 pk = {v[2 * half][0], v[2 * half][1], v[2 * half + 1][0],
+                          v[2 * half + 1][1]};
+        *reinterpret_cast<u32x4*>(out + (int64_t)m * ldo + col) = pk;
       }
     }
+  };
+  auto store_tile = [&](const Tile& t) {
+    if (MODE == kWgrad && a.accumulate && t.r_end <= t.r_begin) return;   // adds nothing
+#pragma unroll
+    for (int j = 0; j < C::MQ; ++j)
+#pragma unroll
+      for (int i = 0; i < C::MP; ++i) store_block(t, i, j, acc[i][j]);
+  };
+
+  // ---- end of a half of a split K-grouped tile.  Each half writes its fp32
+  // accumulators to its own workspace slot (in register order: entry
+  // (i MQ + j) 4 + g of thread tid at ((i MQ + j) 4 + g) NT + tid), waits for
+  // the writes and takes the tile's ticket; the half that draws the second
+  // ticket stores (own + other) -- a commutative sum, so the result does not
+  // depend on which half ends last -- plus the prior value when accumulating,
+  // and resets the ticket for the next launch.  Nothing waits for another
+  // workgroup.  The slots are written and read with device-coherent accesses
+  // (cache policy sc1, what device-scope atomic loads and stores compile to),
+  // so no cache is written back or invalidated; the ticket is a device-scope
+  // atomic add.
+  constexpr int kSlotFloats = C::BP * C::BQ;
+  constexpr int kCoherent = 16;                 // cache policy bit sc1
+  auto finish_half = [&](const Tile& t) {
+    const int sid = t.split >> 1, half = t.split & 1;
+    // (an opaque zero added to the constant entry offsets keeps the compiler
+    // from hoisting 32 of them into registers for the whole kernel)
+    int z;
+    asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+    auto slot_rsrc = [&](int slot) {
+      return __builtin_amdgcn_make_buffer_rsrc(a.ws + (int64_t)slot * kSlotFloats, (short)0,
+                                               kSlotFloats * 4, 0x00020000);
+    };
+    {
+      const auto rs = slot_rsrc(2 * sid + half);
+#pragma unroll
+      for (int ii = 0; ii < C::MP; ++ii)
+#pragma unroll
+        for (int jj = 0; jj < C::MQ; ++jj)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4 v = {acc[ii][jj][4 * g4], acc[ii][jj][4 * g4 + 1], acc[ii][jj][4 * g4 + 2],
+                             acc[ii][jj][4 * g4 + 3]};
+            __builtin_amdgcn_raw_buffer_store_b128(
+                __builtin_bit_cast(i32x4, v), rs, tid * 16,
+                z + ((ii * C::MQ + jj) * 4 + g4) * C::NT * 16, kCoherent);
+          }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    uint32_t* ticket = a.tickets + sid;
+    if (tid == 0)
+      S.scan[8] = (int)__hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (S.scan[8] == 0) return;                 // the other half finishes the tile
+    const auto rs = slot_rsrc(2 * sid + (half ^ 1));
+#pragma unroll
+    for (int jj = 0; jj < C::MQ; ++jj)
+#pragma unroll
+      for (int ii = 0; ii < C::MP; ++ii) {
+        f32x4 v[4];
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          v[g4] = __builtin_bit_cast(
+              f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                         rs, tid * 16, z + ((ii * C::MQ + jj) * 4 + g4) * C::NT * 16, kCoherent));
+        const f32x8 lo = __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7);
+        const f32x8 hi = __builtin_shufflevector(v[2], v[3], 0, 1, 2, 3, 4, 5, 6, 7);
+        const f32x16 other = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10,
+                                                     11, 12, 13, 14, 15);
+        store_block(t, ii, jj, acc[ii][jj] + other);
+      }
+    if (tid == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
 
   // ---- pipeline.  Stage g is consumed in KK k-slices; while slice kk's
@@ -933,7 +1069,8 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
         }
       }
     }
-    store_tile(ct);
+    if (MODE == kWgrad && ct.split >= 0) finish_half(ct);
+    else store_tile(ct);
 #pragma unroll
     for (int i = 0; i < C::MP; ++i)
 #pragma unroll
@@ -982,6 +1119,7 @@ void grouped_gemm_kernel(KernelArgs a) {
   int bw = 1;
   while (bw < S.tilesP && 2 * (2 * bw + 1) * (2 * bw + 1) <= S.per) ++bw;
   S.bw = bw;
+  S.split = MODE == kWgrad && a.ws != nullptr && a.tickets != nullptr;
   if (MODE == kWgrad) {
     setup_kgrouped<C::NT>(a.offsets, E, (int)a.M, S);
     balance_kgrouped<C::NT>(blockIdx.x & 7, blockIdx.x >> 3, nx, S);
@@ -1015,7 +1153,63 @@ static int device_cus() {
   return n;
 }
 
-int launch_grouped(int mode, const KernelArgs& a, int64_t max_m_per_e, hipStream_t s) {
+// Token-split workspace of one (device, stream): the ticket counters (zeroed
+// once here; every launch leaves them zeroed) followed by two fp32 slots of
+// one tile per split tile.  Launches on one stream run in order and share it;
+// launches on different streams get different workspaces.  Allocated on the
+// first K-grouped launch of the pair and kept until the process ends.
+constexpr int kSplitTiles = 8 * kSplitPerXcd;
+constexpr size_t kTicketBytes = 4096;
+static_assert(kSplitTiles * sizeof(uint32_t) <= kTicketBytes, "ticket area");
+struct Workspace {
+  int dev;
+  hipStream_t stream;
+  char* base;
+};
+static std::mutex g_ws_mutex;
+static std::vector<Workspace> g_ws;
+
+static char* stream_workspace(hipStream_t s) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  for (const Workspace& w : g_ws)
+    if (w.dev == dev && w.stream == s) return w.base;
+  const size_t bytes = kTicketBytes + (size_t)2 * kSplitTiles * Cfg::BP * Cfg::BQ * sizeof(float);
+  void* p = nullptr;
+  if (hipMalloc(&p, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;                       // no workspace: launches do not split
+  }
+  if (hipMemsetAsync(p, 0, kTicketBytes, s) != hipSuccess) {
+    (void)hipGetLastError();
+    (void)hipFree(p);
+    return nullptr;
+  }
+  g_ws.push_back({dev, s, static_cast<char*>(p)});
+  return static_cast<char*>(p);
+}
+
+// MGEMM_SPLIT=0 turns the token split off (every tile is then computed whole).
+static bool split_enabled() {
+  static const bool on = [] {
+    const char* v = std::getenv("MGEMM_SPLIT");
+    return !(v != nullptr && v[0] == '0');
+  }();
+  return on;
+}
+
+int launch_grouped(int mode, const KernelArgs& a_in, int64_t max_m_per_e, hipStream_t s) {
+  KernelArgs a = a_in;
+  a.ws = nullptr;
+  a.tickets = nullptr;
+  if (mode == kWgrad && a.M > 0 && split_enabled()) {
+    char* w = stream_workspace(s);
+    if (w != nullptr) {
+      a.tickets = reinterpret_cast<uint32_t*>(w);
+      a.ws = reinterpret_cast<float*>(w + kTicketBytes);
+    }
+  }
   int64_t tiles;
   if (mode == kWgrad) {
     const int64_t tilesP = (a.K + Cfg::BP - 1) / Cfg::BP;

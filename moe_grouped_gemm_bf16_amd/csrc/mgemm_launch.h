@@ -19,6 +19,8 @@ struct KernelArgs {
   int64_t M, N, K;
   int32_t E;
   int32_t accumulate;       // WGRAD only: add into `out`
+  float* ws;                // WGRAD token split: 2 slots of 256 x 256 fp32 per split tile
+  uint32_t* tickets;        // one zeroed counter per split tile (every launch leaves them zeroed)
 };
 
 // Enqueue one grouped GEMM on stream `s`.  Returns a hipError_t value.

@@ -106,6 +106,10 @@ WG_CASES = [
     ([70, 0, 5], 4096, 4096),
     # the largest expert count
     ([int(v) for v in np.random.default_rng(9).integers(0, 9, 1024)], 8, 24),
+    # one expert much heavier than the rest: its tiles are split in two token
+    # halves (odd stage count, ragged last stage, ragged N and K, empty experts)
+    ([2017, 33, 65, 129, 0, 0, 0, 700], 1544, 776),
+    ([2500, 1, 0, 300, 0, 77, 1030, 5], 264, 1032),
 ]
 
 
