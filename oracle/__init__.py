@@ -16,14 +16,22 @@ per expert; nothing blocked, fused or reordered):
     FP32 weight gradient; DeepGEMM issue #10: wgrad is x^T dy):
     dW[e, n, k] = sum_{offsets[e] <= i < offsets[e+1]} dY[i, n] X[i, k],
     laid out like W so that it can update W.
+  * Gate-up forward with SwiGLU on gathered rows (DeepGEMM issue #10: the
+    fused-with-SwiGLU and MoE-layout kernels; RapidGEMM README "Kernels": the
+    stacked gate/up weight gw13 refers to): row i reads token row gather[i],
+    h[i, j] = silu(x . w1[e, j]) * (x . w3[e, j]) with w1, w3 the two halves of
+    the expert's [2I, K] weight.
   * bf16 outputs are the fp64 result rounded once, directly, to bf16 with
     round-to-nearest-even.
 
 Pins (tests/test_oracle_pins.py): exact rational brute force on tiny inputs,
 closed forms on one-hot inputs, a hand-worked example (tests/golden/), the
 adjoint identity tying fwd/dgrad/wgrad together, empty-group insertion,
-exhaustive codec round trips and tie cases.  Every function here is pinned;
-none is "parity unpinned".
+exhaustive codec round trips and tie cases; for the SwiGLU forward, scalar
+brute force with math.exp, one-hot closed forms that tell the gate half from
+the up half, gather-as-permutation identities, and a gate that rejects a wrong
+expert or a dropped term.  Every function here is pinned; none is "parity
+unpinned".
 """
 from .bf16 import bf16_bits_to_f64, f64_to_bf16_bits, bf16_ulp  # noqa: F401
 from .grouped_gemm import (  # noqa: F401
@@ -33,5 +41,7 @@ from .grouped_gemm import (  # noqa: F401
     sample_fwd,
     sample_dgrad,
     sample_wgrad,
+    grouped_fwd_swiglu,
+    sample_fwd_swiglu,
 )
-from .gate import check_bf16, check_fp32, GateReport  # noqa: F401
+from .gate import check_bf16, check_bf16_swiglu, check_fp32, GateReport  # noqa: F401

@@ -16,6 +16,15 @@ it is far above what a sane kernel produces on non-cancelling elements, and
 far below the error of a dropped term, a wrong index or a wrong expert.  The
 strict-failure count is reported next to the pass/fail verdict.
 
+bf16 outputs of the fused SwiGLU forward, h = silu(g) u.  Same strict gate;
+the floor carries the fp32 summation error of g and of u through the
+activation to first order, plus a few fp32 roundings of exp, divide and
+multiply:
+
+    |h_got - h| <= ulp(h_got) / 2 + |silu'(g) u| dg + |silu(g)| du + 2^-20 |h|,
+    dg = 2^-24 sqrt(K) S_g,  du = 2^-24 sqrt(K) S_u,
+    silu'(g) = s (1 + g (1 - s)),  s = 1 / (1 + exp(-g)).
+
 fp32 outputs (wgrad).  Relative Frobenius error <= 1e-4, over the whole
 tensor and per expert (a large expert would otherwise hide a wrong small
 one); an empty expert's block must be exactly zero (or exactly the prior
@@ -63,6 +72,28 @@ def check_bf16(got_bits: np.ndarray, exact: np.ndarray, abs_sum: np.ndarray,
         i = int(np.argmax(np.where(ok, -np.inf, np.abs(g - exact))))
         worst = f"worst@{i}: got={g.flat[i]!r} exact={exact.flat[i]!r}"
     return GateReport(int(g.size), fails == 0, fails, int((~strict).sum()), 0.0, worst)
+
+
+def check_bf16_swiglu(got_bits: np.ndarray, h: np.ndarray, g: np.ndarray, u: np.ndarray,
+                      sum_g: np.ndarray, sum_u: np.ndarray, k_red) -> GateReport:
+    """Gate for the bf16 output of the fused SwiGLU forward (see the header)."""
+    got = bf16_bits_to_f64(got_bits)
+    h = np.asarray(h, np.float64); g = np.asarray(g, np.float64); u = np.asarray(u, np.float64)
+    b = f64_round_bf16(h)
+    strict = np.abs(got - b) <= bf16_ulp(b)
+    with np.errstate(over="ignore"):
+        sg = 1.0 / (1.0 + np.exp(-g))
+    dsilu = sg * (1.0 + g * (1.0 - sg))
+    dg = U32 * np.sqrt(k_red) * sum_g
+    du = U32 * np.sqrt(k_red) * sum_u
+    bound = 0.5 * bf16_ulp(got) + np.abs(dsilu * u) * dg + np.abs(g * sg) * du + 2.0 ** -20 * np.abs(h)
+    ok = (strict | (np.abs(got - h) <= bound)) & np.isfinite(got)
+    fails = int((~ok).sum())
+    worst = ""
+    if fails:
+        i = int(np.argmax(np.where(ok, -np.inf, np.abs(got - h))))
+        worst = f"worst@{i}: got={got.flat[i]!r} exact={h.flat[i]!r}"
+    return GateReport(int(got.size), fails == 0, fails, int((~strict).sum()), 0.0, worst)
 
 
 def rel_frob(got: np.ndarray, exact: np.ndarray) -> float:

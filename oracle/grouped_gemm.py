@@ -73,6 +73,57 @@ def grouped_wgrad(dy: np.ndarray, x: np.ndarray, offsets, E: int,
     return dw
 
 
+def _silu(g: np.ndarray) -> np.ndarray:
+    """silu(g) = g * sigmoid(g) = g / (1 + exp(-g)); exp overflow gives -0."""
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
+def grouped_fwd_swiglu(x: np.ndarray, gather, w13: np.ndarray, offsets) -> np.ndarray:
+    """Gate-up forward with the SwiGLU activation, on gathered rows (fp64).
+
+    The DeepGEMM issue #10 thread names the fused kernels an MoE weight-gradient
+    path needs -- with casting, with SwiGLU, with the MoE layout -- and the
+    RapidGEMM README ("Kernels") calls the first FFN weight gradient gw13: the
+    gate (w1) and up (w3) weights of each expert stacked as one [2I, K] matrix,
+    w1 in rows 0..I-1 and w3 in rows I..2I-1.  Row i of the expert-grouped
+    problem is token row gather[i] of x (gather None: x is already grouped).
+    For offsets[e] <= i < offsets[e+1]:
+        g = x[gather[i]] . w13[e, j],   u = x[gather[i]] . w13[e, I + j],
+        h[i, j] = silu(g) * u,  silu(g) = g / (1 + exp(-g))        (j < I)
+    Rows at or past offsets[E] are NaN."""
+    rows = x if gather is None else x[np.asarray(gather, np.int64)]
+    M, K = rows.shape
+    E, N2, K2 = w13.shape
+    assert K == K2 and N2 % 2 == 0
+    I = N2 // 2
+    o = _check_offsets(offsets, E, M)
+    h = np.full((M, I), np.nan)
+    for e in range(E):
+        lo, hi = o[e], o[e + 1]
+        if hi > lo:
+            g = rows[lo:hi] @ w13[e, :I].T
+            u = rows[lo:hi] @ w13[e, I:].T
+            h[lo:hi] = _silu(g) * u
+    return h
+
+
+def sample_fwd_swiglu(x: np.ndarray, gather, w13: np.ndarray, offsets, rows, cols):
+    """h[rows[j], cols[j]] of grouped_fwd_swiglu one element at a time, fp64.
+
+    Returns (h, g, u, sum |x w1|, sum |x w3|) for the parity gate."""
+    rows = np.asarray(rows); cols = np.asarray(cols)
+    e = expert_of_rows(offsets, rows)
+    assert (e >= 0).all()
+    I = w13.shape[1] // 2
+    src = rows if gather is None else np.asarray(gather, np.int64)[rows]
+    xr = _f64(x[src])
+    pg = xr * _f64(w13[e, cols])
+    pu = xr * _f64(w13[e, I + cols])
+    g, u = pg.sum(axis=1), pu.sum(axis=1)
+    return _silu(g) * u, g, u, np.abs(pg).sum(axis=1), np.abs(pu).sum(axis=1)
+
+
 def expert_of_rows(offsets, rows: np.ndarray) -> np.ndarray:
     """Expert index owning each row (rows past offsets[E] give -1)."""
     o = np.asarray(offsets, dtype=np.int64)

@@ -12,7 +12,10 @@ codec -- fails at least one of them:
     issue #10);
   * inserting an empty group changes nothing;
   * exhaustive and tie-case checks of the bf16 codec, and agreement with
-    torch's own float32 -> bfloat16 rounding on float32-representable values.
+    torch's own float32 -> bfloat16 rounding on float32-representable values;
+  * for the gate-up forward with SwiGLU on gathered rows: scalar brute force,
+    one-hot closed forms (swapping the gate and up halves must change the
+    result), gather-as-permutation identities, sampler/gate consistency.
 """
 import json
 import os
@@ -300,3 +303,127 @@ def test_rational_rounding_matches_codec_on_random_values():
     v = rng.standard_normal(2000) * np.exp2(rng.integers(-140, 120, 2000))
     for x in v:
         assert float(frac_round_bf16(Fraction(float(x)))) == float(f64_round_bf16(np.array(x)))
+
+
+# ------------------------------------------- gate-up forward with SwiGLU --
+
+def brute_swiglu(x, gather, w13, offsets):
+    """Scalar loops with math.exp: an implementation written apart from the
+    oracle's (no matmul, no vector code), for tiny inputs."""
+    import math
+    E, N2, K = w13.shape
+    I = N2 // 2
+    M = len(gather) if gather is not None else x.shape[0]
+    out = [[None] * I for _ in range(M)]
+    for e in range(E):
+        for i in range(int(offsets[e]), int(offsets[e + 1])):
+            src = int(gather[i]) if gather is not None else i
+            for j in range(I):
+                g = 0.0
+                u = 0.0
+                for k in range(K):
+                    g += float(x[src, k]) * float(w13[e, j, k])
+                    u += float(x[src, k]) * float(w13[e, I + j, k])
+                out[i][j] = g / (1.0 + math.exp(-g)) * u
+    return out
+
+
+@pytest.mark.parametrize("sizes,T,K,I,seed", [
+    ([3, 0, 2], 7, 5, 4, 1),
+    ([1, 4], 5, 8, 3, 2),
+    ([0, 0, 6, 1], 9, 3, 2, 3),
+])
+def test_swiglu_brute_force(sizes, T, K, I, seed):
+    from oracle import grouped_fwd_swiglu
+    rng = np.random.default_rng(seed)
+    E = len(sizes)
+    off = offsets_from_sizes(sizes)
+    M = int(off[-1]) + 2                       # two rows past the last offset
+    x = bf16_bits_to_f64(normal_bf16_bits((T, K), 1.0, seed, 1))
+    w13 = bf16_bits_to_f64(normal_bf16_bits((E, 2 * I, K), 1.0, seed, 2))
+    gather = rng.integers(0, T, M)              # repeats allowed (top-k routing)
+    h = grouped_fwd_swiglu(x, gather, w13, off)
+    ref = brute_swiglu(x, gather, w13, off)
+    for i in range(M):
+        for j in range(I):
+            if ref[i][j] is None:
+                assert np.isnan(h[i, j])
+            else:
+                assert h[i, j] == pytest.approx(ref[i][j], rel=1e-12, abs=1e-14)
+
+
+def test_swiglu_closed_forms_and_halves():
+    """One-hot rows pick single weights: h = silu(a) b exactly as math gives
+    it; swapping the two halves of w13 gives silu(b) a (a transposed or
+    mixed-up half fails here); silu(0) = 0 and silu is odd-symmetric around
+    the sigmoid: silu(t) - silu(-t) = t."""
+    import math
+    from oracle import grouped_fwd_swiglu
+    K, I, E = 4, 3, 2
+    x = np.eye(K)                               # token t is one-hot at k = t
+    w13 = np.zeros((E, 2 * I, K))
+    for e in range(E):
+        for j in range(I):
+            for k in range(K):
+                w13[e, j, k] = 0.5 * (1 + e) + 0.25 * j - 0.75 * k      # w1
+                w13[e, I + j, k] = 1.0 - 0.125 * (j + k) + e           # w3
+    gather = np.array([3, 0, 2, 1, 1])
+    off = np.array([0, 2, 5])
+    h = grouped_fwd_swiglu(x, gather, w13, off)
+    swapped = np.concatenate([w13[:, I:], w13[:, :I]], axis=1)
+    hs = grouped_fwd_swiglu(x, gather, swapped, off)
+    for i in range(5):
+        e = 0 if i < 2 else 1
+        k = int(gather[i])
+        for j in range(I):
+            a, b = w13[e, j, k], w13[e, I + j, k]
+            assert h[i, j] == pytest.approx(a / (1 + math.exp(-a)) * b, rel=1e-15)
+            assert hs[i, j] == pytest.approx(b / (1 + math.exp(-b)) * a, rel=1e-15)
+    zero_gate = w13.copy(); zero_gate[:, :I] = 0.0
+    assert (grouped_fwd_swiglu(x, gather, zero_gate, off) == 0.0).all()
+    t = np.linspace(-30.0, 30.0, 61)
+    from oracle.grouped_gemm import _silu
+    assert np.allclose(_silu(t) - _silu(-t), t, rtol=0, atol=1e-12)
+
+
+def test_swiglu_gather_is_a_row_permutation():
+    """Gathering token rows equals grouping them first; reordering the tokens
+    (and remapping the index) changes nothing."""
+    from oracle import grouped_fwd_swiglu
+    rng = np.random.default_rng(11)
+    T, K, I = 13, 6, 5
+    off = offsets_from_sizes([4, 0, 7])
+    x = bf16_bits_to_f64(normal_bf16_bits((T, K), 1.0, 11, 1))
+    w13 = bf16_bits_to_f64(normal_bf16_bits((3, 2 * I, K), 1.0, 11, 2))
+    gather = rng.integers(0, T, int(off[-1]))
+    h = grouped_fwd_swiglu(x, gather, w13, off)
+    np.testing.assert_array_equal(h, grouped_fwd_swiglu(x[gather], None, w13, off))
+    perm = rng.permutation(T)
+    inv = np.argsort(perm)
+    np.testing.assert_array_equal(h, grouped_fwd_swiglu(x[perm], inv[gather], w13, off))
+
+
+def test_swiglu_sampler_and_gate():
+    """The one-element sampler agrees with the full oracle, and the gate
+    accepts the correctly rounded result but rejects a wrong expert's and a
+    dropped term's."""
+    from oracle import check_bf16_swiglu, grouped_fwd_swiglu, sample_fwd_swiglu
+    rng = np.random.default_rng(5)
+    T, K, I = 40, 64, 24
+    off = offsets_from_sizes([10, 0, 25, 5])
+    xb = normal_bf16_bits((T, K), K ** -0.5, 5, 1)
+    wb = normal_bf16_bits((4, 2 * I, K), K ** -0.5, 5, 2)
+    x, w13 = bf16_bits_to_f64(xb), bf16_bits_to_f64(wb)
+    gather = rng.integers(0, T, int(off[-1]))
+    h = grouped_fwd_swiglu(x, gather, w13, off)
+    rows = np.repeat(np.arange(int(off[-1])), I)
+    cols = np.tile(np.arange(I), int(off[-1]))
+    hs, g, u, sg, su = sample_fwd_swiglu(xb, gather, wb, off, rows, cols)
+    np.testing.assert_allclose(hs, h[rows, cols], rtol=1e-13, atol=1e-15)
+    good = f64_to_bf16_bits(h[rows, cols])
+    assert check_bf16_swiglu(good, hs, g, u, sg, su, K).passed
+    wrong_expert = grouped_fwd_swiglu(x, gather, w13[[1, 0, 3, 2]], off)
+    assert not check_bf16_swiglu(f64_to_bf16_bits(wrong_expert[rows, cols]), hs, g, u, sg, su, K).passed
+    w_drop = w13.copy(); w_drop[:, :, K - 1] = 0.0
+    dropped = grouped_fwd_swiglu(x, gather, w_drop, off)
+    assert not check_bf16_swiglu(f64_to_bf16_bits(dropped[rows, cols]), hs, g, u, sg, su, K).passed
