@@ -1,6 +1,8 @@
 """Build libmgemm.so in-tree with hipcc for gfx950.
 
-    python -m moe_grouped_gemm_bf16_amd.build [--verbose]
+    python moe_grouped_gemm_bf16_amd/build.py [--verbose]
+
+(run as a script: importing the package would load the library first).
 
 Always recompiles (it is the "does it build" check as well as the build).
 """
