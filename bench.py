@@ -35,7 +35,7 @@ PEAK_BF16_TFLOPS = 2500.0        # MI355X published dense bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 KERNEL_SRC = os.path.join(ROOT, "moe_grouped_gemm_bf16_amd", "csrc", "mgemm_kernels.hip")
 KERNEL_NAMES = {"fwd": "grouped_gemm_kernel<0>", "dgrad": "grouped_gemm_kernel<1>",
-                "wgrad": "grouped_gemm_kernel<2>"}
+                "wgrad": "grouped_gemm_kernel<2>", "fwd_swiglu": "grouped_gemm_kernel<3>"}
 
 
 def kernel_hash() -> str:
@@ -57,6 +57,9 @@ def parse_args():
                    help="run one plain 1 GiB device copy (for HBM counter calibration)")
     p.add_argument("--comparators", action="store_true",
                    help="also time library baselines on the same inputs (reported only)")
+    p.add_argument("--fusions", action="store_true",
+                   help="also time the gate-up forward with gathered rows and fused SwiGLU "
+                        "against the unfused sequence (reported only)")
     return p.parse_args()
 
 
@@ -177,6 +180,63 @@ def comparators(ops, torch, reps=20):
         out[op.name] = rec
         torch.cuda.empty_cache()
     return out
+
+
+# ------------------------------------------------------------------ fusions --
+
+def fusions(torch, mg, reps=20):
+    """The 30B-A3B share's gate-up GEMM as a trainer runs it: 16384 token rows
+    x [16384, 3072] gathered by the router's row-to-token map into 32 expert
+    groups, w13 [32, 2560, 3072], SwiGLU: h [M, 1280].  Fused: one
+    mgemm_fwd_swiglu launch.  Unfused: torch index_select of the rows, the
+    plain grouped forward to [M, 2560], torch silu(g) * u.  Reported beside
+    the step, never part of `value`."""
+    import numpy as np
+    from workloads import make_workload, normal_bf16_bits
+    from workloads.synth import router_offsets
+    off_np, tok = router_offsets(16384, 128, 8, 32, seed=4)
+    (wl,) = [w for w in make_workload(4) if w.name == "a3b_gate_up"]
+    T, K, I = 16384, 3072, 1280
+    up = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).cuda()
+    x, w13 = up(normal_bf16_bits((T, K), 1.0, 4, 9, 1)), up(wl.w_bits())
+    off = torch.from_numpy(off_np).cuda()
+    gi = torch.from_numpy(tok).cuda()
+    gl = gi.long()
+    M = int(off_np[-1])
+    hint = int(np.diff(off_np).max())
+    h = torch.empty((M, I), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((M, 2 * I), dtype=torch.bfloat16, device="cuda")
+
+    def fused():
+        mg.fwd_swiglu(x, w13, off, gather=gi, max_m_per_e=hint, out=h)
+
+    def unfused():
+        xg = x.index_select(0, gl)
+        mg.fwd(xg, w13, off, hint, out=y)
+        torch.nn.functional.silu(y[:, :I]) * y[:, I:]
+
+    # the two are timed interleaved (one of each per round), so that both see
+    # the same clock and cache state
+    for _ in range(5):
+        fused()
+        unfused()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(2)] for _ in range(reps)]
+    for pair in ev:
+        for (a, b), fn in zip(pair, (fused, unfused)):
+            a.record()
+            fn()
+            b.record()
+    torch.cuda.synchronize()
+    tf = statistics.median(p[0][0].elapsed_time(p[0][1]) for p in ev) * 1e3
+    tu = statistics.median(p[1][0].elapsed_time(p[1][1]) for p in ev) * 1e3
+    flops = 2 * M * (2 * I) * K
+    return {"fwd_swiglu_gathered:a3b_gate_up": {
+        "rows": M, "tokens": T, "fused_us": round(tf, 1), "tflops": round(flops / tf / 1e6, 1),
+        "pct_peak": round(100 * flops / tf / 1e6 / PEAK_BF16_TFLOPS, 1),
+        "unfused_us": round(tu, 1), "speedup": round(tu / tf, 3),
+        "unfused": "torch index_select + mgemm_fwd [M, 2560] + torch silu(g) * u"}}
 
 
 # ------------------------------------------------------------- CPU baseline --
@@ -330,6 +390,11 @@ def main():
         print("[bench] timing library comparators", file=sys.stderr, flush=True)
         comp = comparators(ops, torch)
 
+    fused = None
+    if args.fusions:
+        print("[bench] timing the fused gate-up forward", file=sys.stderr, flush=True)
+        fused = fusions(torch, mg)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
@@ -365,6 +430,8 @@ def main():
     }
     if comp is not None:
         line["comparators"] = comp
+    if fused is not None:
+        line["fused_ops"] = fused
     print(json.dumps(line), flush=True)
 
 

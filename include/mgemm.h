@@ -87,6 +87,25 @@ mg_status mgemm_dgrad(const void* dy, const void* w, const int32_t* offsets, voi
                       int64_t M, int64_t N, int64_t K, int32_t E, int64_t max_m_per_e,
                       void* stream);
 
+/* Gate-up forward with the SwiGLU activation fused into the epilogue, on rows
+ * gathered through an index (the fused-with-SwiGLU and MoE-layout kernels of
+ * the DeepGEMM issue #10 thread; w13 stacks each expert's gate and up weights
+ * as the RapidGEMM README's gw13 gradient does):
+ *   g = x[r] . w13[e, j],  u = x[r] . w13[e, I + j],  r = gather ? gather[i] : i
+ *   h[i, j] = silu(g) * u = g u / (1 + exp(-g))   for offsets[e] <= i < offsets[e+1]
+ * x: bf16 [T, K] when gather != NULL (token-major rows; gather: int32 DEVICE
+ * array [M] of row indices in [0, T), repeats allowed), else bf16 [M, K]
+ * (already expert-grouped; T is ignored).  w13: bf16 [E, 2I, K], gate rows
+ * 0..I-1, up rows I..2I-1.  h: bf16 [M, I] (written).  fp32 accumulation, the
+ * activation in fp32, one rounding to bf16 (nearest even).  Rows i >=
+ * offsets[E] of h are not touched; an index outside [0, T) reads zeros.
+ * I and K multiples of 8; 2 I K and (with gather) T K below 2^31 elements.
+ * M == 0 or I == 0 is a no-op.  Allocates nothing.  max_m_per_e: launch-size
+ * hint, as for mgemm_fwd. */
+mg_status mgemm_fwd_swiglu(const void* x, const int32_t* gather, const void* w13,
+                           const int32_t* offsets, void* h, int64_t M, int64_t T, int64_t I,
+                           int64_t K, int32_t E, int64_t max_m_per_e, void* stream);
+
 /* K-grouped weight gradient in FP32 (RapidGEMM README, "Kernels", Kgemm;
  * wgrad is x^T dy, DeepGEMM issue #10, laid out like w so it can update w):
  *   dw[e, n, k] (= or +=) sum_{offsets[e] <= i < offsets[e+1]} dy[i, n] * x[i, k]

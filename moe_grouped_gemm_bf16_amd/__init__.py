@@ -7,6 +7,8 @@ kernels; PyTorch provides device memory and the current stream.
   fwd(x, w, offsets)      Y[i] = x[i] W[e]^T          M-grouped forward
   dgrad(dy, w, offsets)   dX[i] = dy[i] W[e]          M-grouped input gradient
   wgrad(dy, x, offsets)   dW[e] = sum_i dy[i]^T x[i]  K-grouped fp32 weight gradient
+  fwd_swiglu(x, w13, offsets, gather)                  gate-up forward, SwiGLU fused,
+      h[i] = silu(x[r] w1[e]^T) * (x[r] w3[e]^T), r = gather[i]   rows gathered by index
 
 Page-shaped aliases follow the RapidGEMM README ("Kernels"):
   Mgemm(x, w, cnt, max_M_per_E, transpose_B) and Kgemm(grad, X, cnt, descriptor).
@@ -17,7 +19,8 @@ import torch
 
 from ._lib import LIB, MgemmError, check, status_str  # noqa: F401
 
-__all__ = ["fwd", "dgrad", "wgrad", "Mgemm", "Kgemm", "MgemmError", "status_str", "LIB"]
+__all__ = ["fwd", "dgrad", "wgrad", "fwd_swiglu", "Mgemm", "Kgemm", "MgemmError", "status_str",
+           "LIB"]
 
 
 def _stream(t: torch.Tensor) -> int:
@@ -124,6 +127,49 @@ def wgrad(dy: torch.Tensor, x: torch.Tensor, offsets: torch.Tensor, E: int | Non
         st = LIB.kgemm_wgrad(dy.data_ptr(), x.data_ptr(), offsets.data_ptr(), out.data_ptr(),
                              M, N, K, E, 1 if accumulate else 0, _stream(dy))
     check(st, "kgemm_wgrad")
+    return out
+
+
+def fwd_swiglu(x: torch.Tensor, w13: torch.Tensor, offsets: torch.Tensor,
+               gather: torch.Tensor | None = None, max_m_per_e: int = 0,
+               out: torch.Tensor | None = None) -> torch.Tensor:
+    """Gate-up forward with SwiGLU fused, on rows gathered through an index.
+
+    w13 bf16 [E, 2I, K] stacks each expert's gate (rows 0..I-1) and up
+    (rows I..2I-1) weights.  With `gather` (int32 [M], device), row i of the
+    expert-grouped problem is x[gather[i]] of the token-major x bf16 [T, K];
+    without it x is bf16 [M, K], already grouped.  Returns h bf16 [M, I]:
+    h[i, j] = silu(g) * u, g = x[r] . w13[e, j], u = x[r] . w13[e, I + j].
+    Rows past offsets[E] of `out` are left untouched."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(w13, "w13", torch.bfloat16, 3)
+    T, K = x.shape
+    E, N2, K2 = w13.shape
+    if K2 != K:
+        raise ValueError(f"x is [T, {K}] but w13 is [E, 2I, {K2}]")
+    if N2 % 2:
+        raise ValueError(f"w13 must stack two halves (2I rows), got {N2}")
+    I = N2 // 2
+    if gather is None:
+        M = T
+        gptr = 0
+    else:
+        _need(gather, "gather", torch.int32, 1)
+        if gather.device != x.device:
+            raise ValueError("gather must be on the same device as the data")
+        M = gather.numel()
+        gptr = gather.data_ptr()
+    _offsets(offsets, E, x.device)
+    if out is None:
+        out = torch.empty((M, I), dtype=torch.bfloat16, device=x.device)
+    else:
+        _need(out, "out", torch.bfloat16, 2)
+        if tuple(out.shape) != (M, I):
+            raise ValueError(f"out must be [{M}, {I}]")
+    with torch.cuda.device(x.device):
+        st = LIB.mgemm_fwd_swiglu(x.data_ptr(), gptr, w13.data_ptr(), offsets.data_ptr(),
+                                  out.data_ptr(), M, T, I, K, E, int(max_m_per_e), _stream(x))
+    check(st, "mgemm_fwd_swiglu")
     return out
 
 

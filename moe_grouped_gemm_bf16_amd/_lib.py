@@ -19,6 +19,7 @@ SIGNATURES = {
     "mgemm_fwd": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i64, _vp]),
     "mgemm_dgrad": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i64, _vp]),
     "kgemm_wgrad": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp]),
+    "mgemm_fwd_swiglu": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32, _i64, _vp]),
     "mg_status_str": (ctypes.c_char_p, [_i32]),
     "mg_abi_version": (_i32, []),
     "mg_check_offsets_host": (_i32, [_vp, _i32, _i64]),
@@ -34,7 +35,7 @@ class MgemmError(RuntimeError):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m moe_grouped_gemm_bf16_amd.build` "
+            f"{LIB_PATH} is missing: build it with `python moe_grouped_gemm_bf16_amd/build.py` "
             "(hipcc, gfx950). There is no fallback implementation.")
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():

@@ -111,6 +111,37 @@ mg_status mgemm_dgrad(const void* dy, const void* w, const int32_t* offsets, voi
   return mgrouped(mg::kDgrad, dy, w, offsets, dx, M, N, K, E, max_m_per_e, stream);
 }
 
+mg_status mgemm_fwd_swiglu(const void* x, const int32_t* gather, const void* w13,
+                           const int32_t* offsets, void* h, int64_t M, int64_t T, int64_t I,
+                           int64_t K, int32_t E, int64_t max_m_per_e, void* stream) {
+  mg_status st = check_sizes(M, 2 * I, K, E);
+  if (st != MG_OK) return st;
+  if (max_m_per_e < 0 || I < 0 || (I & 7)) return MG_ERR_SHAPE;   // h rows 16-byte aligned
+  if (gather != nullptr && (T < 0 || T > kMaxRows)) return MG_ERR_SHAPE;
+  // 32-bit buffer offsets: one expert's w13 and (when gathering) all of x
+  constexpr int64_t k4G = int64_t(1) << 32;
+  if (2 * I * K * 2 >= k4G || (gather != nullptr && T * K * 2 >= k4G)) return MG_ERR_SHAPE;
+  if (((M + 255) / 256 + E) * ((I + 127) / 128) > kMaxRows) return MG_ERR_SHAPE;
+  if (M == 0 || I == 0) return MG_OK;
+  if (!offsets || !h || (K > 0 && (!x || !w13))) return MG_ERR_NULL;
+  if ((K > 0 && (!aligned16(x) || !aligned16(w13))) || !aligned16(h) ||
+      (reinterpret_cast<uintptr_t>(offsets) & 3u) || (reinterpret_cast<uintptr_t>(gather) & 3u))
+    return MG_ERR_ALIGN;
+  if ((st = check_device()) != MG_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = maybe_validate(offsets, E, M, s)) != MG_OK) return st;
+  mg::KernelArgs a{};
+  a.p_src = w13;
+  a.q_src = x;
+  a.offsets = offsets;
+  a.out = h;
+  a.M = M; a.N = 2 * I; a.K = K; a.E = E;
+  a.accumulate = 0;
+  a.gather = gather;
+  a.T = gather != nullptr ? T : M;
+  return launch(mg::kFwdSwiglu, a, max_m_per_e, s);
+}
+
 mg_status kgemm_wgrad(const void* dy, const void* x, const int32_t* offsets, float* dw,
                       int64_t M, int64_t N, int64_t K, int32_t E, int32_t accumulate,
                       void* stream) {

@@ -477,7 +477,7 @@ __device__ void balance_kgrouped(int x, int me, int nx, Sched& S) {
 // M-grouped tile id L -> tile.  Ids run expert by expert; within an expert,
 // in groups of gm M-tiles (the last group may be shorter), M-tile fastest,
 // then P-tile.
-template <int BP, int BQ>
+template <int PSTEP, int BQ>
 __device__ __forceinline__ void decode_mgrouped(int L, const Sched& S, Tile& t) {
   const int tilesP = S.tilesP;
   // the expert whose id range [pref[e] tilesP, pref[e+1] tilesP) holds L: the
@@ -499,7 +499,7 @@ __device__ __forceinline__ void decode_mgrouped(int L, const Sched& S, Tile& t) 
   t.e = e;
   t.q0 = S.offs[e] + m * BQ;
   t.q_end = max(S.offs[e + 1], S.offs[e]);
-  t.p0 = tp * BP;
+  t.p0 = tp * PSTEP;
   t.r_begin = 0;
   t.r_end = S.red;
 }
@@ -572,7 +572,8 @@ struct TileSeq {
       const int s = c + j * nx;
       if (s >= count) return false;
       ++j;
-      decode_mgrouped<BP, BQ>(lo + s, S, t);
+      // the fused SwiGLU forward's tile covers BP / 2 output columns (gate + up rows)
+      decode_mgrouped<(MODE == kFwdSwiglu ? BP / 2 : BP), BQ>(lo + s, S, t);
     }
     t.e = __builtin_amdgcn_readfirstlane(t.e);
     t.q0 = __builtin_amdgcn_readfirstlane(t.q0);
@@ -620,14 +621,15 @@ __device__ __forceinline__ bf16x8 frag_rs(const char* tile, uint32_t off, uint32
 template <int MODE, class C>
 __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, char* lds,
                                           int Pdim, int Qdim) {
-  constexpr bool P_RS = MODE != kFwd;      // P is R-strided for dgrad and wgrad
+  constexpr bool SWI = MODE == kFwdSwiglu;
+  constexpr bool P_RS = MODE == kDgrad || MODE == kWgrad;   // P is R-strided for dgrad and wgrad
   constexpr bool Q_RS = MODE == kWgrad;    // Q is R-strided for wgrad
   constexpr int SPW = C::SEGS_PER_WAVE;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
 
   int ldP, ldQ;
-  if (MODE == kFwd) { ldP = (int)a.K; ldQ = (int)a.K; }
+  if (MODE == kFwd || SWI) { ldP = (int)a.K; ldQ = (int)a.K; }
   else if (MODE == kDgrad) { ldP = (int)a.K; ldQ = (int)a.N; }
   else { ldP = (int)a.K; ldQ = (int)a.N; }
 
@@ -643,6 +645,12 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
   const uint32_t lds_base = lds_u32(lds) + (wP ? 0u : (uint32_t)C::P_BYTES) + seg0 * 1024u;
   uint32_t voff[SPW];
   int col[SPW];    // R-contiguous: reduction column; R-strided: outer column
+  int orow[SPW];   // fused SwiGLU forward: the row's output column (P) or row (Q) in the tile
+  // Fused SwiGLU forward: the P tile holds, for each wave row wp, the gate rows
+  // (w13 rows p0 + 64 wp + 0..63) in its blocks 0-1 and the matching up rows
+  // (w13 rows I + p0 + 64 wp + 0..63) in its blocks 2-3, so that acc[i][j]
+  // and acc[i + 2][j] hold g and u of the same outputs.
+  const int I2 = (int)(a.N / 2);
 #pragma unroll
   for (int j = 0; j < SPW; ++j) {
     const int p = (seg0 + j) * 1024 + lane * 16;             // byte within the tile
@@ -651,10 +659,18 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
       const int c = pc ^ rs_swz(r & 3);
       voff[j] = (uint32_t)(r * ld + 8 * c) * 2u;
       col[j] = 8 * c;
+      orow[j] = 0;
     } else {                                                 // [outer][kBK]
       const int row = p / kRowB, pc = (p >> 4) % kRowChunks;
       const int c = pc ^ rc_swz(row);
-      voff[j] = (uint32_t)(row * ld + 8 * c) * 2u;
+      int grow = row;
+      orow[j] = row;
+      if (SWI && wP) {
+        const int wr = row >> 7, blk = (row >> 5) & 3, in = row & 31;
+        orow[j] = 64 * wr + 32 * (blk & 1) + in;
+        grow = (blk < 2 ? 0 : I2) + orow[j];
+      }
+      voff[j] = (uint32_t)(grow * ld + 8 * c) * 2u;
       col[j] = 8 * c;
     }
   }
@@ -666,6 +682,9 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
     if (MODE == kFwd) {            // P = W[e] rows n (R = k), Q = X rows m (R = k)
       P += ((int64_t)t.e * a.N + t.p0) * a.K;
       Q += (int64_t)t.q0 * a.K;
+    } else if (SWI) {              // P = W13[e] rows from p0 (gate; up at + I), Q = X rows
+      P += ((int64_t)t.e * a.N + t.p0) * a.K;
+      if (a.gather == nullptr) Q += (int64_t)t.q0 * a.K;
     } else if (MODE == kDgrad) {   // P = W[e] [n][k] R-strided, Q = dY rows m (R = n)
       P += (int64_t)t.e * a.N * a.K + t.p0;
       Q += (int64_t)t.q0 * a.N;
@@ -686,6 +705,10 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
   int p_nouter = 0, p_red = 0, p_nk = 0, p_kt = 0;
   i32x4 p_rc = {0, 0, 0, 0};
   bool p_live = false;
+  uint32_t tvoff[SPW];            // fused SwiGLU forward: this tile's row offsets
+  uint32_t tmask = 0;             // and which of the lane's rows are valid
+#pragma unroll
+  for (int j = 0; j < SPW; ++j) tvoff[j] = voff[j];
   auto p_next_tile = [&]() {
     Tile t;
     p_live = false;
@@ -699,6 +722,29 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
       p_kt = 0;
       const int rows = p_nouter < outer ? (p_nouter > 0 ? p_nouter : 0) : outer;
       p_rc = make_rsrc(p_src, (uint32_t)rows * (uint32_t)ld * 2u);
+      if (SWI) {
+        tmask = 0;
+        if (wP) {
+          // gate and up rows of this tile: the descriptor spans the expert's
+          // rows from p0 on; a column past I is masked
+          p_rc = make_rsrc(p_src, (uint32_t)(a.N - t.p0) * (uint32_t)ld * 2u);
+#pragma unroll
+          for (int j = 0; j < SPW; ++j) tmask |= (t.p0 + orow[j] < I2 ? 1u : 0u) << j;
+        } else if (a.gather != nullptr) {
+          // gathered rows: offsets from the index, descriptor over all of x
+          p_rc = make_rsrc(p_src, (uint32_t)a.T * (uint32_t)ld * 2u);
+#pragma unroll
+          for (int j = 0; j < SPW; ++j) {
+            const bool ok = t.q0 + orow[j] < t.q_end;
+            const int src = ok ? a.gather[t.q0 + orow[j]] : 0;
+            tvoff[j] = (uint32_t)src * (uint32_t)ld * 2u + (uint32_t)col[j] * 2u;
+            tmask |= (ok ? 1u : 0u) << j;
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < SPW; ++j) tmask |= (orow[j] < p_nouter ? 1u : 0u) << j;
+        }
+      }
       p_live = true;
       return;
     }
@@ -721,8 +767,13 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
     return make_rsrc(p_src + (int64_t)r0 * ld, bytes);
   };
   auto dma_one = [&](const i32x4& rsrc, uint32_t dst, int d, int r0) {
-    const uint32_t off = rs ? (voff[d] | (col[d] < p_nouter ? 0u : kOOB))
-                            : ((voff[d] + (uint32_t)r0 * 2u) | (r0 + col[d] < p_red ? 0u : kOOB));
+    uint32_t off;
+    if (SWI)
+      off = (tvoff[d] + (uint32_t)r0 * 2u) |
+            (r0 + col[d] < p_red && ((tmask >> d) & 1u) ? 0u : kOOB);
+    else
+      off = rs ? (voff[d] | (col[d] < p_nouter ? 0u : kOOB))
+               : ((voff[d] + (uint32_t)r0 * 2u) | (r0 + col[d] < p_red ? 0u : kOOB));
     dma16(rsrc, dst + d * 1024u, off);
   };
   auto p_advance = [&]() {
@@ -930,7 +981,7 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
         swap32(v[2][e], v[3][e]);
       }
       const int m0 = t.q0 + wq * C::WTQ + j * 32 + l16;
-      const int col = t.p0 + wp * C::WTP + i * 32 + 4 * c;
+      const int col = t.p0 + wp * (SWI ? C::WTP / 2 : C::WTP) + i * 32 + 4 * c;
       if (col >= Pdim) return;
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
@@ -942,8 +993,29 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
       }
     }
   };
+  // h = silu(g) u = g u / (1 + e^-g), in fp32 (e^-g = 2^(-g log2 e) with the
+  // hardware base-2 exponential; an overflow gives h = -0 or 0, never NaN
+  // for finite g and u)
+  auto swiglu = [](const f32x16& g, const f32x16& u) {
+    f32x16 h;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float gv = g[e];
+      const float ex = __builtin_amdgcn_exp2f(-gv * 1.4426950408889634f);
+      h[e] = gv / (1.0f + ex) * u[e];
+    }
+    return h;
+  };
   auto store_tile = [&](const Tile& t) {
     if (MODE == kWgrad && a.accumulate && t.r_end <= t.r_begin) return;   // adds nothing
+    if (SWI) {
+#pragma unroll
+      for (int j = 0; j < C::MQ; ++j)
+#pragma unroll
+        for (int i = 0; i < C::MP / 2; ++i)
+          store_block(t, i, j, swiglu(acc[i][j], acc[i + C::MP / 2][j]));
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < C::MQ; ++j)
 #pragma unroll
@@ -1090,6 +1162,8 @@ void grouped_gemm_kernel(KernelArgs a) {
   int Pdim, Qdim;
   if (MODE == kFwd) {
     Pdim = (int)a.N; Qdim = (int)a.M;
+  } else if (MODE == kFwdSwiglu) {
+    Pdim = (int)(a.N / 2); Qdim = (int)a.M;      // outputs: I = N / 2 columns
   } else if (MODE == kDgrad) {
     Pdim = (int)a.K; Qdim = (int)a.M;
   } else {
@@ -1105,9 +1179,10 @@ void grouped_gemm_kernel(KernelArgs a) {
   S.inv = S.offs + (E + 1);
   S.nmine = 0;
   S.E = E;
-  S.tilesP = (Pdim + C::BP - 1) / C::BP;
+  constexpr int kPStep = MODE == kFwdSwiglu ? C::BP / 2 : C::BP;
+  S.tilesP = (Pdim + kPStep - 1) / kPStep;
   S.tilesQ = (Qdim + C::BQ - 1) / C::BQ;
-  S.red = MODE == kFwd ? (int)a.K : (int)a.N;
+  S.red = MODE == kFwd || MODE == kFwdSwiglu ? (int)a.K : (int)a.N;
   // raster group: about sqrt(nx) M-tiles, more when there are few P-tiles,
   // so that the nx tiles an XCD runs at once span ~gm x (nx / gm) panels
   const int nx = gridDim.x >> 3;
@@ -1216,8 +1291,9 @@ int launch_grouped(int mode, const KernelArgs& a_in, int64_t max_m_per_e, hipStr
     const int64_t tilesQ = (a.N + Cfg::BQ - 1) / Cfg::BQ;
     tiles = (int64_t)a.E * tilesQ * tilesP;
   } else {
-    const int64_t Pdim = mode == kFwd ? a.N : a.K;
-    const int64_t tilesP = (Pdim + Cfg::BP - 1) / Cfg::BP;
+    const int64_t Pdim = mode == kFwd ? a.N : (mode == kFwdSwiglu ? a.N / 2 : a.K);
+    const int64_t pstep = mode == kFwdSwiglu ? Cfg::BP / 2 : Cfg::BP;
+    const int64_t tilesP = (Pdim + pstep - 1) / pstep;
     int64_t mt = (a.M + Cfg::BQ - 1) / Cfg::BQ + a.E;       // sum_e ceil(m_e/BQ) <= this
     if (max_m_per_e > 0) {
       const int64_t alt = (int64_t)a.E * ((max_m_per_e + Cfg::BQ - 1) / Cfg::BQ);
@@ -1237,6 +1313,9 @@ int launch_grouped(int mode, const KernelArgs& a_in, int64_t max_m_per_e, hipStr
   switch (mode) {
     case kFwd: hipLaunchKernelGGL((grouped_gemm_kernel<kFwd, Cfg>), g, b, 0, s, a); break;
     case kDgrad: hipLaunchKernelGGL((grouped_gemm_kernel<kDgrad, Cfg>), g, b, 0, s, a); break;
+    case kFwdSwiglu:
+      hipLaunchKernelGGL((grouped_gemm_kernel<kFwdSwiglu, Cfg>), g, b, 0, s, a);
+      break;
     default: hipLaunchKernelGGL((grouped_gemm_kernel<kWgrad, Cfg>), g, b, 0, s, a); break;
   }
   return (int)hipGetLastError();

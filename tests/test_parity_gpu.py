@@ -235,3 +235,91 @@ def test_a3b_zipf_wgrad_sampled(name):
     r = gate_wgrad_sampled(dyb, xb, wl.offsets, got); assert r.passed, str(r)
     empty = np.flatnonzero(wl.sizes() == 0)
     assert len(empty) == 4 and (got[empty] == 0).all()
+
+
+# ------------------------------------- gate-up forward with SwiGLU, gathered --
+
+SW_CASES = [
+    # sizes, T (token rows; None = rows already grouped, no index), I, K, extra rows
+    ([200, 0, 184, 128], 300, 128, 256, 3),
+    ([1, 255, 256, 257], None, 264, 136, 5),      # I = 2 tiles + 8 columns
+    ([0, 513, 0, 1, 300], 900, 520, 200, 0),      # repeated indices, empty experts
+    ([700, 0, 0], 50, 72, 1032, 2),               # 14 uses of each token, long K
+    ([64] * 9, 4096, 384, 64, 0),                 # indices spread over a tall x
+]
+
+
+def _swiglu_check(xb, gather, wb, off, got_bits, rows=None, cols=None):
+    from oracle import check_bf16_swiglu, sample_fwd_swiglu
+    I = wb.shape[1] // 2
+    K = wb.shape[2]
+    if rows is None:
+        n = int(off[-1])
+        rows = np.repeat(np.arange(n), I)
+        cols = np.tile(np.arange(I), n)
+    h, g, u, sg, su = sample_fwd_swiglu(xb, gather, wb, off, rows, cols)
+    return check_bf16_swiglu(got_bits[rows, cols], h, g, u, sg, su, K)
+
+
+@pytest.mark.parametrize("case", range(len(SW_CASES)))
+def test_fwd_swiglu(case):
+    sizes, T, I, K, extra = SW_CASES[case]
+    _say("fwd_swiglu", sizes, T, I, K, extra)
+    off = offsets_from_sizes(sizes)
+    M = int(off[-1]) + extra
+    E = len(sizes)
+    rng = np.random.default_rng(400 + case)
+    xb = normal_bf16_bits((T if T else M, K), 1.0, 400 + case, 1)
+    wb = normal_bf16_bits((E, 2 * I, K), K ** -0.5, 400 + case, 2)
+    gather = rng.integers(0, T, M).astype(np.int32) if T else None
+    out = sentinel_bf16((M, I))
+    h = mg.fwd_swiglu(dev_bf16(xb), dev_bf16(wb), dev_i32(off),
+                      gather=None if gather is None else dev_i32(gather), out=out)
+    torch.cuda.synchronize()
+    got = host_bits(h)
+    r = _swiglu_check(xb, gather, wb, off, got)
+    assert r.passed, str(r)
+    _check_untouched(got, off)
+
+
+def test_fwd_swiglu_gather_equals_pregathered():
+    """Gathering inside the operand loads gives bitwise the result of
+    gathering the rows first (torch index_select) and running ungathered."""
+    sizes, T, I, K = [300, 5, 0, 700], 640, 256, 512
+    off = offsets_from_sizes(sizes)
+    M = int(off[-1])
+    xb = normal_bf16_bits((T, K), 1.0, 450, 1)
+    wb = normal_bf16_bits((len(sizes), 2 * I, K), K ** -0.5, 450, 2)
+    gather = np.random.default_rng(450).integers(0, T, M).astype(np.int32)
+    x, w, o, gi = dev_bf16(xb), dev_bf16(wb), dev_i32(off), dev_i32(gather)
+    h1 = mg.fwd_swiglu(x, w, o, gather=gi)
+    h2 = mg.fwd_swiglu(x.index_select(0, gi.long()).contiguous(), w, o)
+    torch.cuda.synchronize()
+    assert torch.equal(h1, h2)
+
+
+def test_a3b_gate_up_swiglu_gathered_sampled():
+    """The 30B-A3B share's gate-up GEMM as a trainer would run it: 16384 tokens
+    [16384, 3072] gathered through the router's row-to-token map into 32 expert
+    groups, w13 [32, 2560, 3072], SwiGLU fused: h [M, 1280]."""
+    from workloads.synth import router_offsets
+    off, token_of_row = router_offsets(16384, 128, 8, 32, seed=4)
+    (wl,) = [w for w in make_workload(4) if w.name == "a3b_gate_up"]
+    assert np.array_equal(off, wl.offsets)
+    T, K, I = 16384, 3072, 1280
+    xb = normal_bf16_bits((T, K), 1.0, 4, 9, 1)
+    wb = wl.w_bits()
+    _say("a3b gate-up swiglu gathered", int(off[-1]))
+    h = mg.fwd_swiglu(dev_bf16(xb), dev_bf16(wb), dev_i32(off), gather=dev_i32(token_of_row),
+                      max_m_per_e=int(wl.sizes().max()))
+    torch.cuda.synchronize()
+    got = host_bits(h)
+    rng = np.random.default_rng(7)
+    rows = rng.integers(0, int(off[-1]), 4096)
+    cols = rng.integers(0, I, 4096)
+    # plus every column of the first and last row of each expert (tile edges)
+    edge = np.concatenate([[off[e], off[e + 1] - 1] for e in range(32) if off[e + 1] > off[e]])
+    rows = np.concatenate([rows, np.repeat(edge, 16)])
+    cols = np.concatenate([cols, np.tile(np.arange(I - 16, I), edge.size)])
+    r = _swiglu_check(xb, token_of_row, wb, off, got, rows, cols)
+    assert r.passed, str(r)
