@@ -21,6 +21,9 @@ per expert; nothing blocked, fused or reordered):
     stacked gate/up weight gw13 refers to): row i reads token row gather[i],
     h[i, j] = silu(x . w1[e, j]) * (x . w3[e, j]) with w1, w3 the two halves of
     the expert's [2I, K] weight.
+  * A list of independent GEMMs D_g = A_g B_g^T with per-group shapes (the
+    TransformerEngine PR #2045 review: one C API over lists of tensors; the
+    CUTLASS discussion #1452: nested grouped GEMMs flattened into one list).
   * bf16 outputs are the fp64 result rounded once, directly, to bf16 with
     round-to-nearest-even.
 
@@ -30,7 +33,10 @@ adjoint identity tying fwd/dgrad/wgrad together, empty-group insertion,
 exhaustive codec round trips and tie cases; for the SwiGLU forward, scalar
 brute force with math.exp, one-hot closed forms that tell the gate half from
 the up half, gather-as-permutation identities, and a gate that rejects a wrong
-expert or a dropped term.  Every function here is pinned; none is "parity
+expert or a dropped term; for the descriptor list, exact rational brute force on
+groups of mixed shapes (empty and zero-reduction ones included), a one-hot
+transpose check and the flattened LoRA x experts identity.  Every function here
+is pinned; none is "parity
 unpinned".
 """
 from .bf16 import bf16_bits_to_f64, f64_to_bf16_bits, bf16_ulp  # noqa: F401
@@ -43,5 +49,6 @@ from .grouped_gemm import (  # noqa: F401
     sample_wgrad,
     grouped_fwd_swiglu,
     sample_fwd_swiglu,
+    grouped_list,
 )
 from .gate import check_bf16, check_bf16_swiglu, check_fp32, GateReport  # noqa: F401

@@ -124,6 +124,22 @@ def sample_fwd_swiglu(x: np.ndarray, gather, w13: np.ndarray, offsets, rows, col
     return _silu(g) * u, g, u, np.abs(pg).sum(axis=1), np.abs(pu).sum(axis=1)
 
 
+def grouped_list(groups) -> list:
+    """A list of independent GEMMs, one per group: D_g = A_g @ B_g.T  (fp64).
+
+    The TransformerEngine PR #2045 review asks for one C API over lists of
+    per-group tensors, and the CUTLASS discussion #1452 ("Grouped GEMM where
+    each subproblem is another grouped gemm instance") flattens nested grouped
+    GEMMs such as LoRA x experts into such a list.  groups: sequence of
+    (A [m, k], B [n, k]) float64 arrays; returns the list of D [m, n]."""
+    out = []
+    for a, b in groups:
+        a = np.asarray(a, np.float64); b = np.asarray(b, np.float64)
+        assert a.ndim == 2 and b.ndim == 2 and a.shape[1] == b.shape[1]
+        out.append(a @ b.T)
+    return out
+
+
 def expert_of_rows(offsets, rows: np.ndarray) -> np.ndarray:
     """Expert index owning each row (rows past offsets[E] give -1)."""
     o = np.asarray(offsets, dtype=np.int64)

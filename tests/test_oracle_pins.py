@@ -427,3 +427,49 @@ def test_swiglu_sampler_and_gate():
     w_drop = w13.copy(); w_drop[:, :, K - 1] = 0.0
     dropped = grouped_fwd_swiglu(x, gather, w_drop, off)
     assert not check_bf16_swiglu(f64_to_bf16_bits(dropped[rows, cols]), hs, g, u, sg, su, K).passed
+
+
+# ------------------------------------------------ per-group descriptor list --
+
+def test_list_brute_force_exact():
+    """Exact rational triple loops on tiny groups of different shapes,
+    including empty and zero-reduction groups."""
+    from oracle import grouped_list
+    shapes = [(3, 4, 5), (0, 2, 3), (2, 0, 4), (1, 3, 0), (4, 1, 2)]
+    groups = []
+    for g, (m, n, k) in enumerate(shapes):
+        a = bf16_bits_to_f64(normal_bf16_bits((m, k), 1.0, 60, g, 1))
+        b = bf16_bits_to_f64(normal_bf16_bits((n, k), 1.0, 60, g, 2))
+        groups.append((a, b))
+    out = grouped_list(groups)
+    for (a, b), d, (m, n, k) in zip(groups, out, shapes):
+        assert d.shape == (m, n)
+        for i in range(m):
+            for j in range(n):
+                ex = sum((Fraction(float(a[i, t])) * Fraction(float(b[j, t])) for t in range(k)),
+                         Fraction(0))
+                assert Fraction(float(d[i, j])) == ex or abs(float(d[i, j]) - float(ex)) <= 1e-15 * max(1.0, abs(float(ex)))
+                assert f64_round_bf16(np.array([float(ex)]))[0] == f64_round_bf16(np.array([d[i, j]]))[0]
+
+
+def test_list_one_hot_and_flattened_lora():
+    """One-hot rows of A pick columns of B (a transposed B fails); and a nested
+    LoRA x experts product flattens into one list: for each (adapter l, expert
+    e) group, D = X_e A_l^T matches the rows of X_e times the adapter computed
+    one dot product at a time."""
+    from oracle import grouped_list
+    k = 5
+    a = np.eye(k)[[4, 0, 2]]                            # rows pick k = 4, 0, 2
+    b = np.arange(3 * k, dtype=np.float64).reshape(3, k)
+    (d,) = grouped_list([(a, b)])
+    np.testing.assert_array_equal(d, b[:, [4, 0, 2]].T)
+    rng = np.random.default_rng(3)
+    xs = [rng.standard_normal((m, 8)) for m in (3, 0, 5)]     # three experts
+    ads = [rng.standard_normal((2, 8)) for _ in range(2)]     # two rank-2 adapters
+    flat = [(x, ad) for ad in ads for x in xs]
+    out = grouped_list(flat)
+    for (x, ad), dd in zip(flat, out):
+        for i in range(x.shape[0]):
+            for r in range(2):
+                assert dd[i, r] == pytest.approx(float(sum(x[i, t] * ad[r, t] for t in range(8))),
+                                                 rel=1e-12, abs=1e-12)
