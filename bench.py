@@ -35,7 +35,8 @@ PEAK_BF16_TFLOPS = 2500.0        # MI355X published dense bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 KERNEL_SRC = os.path.join(ROOT, "moe_grouped_gemm_bf16_amd", "csrc", "mgemm_kernels.hip")
 KERNEL_NAMES = {"fwd": "grouped_gemm_kernel<0>", "dgrad": "grouped_gemm_kernel<1>",
-                "wgrad": "grouped_gemm_kernel<2>", "fwd_swiglu": "grouped_gemm_kernel<3>"}
+                "wgrad": "grouped_gemm_kernel<2>", "fwd_swiglu": "grouped_gemm_kernel<3>",
+                "list": "grouped_gemm_kernel<4>"}
 
 
 def kernel_hash() -> str:
@@ -57,6 +58,9 @@ def parse_args():
                    help="run one plain 1 GiB device copy (for HBM counter calibration)")
     p.add_argument("--comparators", action="store_true",
                    help="also time library baselines on the same inputs (reported only)")
+    p.add_argument("--lists", action="store_true",
+                   help="also time the descriptor-list call against the M-grouped one "
+                        "(reported only)")
     p.add_argument("--fusions", action="store_true",
                    help="also time the gate-up forward with gathered rows and fused SwiGLU "
                         "against the unfused sequence (reported only)")
@@ -239,6 +243,61 @@ def fusions(torch, mg, reps=20):
         "unfused": "torch index_select + mgemm_fwd [M, 2560] + torch silu(g) * u"}}
 
 
+# -------------------------------------------------------------------- lists --
+
+def lists(torch, mg, reps=20):
+    """The descriptor-list call (one launch over per-group pointers and shapes)
+    on the 30B-A3B share: (1) the gate-up forward as 32 per-expert groups
+    against the M-grouped call on the same data; (2) gate-up and down forwards
+    of all 32 experts mixed in one 64-group launch against two M-grouped
+    launches.  Timed interleaved; reported beside the step only."""
+    import numpy as np
+    from workloads import make_workload
+    wls = {w.name: w for w in make_workload(4)}
+    up = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).cuda()
+    ins = {}
+    for name in ("a3b_gate_up", "a3b_down"):
+        wl = wls[name]
+        off = [int(v) for v in wl.offsets]
+        x, w = up(wl.x_bits()), up(wl.w_bits())
+        y = torch.empty((wl.M, wl.N), dtype=torch.bfloat16, device="cuda")
+        groups = [(x[off[e]:off[e + 1]], w[e]) for e in range(wl.E)]
+        outs = [y[off[e]:off[e + 1]] for e in range(wl.E)]
+        ins[name] = (wl, x, w, torch.from_numpy(wl.offsets).cuda(), y, groups, outs,
+                     int(wl.sizes().max()))
+    gu, dn = ins["a3b_gate_up"], ins["a3b_down"]
+    d_gu = mg.list_descriptors(gu[5], gu[6])
+    d_mix = mg.list_descriptors(gu[5] + dn[5], gu[6] + dn[6])
+    cases = {
+        "gate_up_32_groups": (lambda: mg.grouped_list_desc(d_gu, 32),
+                              lambda: mg.fwd(gu[1], gu[2], gu[3], gu[7], out=gu[4]),
+                              gu[0].flops()),
+        "gate_up_and_down_64_groups": (lambda: mg.grouped_list_desc(d_mix, 64),
+                                       lambda: (mg.fwd(gu[1], gu[2], gu[3], gu[7], out=gu[4]),
+                                                mg.fwd(dn[1], dn[2], dn[3], dn[7], out=dn[4])),
+                                       gu[0].flops() + dn[0].flops()),
+    }
+    out = {}
+    for name, (fl, fm, flops) in cases.items():
+        for _ in range(5):
+            fl(); fm()
+        torch.cuda.synchronize()
+        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(2)] for _ in range(reps)]
+        for pair in ev:
+            for (a, b), fn in zip(pair, (fl, fm)):
+                a.record()
+                fn()
+                b.record()
+        torch.cuda.synchronize()
+        tl = statistics.median(p[0][0].elapsed_time(p[0][1]) for p in ev) * 1e3
+        tm = statistics.median(p[1][0].elapsed_time(p[1][1]) for p in ev) * 1e3
+        out[name] = {"list_us": round(tl, 1), "tflops": round(flops / tl / 1e6, 1),
+                     "pct_peak": round(100 * flops / tl / 1e6 / PEAK_BF16_TFLOPS, 1),
+                     "mgrouped_us": round(tm, 1), "ratio": round(tm / tl, 3)}
+    return out
+
+
 # ------------------------------------------------------------- CPU baseline --
 
 def cpu_baseline(workload: str):
@@ -390,6 +449,11 @@ def main():
         print("[bench] timing library comparators", file=sys.stderr, flush=True)
         comp = comparators(ops, torch)
 
+    listed = None
+    if args.lists:
+        print("[bench] timing the descriptor-list call", file=sys.stderr, flush=True)
+        listed = lists(torch, mg)
+
     fused = None
     if args.fusions:
         print("[bench] timing the fused gate-up forward", file=sys.stderr, flush=True)
@@ -432,6 +496,8 @@ def main():
         line["comparators"] = comp
     if fused is not None:
         line["fused_ops"] = fused
+    if listed is not None:
+        line["list_ops"] = listed
     print(json.dumps(line), flush=True)
 
 

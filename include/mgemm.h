@@ -106,6 +106,35 @@ mg_status mgemm_fwd_swiglu(const void* x, const int32_t* gather, const void* w13
                            const int32_t* offsets, void* h, int64_t M, int64_t T, int64_t I,
                            int64_t K, int32_t E, int64_t max_m_per_e, void* stream);
 
+/* One group of mgemm_list: D [m, n] = A [m, k] B [n, k]^T (bf16 in and out,
+ * fp32 accumulation, round to nearest even), row-major with row strides in
+ * elements.  All three pointers are DEVICE pointers, 16-byte aligned; k, n and
+ * the strides multiples of 8, lda >= k, ldb >= k, ldd >= n, strides <= 2^22.
+ * m, n, k >= 0: a group with m == 0 or n == 0 does nothing; k == 0 writes
+ * zeros. */
+typedef struct mg_gemm_desc {
+  const void* a;
+  const void* b;
+  void* d;
+  int32_t m, n, k;
+  int32_t lda, ldb, ldd;
+} mg_gemm_desc;
+
+/* A list of independent GEMMs with per-group shapes and pointers in one
+ * launch (the TransformerEngine PR #2045 review asks for one C API over lists
+ * of per-group tensors; the CUTLASS discussion #1452 flattens nested grouped
+ * GEMMs -- LoRA adapters x MoE experts -- into such a list).  desc: DEVICE
+ * array of G descriptors, 8-byte aligned, 1 <= G <= 1024; read by the kernel's
+ * own scheduler, never on the host (checked on the host only under
+ * MGEMM_VALIDATE=1, with mg_check_list_host).  The D regions must not overlap
+ * each other or any input.  Allocates nothing. */
+mg_status mgemm_list(const mg_gemm_desc* desc, int32_t G, void* stream);
+
+/* Host-side check of a descriptor list held in HOST memory (no device use):
+ * MG_OK, or MG_ERR_SHAPE / MG_ERR_NULL / MG_ERR_ALIGN for the first group that
+ * breaks the rules above. */
+mg_status mg_check_list_host(const mg_gemm_desc* desc_host, int32_t G);
+
 /* K-grouped weight gradient in FP32 (RapidGEMM README, "Kernels", Kgemm;
  * wgrad is x^T dy, DeepGEMM issue #10, laid out like w so it can update w):
  *   dw[e, n, k] (= or +=) sum_{offsets[e] <= i < offsets[e+1]} dy[i, n] * x[i, k]

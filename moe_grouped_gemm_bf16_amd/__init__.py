@@ -9,6 +9,7 @@ kernels; PyTorch provides device memory and the current stream.
   wgrad(dy, x, offsets)   dW[e] = sum_i dy[i]^T x[i]  K-grouped fp32 weight gradient
   fwd_swiglu(x, w13, offsets, gather)                  gate-up forward, SwiGLU fused,
       h[i] = silu(x[r] w1[e]^T) * (x[r] w3[e]^T), r = gather[i]   rows gathered by index
+  grouped_list([(A_g, B_g), ...])   D_g = A_g B_g^T    independent GEMMs, per-group shapes
 
 Page-shaped aliases follow the RapidGEMM README ("Kernels"):
   Mgemm(x, w, cnt, max_M_per_E, transpose_B) and Kgemm(grad, X, cnt, descriptor).
@@ -17,10 +18,10 @@ from __future__ import annotations
 
 import torch
 
-from ._lib import LIB, MgemmError, check, status_str  # noqa: F401
+from ._lib import LIB, GemmDesc, MgemmError, check, status_str  # noqa: F401
 
-__all__ = ["fwd", "dgrad", "wgrad", "fwd_swiglu", "Mgemm", "Kgemm", "MgemmError", "status_str",
-           "LIB"]
+__all__ = ["fwd", "dgrad", "wgrad", "fwd_swiglu", "grouped_list", "list_descriptors",
+           "grouped_list_desc", "Mgemm", "Kgemm", "MgemmError", "status_str", "LIB"]
 
 
 def _stream(t: torch.Tensor) -> int:
@@ -171,6 +172,63 @@ def fwd_swiglu(x: torch.Tensor, w13: torch.Tensor, offsets: torch.Tensor,
                                   out.data_ptr(), M, T, I, K, E, int(max_m_per_e), _stream(x))
     check(st, "mgemm_fwd_swiglu")
     return out
+
+
+def _matrix(t: torch.Tensor, name: str) -> int:
+    """Row stride of a bf16 matrix view whose rows are contiguous."""
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or t.dim() != 2:
+        raise TypeError(f"{name} must be a 2-D bfloat16 tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU device")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have contiguous rows")
+    return int(t.stride(0)) if t.shape[0] > 1 else int(t.shape[1])
+
+
+def list_descriptors(groups, outs) -> torch.Tensor:
+    """Device array of mg_gemm_desc for groups [(A [m, k], B [n, k]), ...] and
+    outputs [D [m, n], ...] (row-strided views are fine).  The copy to the
+    device is synchronous, so the host staging buffer outlives it."""
+    descs = (GemmDesc * len(groups))()
+    dev = None
+    for g, ((a, b), d) in enumerate(zip(groups, outs)):
+        lda, ldb, ldd = _matrix(a, f"A[{g}]"), _matrix(b, f"B[{g}]"), _matrix(d, f"D[{g}]")
+        m, k = a.shape
+        n, k2 = b.shape
+        if k2 != k or tuple(d.shape) != (m, n):
+            raise ValueError(f"group {g}: A {tuple(a.shape)}, B {tuple(b.shape)}, D {tuple(d.shape)}")
+        dev = a.device if dev is None else dev
+        if a.device != dev or b.device != dev or d.device != dev:
+            raise ValueError("all groups must live on one device")
+        descs[g] = GemmDesc(a.data_ptr(), b.data_ptr(), d.data_ptr(), m, n, k, lda, ldb, ldd)
+    st = LIB.mg_check_list_host(descs, len(groups))
+    check(st, "mg_check_list_host")
+    raw = torch.frombuffer(bytearray(bytes(descs)), dtype=torch.uint8)
+    return raw.to(dev)
+
+
+def grouped_list_desc(desc: torch.Tensor, G: int) -> None:
+    """mgemm_list on a device descriptor array (from list_descriptors)."""
+    if desc.dtype != torch.uint8 or not desc.is_cuda or desc.numel() != 48 * G:
+        raise ValueError("desc must be the device uint8 array of G descriptors")
+    with torch.cuda.device(desc.device):
+        st = LIB.mgemm_list(desc.data_ptr(), int(G), _stream(desc))
+    check(st, "mgemm_list")
+
+
+def grouped_list(groups, outs=None):
+    """Independent GEMMs D_g = A_g @ B_g.T with per-group shapes in one launch.
+
+    groups: [(A_g bf16 [m_g, k_g], B_g bf16 [n_g, k_g]), ...]; outs: optional
+    [D_g bf16 [m_g, n_g], ...] (allocated when None).  Returns the D list."""
+    if not groups:
+        return []
+    if outs is None:
+        outs = [torch.empty((a.shape[0], b.shape[0]), dtype=torch.bfloat16, device=a.device)
+                for a, b in groups]
+    desc = list_descriptors(groups, outs)
+    grouped_list_desc(desc, len(groups))
+    return outs
 
 
 def Mgemm(x: torch.Tensor, w: torch.Tensor, cnt: torch.Tensor, max_M_per_E: int = 0,

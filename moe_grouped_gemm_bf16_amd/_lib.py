@@ -20,10 +20,22 @@ SIGNATURES = {
     "mgemm_dgrad": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i64, _vp]),
     "kgemm_wgrad": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp]),
     "mgemm_fwd_swiglu": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32, _i64, _vp]),
+    "mgemm_list": (_i32, [_vp, _i32, _vp]),
+    "mg_check_list_host": (_i32, [_vp, _i32]),
     "mg_status_str": (ctypes.c_char_p, [_i32]),
     "mg_abi_version": (_i32, []),
     "mg_check_offsets_host": (_i32, [_vp, _i32, _i64]),
 }
+
+
+class GemmDesc(ctypes.Structure):
+    """mg_gemm_desc of include/mgemm.h: one group of mgemm_list."""
+    _fields_ = [("a", ctypes.c_void_p), ("b", ctypes.c_void_p), ("d", ctypes.c_void_p),
+                ("m", ctypes.c_int32), ("n", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("lda", ctypes.c_int32), ("ldb", ctypes.c_int32), ("ldd", ctypes.c_int32)]
+
+
+assert ctypes.sizeof(GemmDesc) == 48
 
 
 class MgemmError(RuntimeError):

@@ -10,6 +10,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cstddef>
 #include <cstdlib>
 #include <cstring>
 #include <vector>
@@ -62,6 +63,11 @@ mg_status maybe_validate(const int32_t* offsets, int32_t E, int64_t M, hipStream
     return MG_ERR_DEVICE;
   return mg_check_offsets_host(h.data(), E, M);
 }
+
+static_assert(sizeof(mg_gemm_desc) == sizeof(mg::ListDesc) &&
+                  offsetof(mg_gemm_desc, m) == offsetof(mg::ListDesc, m) &&
+                  offsetof(mg_gemm_desc, ldd) == offsetof(mg::ListDesc, ldd),
+              "mg_gemm_desc and the kernel's descriptor must have one layout");
 
 mg_status launch(int mode, const mg::KernelArgs& a, int64_t max_m_per_e, hipStream_t s) {
   int err = mg::launch_grouped(mode, a, max_m_per_e, s);
@@ -142,6 +148,31 @@ mg_status mgemm_fwd_swiglu(const void* x, const int32_t* gather, const void* w13
   return launch(mg::kFwdSwiglu, a, max_m_per_e, s);
 }
 
+mg_status mgemm_list(const mg_gemm_desc* desc, int32_t G, void* stream) {
+  if (G < 1 || G > mg::kMaxExperts) return MG_ERR_SHAPE;
+  if (!desc) return MG_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(desc) & 7u) return MG_ERR_ALIGN;
+  mg_status st = check_device();
+  if (st != MG_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  static const bool validate = [] {
+    const char* v = std::getenv("MGEMM_VALIDATE");
+    return v != nullptr && v[0] == '1';
+  }();
+  if (validate) {
+    std::vector<mg_gemm_desc> h(static_cast<size_t>(G));
+    if (hipMemcpyAsync(h.data(), desc, h.size() * sizeof(mg_gemm_desc), hipMemcpyDeviceToHost,
+                       s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+      return MG_ERR_DEVICE;
+    if ((st = mg_check_list_host(h.data(), G)) != MG_OK) return st;
+  }
+  mg::KernelArgs a{};
+  a.list = reinterpret_cast<const mg::ListDesc*>(desc);
+  a.E = G;
+  return launch(mg::kList, a, 0, s);
+}
+
 mg_status kgemm_wgrad(const void* dy, const void* x, const int32_t* offsets, float* dw,
                       int64_t M, int64_t N, int64_t K, int32_t E, int32_t accumulate,
                       void* stream) {
@@ -180,6 +211,23 @@ const char* mg_status_str(int32_t status) {
 }
 
 int32_t mg_abi_version(void) { return 1; }
+
+mg_status mg_check_list_host(const mg_gemm_desc* desc_host, int32_t G) {
+  if (!desc_host) return MG_ERR_NULL;
+  if (G < 1 || G > mg::kMaxExperts) return MG_ERR_SHAPE;
+  for (int32_t g = 0; g < G; ++g) {
+    const mg_gemm_desc& d = desc_host[g];
+    if (d.m < 0 || d.n < 0 || d.k < 0) return MG_ERR_SHAPE;
+    if ((d.n & 7) || (d.k & 7) || (d.lda & 7) || (d.ldb & 7) || (d.ldd & 7)) return MG_ERR_SHAPE;
+    if (d.lda < d.k || d.ldb < d.k || d.ldd < d.n || d.lda > kMaxDim || d.ldb > kMaxDim ||
+        d.ldd > kMaxDim)
+      return MG_ERR_SHAPE;
+    if (d.m == 0 || d.n == 0) continue;
+    if (!d.d || (d.k > 0 && (!d.a || !d.b))) return MG_ERR_NULL;
+    if (!aligned16(d.d) || (d.k > 0 && (!aligned16(d.a) || !aligned16(d.b)))) return MG_ERR_ALIGN;
+  }
+  return MG_OK;
+}
 
 mg_status mg_check_offsets_host(const int32_t* offsets_host, int32_t E, int64_t M) {
   if (!offsets_host) return MG_ERR_NULL;

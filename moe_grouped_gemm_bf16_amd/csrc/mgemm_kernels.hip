@@ -184,6 +184,52 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int* scratch, int* to
   return before + incl - x;
 }
 
+// The same over 64-bit values (block total to *total).
+template <int NT>
+__device__ __forceinline__ int64_t block_exclusive_scan64(int64_t x, int64_t* scratch,
+                                                          int64_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int64_t incl = x;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int64_t y = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += y;
+  }
+  __syncthreads();
+  if (lane == 63) scratch[wave] = incl;
+  __syncthreads();
+  int64_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const int64_t v = scratch[w];
+    before += (w < wave) ? v : 0;
+    all += v;
+  }
+  *total = all;
+  return before + incl - x;
+}
+
+// Descriptor g of the list, read through the constant address space: the
+// kernel never writes the descriptors, and with a wave-uniform g this
+// compiles to scalar loads (waited on with lgkmcnt), not vector loads whose
+// wait would also cover the in-flight operand loads.
+typedef __attribute__((address_space(4))) const ListDesc ConstListDesc;
+__device__ __forceinline__ ListDesc list_desc(const ListDesc* list, int g) {
+  const ConstListDesc* p = reinterpret_cast<const ConstListDesc*>(
+      reinterpret_cast<uintptr_t>(list)) + __builtin_amdgcn_readfirstlane(g);
+  ListDesc d;
+  d.a = p->a;
+  d.b = p->b;
+  d.d = p->d;
+  d.m = p->m;
+  d.n = p->n;
+  d.k = p->k;
+  d.lda = p->lda;
+  d.ldb = p->ldb;
+  d.ldd = p->ldd;
+  return d;
+}
+
 struct Tile {
   int e;        // expert
   int q0;       // first Q index of the tile (global row for M-grouped, n for K-grouped)
@@ -209,6 +255,7 @@ struct Sched {
   int bw;       // K-grouped: P-tiles per band
   int per;      // K-grouped: tiles per expert
   bool split;   // K-grouped: heavy tiles may be split in two token halves
+  const ListDesc* list;   // descriptor list (E groups), else null
 };
 
 // Offsets are read clamped to [0, M] and made non-decreasing per expert, so
@@ -252,6 +299,105 @@ __device__ void setup_mgrouped(const int32_t* __restrict__ offsets, int E, int M
   if (threadIdx.x == 0) S.pref[E] = mtiles;
   __syncthreads();
   S.total = mtiles * S.tilesP;
+}
+
+// Descriptor-list set-up: group g has ceil(m / BQ) x ceil(n / BP) tiles (none
+// when m or n is not positive); S.pref holds their exclusive prefix.
+template <int NT, int BP, int BQ>
+__device__ void setup_list(const ListDesc* __restrict__ desc, int G, Sched& S) {
+  constexpr int kPer = (kMaxExperts + NT - 1) / NT;
+  const int g0 = threadIdx.x * kPer;
+  int cnt[kPer];
+  int mine = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int g = g0 + j;
+    cnt[j] = 0;
+    if (g < G) {
+      const int m = desc[g].m, n = desc[g].n;
+      cnt[j] = m > 0 && n > 0 ? ((m + BQ - 1) / BQ) * ((n + BP - 1) / BP) : 0;
+      mine += cnt[j];
+    }
+  }
+  int total;
+  int run = block_exclusive_scan<NT>(mine, S.scan, &total);
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int g = g0 + j;
+    if (g < G) S.pref[g] = run;
+    run += cnt[j];
+  }
+  if (threadIdx.x == 0) S.pref[G] = total;
+  __syncthreads();
+  S.total = total;
+  // Groups may differ in k, so tiles differ in cost (stages + 3 for the
+  // store): the XCDs get contiguous tile ranges of equal total cost rather
+  // than equal tile counts.  XCD x starts at T_x, the number of tiles whose
+  // cost midpoint lies below x / 8 of the total W: a tile u of a group whose
+  // tiles cost w each and start at cumulative cost c0 counts when
+  // 8 (c0 + u w) + 4 w < x W.  T_x is kept in S.keys[x] (x = 0..8).
+  int64_t cost = 0;
+  int64_t w[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int g = g0 + j;
+    w[j] = 0;
+    if (g < G) {
+      w[j] = (int64_t)((max(desc[g].k, 0) + kBK - 1) / kBK + 3);
+      cost += (int64_t)cnt[j] * w[j];
+    }
+  }
+  int64_t* scratch64 = reinterpret_cast<int64_t*>(S.keys + 16);
+  int64_t wtot;
+  int64_t crun = block_exclusive_scan64<NT>(cost, scratch64, &wtot);
+  int below[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    if (g0 + j < G && cnt[j] > 0) {
+      for (int x = 1; x < 8; ++x) {
+        const int64_t num = (int64_t)x * wtot - 8 * crun - 4 * w[j];
+        const int64_t q = num <= 0 ? 0 : (num + 8 * w[j] - 1) / (8 * w[j]);
+        below[x] += (int)(q < cnt[j] ? q : cnt[j]);
+      }
+      crun += (int64_t)cnt[j] * w[j];
+    }
+  }
+  if (threadIdx.x < 9) S.keys[threadIdx.x] = threadIdx.x == 8 ? total : 0;
+  __syncthreads();
+  for (int x = 1; x < 8; ++x) {
+    int v = below[x];
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+    if ((threadIdx.x & 63) == 0 && v != 0) atomicAdd(&S.keys[x], v);
+  }
+  __syncthreads();
+}
+
+// Tile id L of the list -> tile: the group holding L (binary search on the
+// prefix; groups without tiles share their successor's prefix), then, within
+// the group, raster groups of gm M-tiles, M-tile fastest.
+template <int BP, int BQ>
+__device__ __forceinline__ void decode_list(int L, const Sched& S, const ListDesc* desc, Tile& t) {
+  int lo = 0, hi = S.E - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (S.pref[mid] <= L) lo = mid; else hi = mid - 1;
+  }
+  const int g = __builtin_amdgcn_readfirstlane(lo);
+  const ListDesc dg = list_desc(desc, g);
+  const int m = dg.m, n = dg.n, k = dg.k;
+  const int local = L - S.pref[g];
+  const int mt = (m + BQ - 1) / BQ, tilesP = (n + BP - 1) / BP;
+  const int gg = local / (S.gm * tilesP);
+  const int rem = local - gg * S.gm * tilesP;
+  const int gh = min(S.gm, mt - gg * S.gm);
+  const int tp = rem / gh;
+  t.e = g;
+  t.q0 = (gg * S.gm + (rem - tp * gh)) * BQ;
+  t.q_end = m;
+  t.p0 = tp * BP;
+  t.r_begin = 0;
+  t.r_end = max(k, 0);
 }
 
 // K-grouped: chunk k (0..7) of an expert's tile grid is the band-order index
@@ -541,9 +687,14 @@ struct TileSeq {
     j = 0;
     ie = 0;
     if (MODE != kWgrad) {
-      const int q8 = S.total >> 3, r8 = S.total & 7;
-      count = q8 + (x < r8 ? 1 : 0);
-      lo = x * q8 + (x < r8 ? x : r8);
+      if (MODE == kList) {              // cost-balanced ranges from the set-up
+        lo = S.keys[x];
+        count = S.keys[x + 1] - lo;
+      } else {
+        const int q8 = S.total >> 3, r8 = S.total & 7;
+        count = q8 + (x < r8 ? 1 : 0);
+        lo = x * q8 + (x < r8 ? x : r8);
+      }
     }
   }
 
@@ -573,7 +724,8 @@ struct TileSeq {
       if (s >= count) return false;
       ++j;
       // the fused SwiGLU forward's tile covers BP / 2 output columns (gate + up rows)
-      decode_mgrouped<(MODE == kFwdSwiglu ? BP / 2 : BP), BQ>(lo + s, S, t);
+      if (MODE == kList) decode_list<BP, BQ>(lo + s, S, S.list, t);
+      else decode_mgrouped<(MODE == kFwdSwiglu ? BP / 2 : BP), BQ>(lo + s, S, t);
     }
     t.e = __builtin_amdgcn_readfirstlane(t.e);
     t.q0 = __builtin_amdgcn_readfirstlane(t.q0);
@@ -622,6 +774,7 @@ template <int MODE, class C>
 __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, char* lds,
                                           int Pdim, int Qdim) {
   constexpr bool SWI = MODE == kFwdSwiglu;
+  constexpr bool LIST = MODE == kList;
   constexpr bool P_RS = MODE == kDgrad || MODE == kWgrad;   // P is R-strided for dgrad and wgrad
   constexpr bool Q_RS = MODE == kWgrad;    // Q is R-strided for wgrad
   constexpr int SPW = C::SEGS_PER_WAVE;
@@ -629,7 +782,7 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
 
   int ldP, ldQ;
-  if (MODE == kFwd || SWI) { ldP = (int)a.K; ldQ = (int)a.K; }
+  if (MODE == kFwd || SWI || LIST) { ldP = (int)a.K; ldQ = (int)a.K; }   // LIST: per tile
   else if (MODE == kDgrad) { ldP = (int)a.K; ldQ = (int)a.N; }
   else { ldP = (int)a.K; ldQ = (int)a.N; }
 
@@ -640,7 +793,7 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
   const bool wP = wave * SPW < C::SEGS_P;                    // wave-uniform
   const bool rs = wP ? P_RS : Q_RS;
   const int outer = wP ? C::BP : C::BQ;
-  const int ld = wP ? ldP : ldQ;
+  int ld = wP ? ldP : ldQ;              // LIST: the tile's group's row stride
   const int seg0 = wP ? wave * SPW : wave * SPW - C::SEGS_P;
   const uint32_t lds_base = lds_u32(lds) + (wP ? 0u : (uint32_t)C::P_BYTES) + seg0 * 1024u;
   uint32_t voff[SPW];
@@ -685,6 +838,10 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
     } else if (SWI) {              // P = W13[e] rows from p0 (gate; up at + I), Q = X rows
       P += ((int64_t)t.e * a.N + t.p0) * a.K;
       if (a.gather == nullptr) Q += (int64_t)t.q0 * a.K;
+    } else if (LIST) {             // P = B_g rows n, Q = A_g rows m (R = k), own strides
+      const ListDesc dg = list_desc(S.list, t.e);
+      P = reinterpret_cast<const uint16_t*>(dg.b) + (int64_t)t.p0 * dg.ldb;
+      Q = reinterpret_cast<const uint16_t*>(dg.a) + (int64_t)t.q0 * dg.lda;
     } else if (MODE == kDgrad) {   // P = W[e] [n][k] R-strided, Q = dY rows m (R = n)
       P += (int64_t)t.e * a.N * a.K + t.p0;
       Q += (int64_t)t.q0 * a.N;
@@ -692,7 +849,7 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
       P += (int64_t)t.r_begin * a.K + t.p0;
       Q += (int64_t)t.r_begin * a.N + t.q0;
     }
-    const int nP = Pdim - t.p0;
+    const int nP = (LIST ? list_desc(S.list, t.e).n : Pdim) - t.p0;
     const int nQ = MODE == kWgrad ? Qdim - t.q0 : t.q_end - t.q0;
     src = wP ? P : Q;
     nouter = wP ? nP : nQ;
@@ -716,6 +873,14 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
       const int red = t.r_end - t.r_begin;
       const int nk = (red + kBK - 1) / kBK;
       if (nk <= 0) continue;                  // nothing to stage: the consumer stores zeros
+      if (LIST) {
+        // the group's row stride, and the lanes' row offsets under it
+        const ListDesc dg = list_desc(S.list, t.e);
+        ld = wP ? dg.ldb : dg.lda;
+#pragma unroll
+        for (int j = 0; j < SPW; ++j) tvoff[j] = (uint32_t)(orow[j] * ld + col[j]) * 2u;
+        tmask = (1u << SPW) - 1u;             // rows past the group's end: descriptor range
+      }
       tile_src(t, p_src, p_nouter);
       p_red = red;
       p_nk = nk;
@@ -768,7 +933,7 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
   };
   auto dma_one = [&](const i32x4& rsrc, uint32_t dst, int d, int r0) {
     uint32_t off;
-    if (SWI)
+    if (SWI || LIST)
       off = (tvoff[d] + (uint32_t)r0 * 2u) |
             (r0 + col[d] < p_red && ((tmask >> d) & 1u) ? 0u : kOOB);
     else
@@ -925,8 +1090,29 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
     y = r[1];
   };
   const int l16 = lane & 15, pa = (lane >> 4) & 1, pb = lane >> 5;
+  // Where a tile's bf16 result goes: the output, its row stride and column
+  // bound (the descriptor list's group has its own; read once per tile, as
+  // the stores could otherwise be taken to alias the descriptors).
+  struct OutView {
+    uint16_t* out;
+    int ldo, pbound;
+  };
+  auto out_view = [&](const Tile& t) {
+    OutView v;
+    if (LIST) {
+      const ListDesc dg = list_desc(S.list, t.e);
+      v.out = reinterpret_cast<uint16_t*>(dg.d);
+      v.ldo = dg.ldd;
+      v.pbound = dg.n;
+    } else {
+      v.out = reinterpret_cast<uint16_t*>(a.out);
+      v.ldo = Pdim;
+      v.pbound = Pdim;
+    }
+    return v;
+  };
   // Result block (i, j) held in `blk` (the register layout of acc[i][j]).
-  auto store_block = [&](const Tile& t, int i, int j, const f32x16& blk) {
+  auto store_block = [&](const Tile& t, const OutView& ov, int i, int j, const f32x16& blk) {
     if (MODE == kWgrad) {
       float* out = reinterpret_cast<float*>(a.out) + (int64_t)t.e * a.N * a.K;
       const int c = pb + 2 * pa;                          // chunk of groups 0 and 1
@@ -958,8 +1144,9 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
         *dst = r;
       }
     } else {
-      uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
-      const int ldo = Pdim;
+      uint16_t* out = ov.out;
+      const int ldo = ov.ldo;
+      const int pbound = ov.pbound;
       const int c = 4 * pa + 2 * pb;                      // first of the lane's two chunks
       uint32_t v[4][2];
 #pragma unroll
@@ -982,7 +1169,7 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
       }
       const int m0 = t.q0 + wq * C::WTQ + j * 32 + l16;
       const int col = t.p0 + wp * (SWI ? C::WTP / 2 : C::WTP) + i * 32 + 4 * c;
-      if (col >= Pdim) return;
+      if (col >= pbound) return;
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int m = m0 + 16 * half;
@@ -1008,18 +1195,19 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
   };
   auto store_tile = [&](const Tile& t) {
     if (MODE == kWgrad && a.accumulate && t.r_end <= t.r_begin) return;   // adds nothing
+    const OutView ov = out_view(t);
     if (SWI) {
 #pragma unroll
       for (int j = 0; j < C::MQ; ++j)
 #pragma unroll
         for (int i = 0; i < C::MP / 2; ++i)
-          store_block(t, i, j, swiglu(acc[i][j], acc[i + C::MP / 2][j]));
+          store_block(t, ov, i, j, swiglu(acc[i][j], acc[i + C::MP / 2][j]));
       return;
     }
 #pragma unroll
     for (int j = 0; j < C::MQ; ++j)
 #pragma unroll
-      for (int i = 0; i < C::MP; ++i) store_block(t, i, j, acc[i][j]);
+      for (int i = 0; i < C::MP; ++i) store_block(t, ov, i, j, acc[i][j]);
   };
 
   // ---- end of a half of a split K-grouped tile.  Each half writes its fp32
@@ -1068,6 +1256,7 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
                                               __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (S.scan[8] == 0) return;                 // the other half finishes the tile
+    const OutView ov = out_view(t);
     const auto rs = slot_rsrc(2 * sid + (half ^ 1));
 #pragma unroll
     for (int jj = 0; jj < C::MQ; ++jj)
@@ -1083,7 +1272,7 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
         const f32x8 hi = __builtin_shufflevector(v[2], v[3], 0, 1, 2, 3, 4, 5, 6, 7);
         const f32x16 other = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10,
                                                      11, 12, 13, 14, 15);
-        store_block(t, ii, jj, acc[ii][jj] + other);
+        store_block(t, ov, ii, jj, acc[ii][jj] + other);
       }
     if (tid == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
@@ -1164,6 +1353,8 @@ void grouped_gemm_kernel(KernelArgs a) {
     Pdim = (int)a.N; Qdim = (int)a.M;
   } else if (MODE == kFwdSwiglu) {
     Pdim = (int)(a.N / 2); Qdim = (int)a.M;      // outputs: I = N / 2 columns
+  } else if (MODE == kList) {
+    Pdim = 0; Qdim = 0;                          // per group, from the descriptors
   } else if (MODE == kDgrad) {
     Pdim = (int)a.K; Qdim = (int)a.M;
   } else {
@@ -1180,7 +1371,8 @@ void grouped_gemm_kernel(KernelArgs a) {
   S.nmine = 0;
   S.E = E;
   constexpr int kPStep = MODE == kFwdSwiglu ? C::BP / 2 : C::BP;
-  S.tilesP = (Pdim + kPStep - 1) / kPStep;
+  S.tilesP = MODE == kList ? 1 : (Pdim + kPStep - 1) / kPStep;
+  S.list = MODE == kList ? a.list : nullptr;
   S.tilesQ = (Qdim + C::BQ - 1) / C::BQ;
   S.red = MODE == kFwd || MODE == kFwdSwiglu ? (int)a.K : (int)a.N;
   // raster group: about sqrt(nx) M-tiles, more when there are few P-tiles,
@@ -1198,6 +1390,8 @@ void grouped_gemm_kernel(KernelArgs a) {
   if (MODE == kWgrad) {
     setup_kgrouped<C::NT>(a.offsets, E, (int)a.M, S);
     balance_kgrouped<C::NT>(blockIdx.x & 7, blockIdx.x >> 3, nx, S);
+  } else if (MODE == kList) {
+    setup_list<C::NT, C::BP, C::BQ>(a.list, E, S);
   } else {
     setup_mgrouped<C::NT, C::BQ>(a.offsets, E, (int)a.M, S);
   }
@@ -1286,7 +1480,9 @@ int launch_grouped(int mode, const KernelArgs& a_in, int64_t max_m_per_e, hipStr
     }
   }
   int64_t tiles;
-  if (mode == kWgrad) {
+  if (mode == kList) {
+    tiles = int64_t(1) << 30;                 // unknown on the host: one workgroup per CU
+  } else if (mode == kWgrad) {
     const int64_t tilesP = (a.K + Cfg::BP - 1) / Cfg::BP;
     const int64_t tilesQ = (a.N + Cfg::BQ - 1) / Cfg::BQ;
     tiles = (int64_t)a.E * tilesQ * tilesP;
@@ -1316,6 +1512,7 @@ int launch_grouped(int mode, const KernelArgs& a_in, int64_t max_m_per_e, hipStr
     case kFwdSwiglu:
       hipLaunchKernelGGL((grouped_gemm_kernel<kFwdSwiglu, Cfg>), g, b, 0, s, a);
       break;
+    case kList: hipLaunchKernelGGL((grouped_gemm_kernel<kList, Cfg>), g, b, 0, s, a); break;
     default: hipLaunchKernelGGL((grouped_gemm_kernel<kWgrad, Cfg>), g, b, 0, s, a); break;
   }
   return (int)hipGetLastError();

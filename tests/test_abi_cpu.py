@@ -111,3 +111,28 @@ def test_python_binding_rejects_bad_tensors_on_host():
         mg.fwd(x, w[:, :, :8].contiguous(), off)
     with pytest.raises(ValueError):
         mg.Kgemm(x, x, off, descriptor="gw9")
+
+
+def test_host_list_check():
+    """mg_check_list_host enforces the mg_gemm_desc rules (no device use)."""
+    import ctypes
+    from moe_grouped_gemm_bf16_amd._lib import GemmDesc
+    P = 0x10000                                   # any 16-byte aligned address
+    def chk(*descs):
+        arr = (GemmDesc * len(descs))(*descs)
+        return _lib.LIB.mg_check_list_host(arr, len(descs))
+    ok = GemmDesc(P, P, P, 5, 16, 24, 24, 32, 16)
+    assert chk(ok) == _lib.MG_OK
+    assert chk(ok, GemmDesc(0, 0, 0, 0, 8, 8, 8, 8, 8)) == _lib.MG_OK       # empty group
+    assert chk(GemmDesc(0, 0, P, 3, 8, 0, 0, 0, 8)) == _lib.MG_OK          # k == 0
+    assert chk(GemmDesc(P, P, P, -1, 8, 8, 8, 8, 8)) == _lib.MG_ERR_SHAPE
+    assert chk(GemmDesc(P, P, P, 2, 12, 8, 8, 8, 16)) == _lib.MG_ERR_SHAPE  # n % 8
+    assert chk(GemmDesc(P, P, P, 2, 8, 16, 8, 16, 8)) == _lib.MG_ERR_SHAPE  # lda < k
+    assert chk(GemmDesc(P, P, P, 2, 16, 8, 8, 8, 8)) == _lib.MG_ERR_SHAPE   # ldd < n
+    assert chk(GemmDesc(P, 0, P, 2, 8, 8, 8, 8, 8)) == _lib.MG_ERR_NULL
+    assert chk(GemmDesc(P + 8, P, P, 2, 8, 8, 8, 8, 8)) == _lib.MG_ERR_ALIGN
+    assert _lib.LIB.mg_check_list_host(None, 1) == _lib.MG_ERR_NULL
+    arr = (GemmDesc * 1)(ok)
+    assert _lib.LIB.mg_check_list_host(arr, 0) == _lib.MG_ERR_SHAPE
+    assert _lib.LIB.mgemm_list(None, 1, None) == _lib.MG_ERR_NULL
+    assert _lib.LIB.mgemm_list(ctypes.addressof(arr), 2000, None) == _lib.MG_ERR_SHAPE

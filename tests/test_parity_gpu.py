@@ -323,3 +323,81 @@ def test_a3b_gate_up_swiglu_gathered_sampled():
     cols = np.concatenate([cols, np.tile(np.arange(I - 16, I), edge.size)])
     r = _swiglu_check(xb, token_of_row, wb, off, got, rows, cols)
     assert r.passed, str(r)
+
+
+# ------------------------------------------------ per-group descriptor list --
+
+def _list_check(groups_bits, outs):
+    """Every output element of every group against the oracle, bf16 gate."""
+    from oracle import bf16_bits_to_f64, check_bf16, grouped_list
+    a64 = [(bf16_bits_to_f64(a), bf16_bits_to_f64(b)) for a, b in groups_bits]
+    ref = grouped_list(a64)
+    mag = grouped_list([(np.abs(a), np.abs(b)) for a, b in a64])
+    for g, ((a, b), d, r, s) in enumerate(zip(groups_bits, outs, ref, mag)):
+        if r.size == 0:
+            continue
+        k = max(a.shape[1], 1)
+        rep = check_bf16(host_bits(d), r, s, k)
+        assert rep.passed, f"group {g}: {rep}"
+
+
+def test_grouped_list_mixed_shapes():
+    """Groups of different m, n, k in one launch: ragged tiles, row strides
+    wider than the rows (views into bigger buffers), an empty group, a group
+    with k = 0 (zeros), several tiles per group."""
+    shapes = [(300, 264, 136), (0, 64, 64), (1, 8, 8), (513, 520, 200), (40, 16, 0),
+              (256, 256, 512), (77, 1032, 72)]
+    groups_bits, groups, outs = [], [], []
+    for g, (m, n, k) in enumerate(shapes):
+        ab = normal_bf16_bits((m, k), 1.0, 500 + g, 1)
+        bb = normal_bf16_bits((n, k), k ** -0.5 if k else 1.0, 500 + g, 2)
+        groups_bits.append((ab, bb))
+        # A and B as views with padded rows (stride k + 16), D inside a wider buffer
+        abuf = torch.zeros((m, k + 16), dtype=torch.bfloat16, device="cuda")
+        bbuf = torch.zeros((n, k + 16), dtype=torch.bfloat16, device="cuda")
+        if m * k:
+            abuf[:, :k] = dev_bf16(ab)
+        if n * k:
+            bbuf[:, :k] = dev_bf16(bb)
+        dbuf = sentinel_bf16((m, n + 24))
+        groups.append((abuf[:, :k], bbuf[:, :k]))
+        outs.append(dbuf[:, :n])
+    _say("grouped_list mixed", shapes)
+    mg.grouped_list(groups, outs)
+    torch.cuda.synchronize()
+    _list_check(groups_bits, outs)
+    for g, (m, n, k) in enumerate(shapes):
+        pad = host_bits(outs[g]._base)[:, n:] if m else None
+        if pad is not None:
+            assert (pad == SENTINEL).all(), f"group {g}: padding columns written"
+
+
+def test_grouped_list_equals_mgrouped_forward():
+    """Per-expert groups pointing into one X and one W give bitwise the
+    M-grouped forward's result (same tiles, same reduction order)."""
+    sizes, N, K = [300, 0, 517, 64, 1000], 520, 264
+    off = offsets_from_sizes(sizes)
+    M = int(off[-1])
+    x = dev_bf16(normal_bf16_bits((M, K), K ** -0.5, 510, 1))
+    w = dev_bf16(normal_bf16_bits((len(sizes), N, K), K ** -0.5, 510, 2))
+    y = mg.fwd(x, w, dev_i32(off))
+    ylist = torch.empty_like(y)
+    groups = [(x[off[e]:off[e + 1]], w[e]) for e in range(len(sizes))]
+    outs = [ylist[off[e]:off[e + 1]] for e in range(len(sizes))]
+    mg.grouped_list(groups, outs)
+    torch.cuda.synchronize()
+    assert torch.equal(y, ylist)
+
+
+def test_grouped_list_flattened_lora_experts():
+    """Nested grouped GEMM flattened: 3 LoRA adapters x 4 experts = 12 groups,
+    each expert's rows times each adapter's rank-16 down projection."""
+    rng = np.random.default_rng(520)
+    K, R = 1024, 16
+    xs = [normal_bf16_bits((int(m), K), 1.0, 520, e, 1) for e, m in enumerate(rng.integers(0, 400, 4))]
+    ads = [normal_bf16_bits((R, K), K ** -0.5, 520, l, 2) for l in range(3)]
+    groups_bits = [(x, ad) for ad in ads for x in xs]
+    groups = [(dev_bf16(a), dev_bf16(b)) for a, b in groups_bits]
+    outs = mg.grouped_list(groups)
+    torch.cuda.synchronize()
+    _list_check(groups_bits, outs)
