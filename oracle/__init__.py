@@ -24,6 +24,11 @@ per expert; nothing blocked, fused or reordered):
   * A list of independent GEMMs D_g = A_g B_g^T with per-group shapes (the
     TransformerEngine PR #2045 review: one C API over lists of tensors; the
     CUTLASS discussion #1452: nested grouped GEMMs flattened into one list).
+  * MXFP8 M-grouped forward (torchao PR #3416: MXFP8 MoE grouped GEMMs with
+    e8m0 block scales in a blocked layout; DeepGEMM issue #10: operands
+    quantized along each GEMM's reduction axis): E4M3 elements, one E8M0
+    scale per 32 reduction steps, decoded exactly and summed in fp64; and the
+    blocked scale layout [ceil(K/128)][rows][4] the GEMM call reads.
   * bf16 outputs are the fp64 result rounded once, directly, to bf16 with
     round-to-nearest-even.
 
@@ -35,7 +40,11 @@ brute force with math.exp, one-hot closed forms that tell the gate half from
 the up half, gather-as-permutation identities, and a gate that rejects a wrong
 expert or a dropped term; for the descriptor list, exact rational brute force on
 groups of mixed shapes (empty and zero-reduction ones included), a one-hot
-transpose check and the flattened LoRA x experts identity.  Every function here
+transpose check and the flattened LoRA x experts identity; for MXFP8, the
+element and scale decoders against torch's float8_e4m3fn / float8_e8m0fnu
+casts on every code, closed forms, exact rational brute force on tiny inputs,
+power-of-two scale shifts that move whole rows or experts exactly, and the
+blocked layout against an index-by-index brute force.  Every function here
 is pinned; none is "parity
 unpinned".
 """
@@ -51,4 +60,12 @@ from .grouped_gemm import (  # noqa: F401
     sample_fwd_swiglu,
     grouped_list,
 )
-from .gate import check_bf16, check_bf16_swiglu, check_fp32, GateReport  # noqa: F401
+from .mx import (  # noqa: F401
+    e4m3_decode,
+    e8m0_decode,
+    mx_dequant,
+    grouped_fwd_mx,
+    sample_fwd_mx,
+    mx_scales_blocked,
+)
+from .gate import check_bf16, check_bf16_swiglu, check_bf16_mx, check_fp32, GateReport  # noqa: F401

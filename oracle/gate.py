@@ -25,6 +25,23 @@ multiply:
     dg = 2^-24 sqrt(K) S_g,  du = 2^-24 sqrt(K) S_u,
     silu'(g) = s (1 + g (1 - s)),  s = 1 / (1 + exp(-g)).
 
+bf16 outputs of the MXFP8 forward.  Same strict gate; the floor is that of
+the fp8 dot products of gfx950's scaled matrix-core instruction, which do not
+sum in fp32: measured on random E4M3 operands with random E8M0 scales, one
+64-deep instruction lands within 1.1e-4 (about 2^-13) of the sum of the
+absolute scaled products, as if the products were aligned to the largest one
+and kept to about 14 fractional bits.  The errors of successive instructions
+add at most linearly, so with a factor of two in hand:
+
+    |g - exact| <= ulp(g) / 2 + 2^-12 * S,   S = sum_k |a_k b_k|  (scaled values).
+
+A 32-element block dropped, scaled by a wrong power of two or taken from a
+wrong row moves an element by about sqrt(32) times a typical product: with
+block scales within a factor of two of each other (block maxima of Gaussian
+data) and K = 2048, some 20 times this floor.  A block far smaller than the
+largest ones of its sum is below it, as it is below the matrix cores' own
+precision.
+
 fp32 outputs (wgrad).  Relative Frobenius error <= 1e-4, over the whole
 tensor and per expert (a large expert would otherwise hide a wrong small
 one); an empty expert's block must be exactly zero (or exactly the prior
@@ -94,6 +111,25 @@ def check_bf16_swiglu(got_bits: np.ndarray, h: np.ndarray, g: np.ndarray, u: np.
         i = int(np.argmax(np.where(ok, -np.inf, np.abs(got - h))))
         worst = f"worst@{i}: got={got.flat[i]!r} exact={h.flat[i]!r}"
     return GateReport(int(got.size), fails == 0, fails, int((~strict).sum()), 0.0, worst)
+
+
+MX_FLOOR = 2.0 ** -12
+
+
+def check_bf16_mx(got_bits: np.ndarray, exact: np.ndarray, abs_sum: np.ndarray) -> GateReport:
+    """Gate for the bf16 output of the MXFP8 forward (see the header)."""
+    g = bf16_bits_to_f64(got_bits)
+    exact = np.asarray(exact, np.float64)
+    b = f64_round_bf16(exact)
+    strict = np.abs(g - b) <= bf16_ulp(b)
+    floor = np.abs(g - exact) <= 0.5 * bf16_ulp(g) + MX_FLOOR * abs_sum
+    ok = (strict | floor) & np.isfinite(g)
+    fails = int((~ok).sum())
+    worst = ""
+    if fails:
+        i = int(np.argmax(np.where(ok, -np.inf, np.abs(g - exact))))
+        worst = f"worst@{i}: got={g.flat[i]!r} exact={exact.flat[i]!r}"
+    return GateReport(int(g.size), fails == 0, fails, int((~strict).sum()), 0.0, worst)
 
 
 def rel_frob(got: np.ndarray, exact: np.ndarray) -> float:

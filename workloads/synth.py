@@ -223,3 +223,29 @@ def make_workload(cfg: int, name: Optional[str] = None) -> List[Workload]:
         if not ws:
             raise KeyError(name)
     return ws
+
+
+def mx_e4m3_codes(shape: Sequence[int], *key: int) -> np.ndarray:
+    """uint8 OCP E4M3 codes of roughly Gaussian values of the size MX blocks
+    hold (|v| mostly in [2^3, 2^8]): sign and 3-bit mantissa uniform, the
+    4-bit exponent field from floor(log2(64 |N(0, 1)|)) + 7 clipped to
+    [0, 15]; the NaN code S.1111.111 is never drawn."""
+    n = int(np.prod(shape, dtype=np.int64))
+    rng = _stream(*key)
+    out = np.empty(n, dtype=np.uint8)
+    for lo in range(0, n, _CHUNK):
+        hi = min(n, lo + _CHUNK)
+        v = np.abs(rng.standard_normal(hi - lo)) * 64.0
+        ex = np.clip(np.floor(np.log2(np.maximum(v, 1e-30))) + 7, 0, 15).astype(np.int64)
+        m = rng.integers(0, 8, hi - lo)
+        m = np.where((ex == 15) & (m == 7), 6, m)
+        sg = rng.integers(0, 2, hi - lo)
+        out[lo:hi] = (sg << 7 | ex << 3 | m).astype(np.uint8)
+    return out.reshape(tuple(shape))
+
+
+def mx_e8m0_codes(shape: Sequence[int], center: int, spread: int, *key: int) -> np.ndarray:
+    """uint8 E8M0 scale codes, uniform in [center - spread, center + spread]."""
+    rng = _stream(*key)
+    c = rng.integers(center - spread, center + spread + 1, int(np.prod(shape, dtype=np.int64)))
+    return np.clip(c, 0, 254).astype(np.uint8).reshape(tuple(shape))
