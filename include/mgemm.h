@@ -135,6 +135,40 @@ mg_status mgemm_list(const mg_gemm_desc* desc, int32_t G, void* stream);
  * breaks the rules above. */
 mg_status mg_check_list_host(const mg_gemm_desc* desc_host, int32_t G);
 
+/* MXFP8 M-grouped forward (torchao PR #3416: MoE training with MXFP8
+ * grouped GEMMs whose e8m0 block scales are first rearranged into the layout
+ * the GEMM reads; MXFP8 taken as the OCP microscaling format: E4M3 elements,
+ * one E8M0 scale 2^(s - 127) per 32 consecutive reduction steps):
+ *   y[i, n] = sum_k X[i, k] W[e, n, k]   for offsets[e] <= i < offsets[e+1],
+ *   X[i, k] = e4m3(x[i, k]) 2^(xs(i, k/32) - 127),  W likewise with ws.
+ * x: uint8 E4M3 codes [M, K]; w: uint8 E4M3 codes [E, N, K]; y: bf16 [M, N]
+ * (written, round to nearest even).
+ * x_scale: uint8 E8M0 codes in the BLOCKED layout [ceil(K/128)][M][4] (entry
+ * [t][i][j] scales x[i, 128 t + 32 j .. + 31]); w_scale: [E][ceil(K/128)][N][4]
+ * likewise per expert.  mg_mx_scales_blocked makes this layout from the plain
+ * [rows][K/32] one.  Pointers: x, w, y 16-byte aligned, scales 4-byte aligned.
+ * K a multiple of 32, N a multiple of 8; ceil(K/128) M and ceil(K/128) N
+ * below 2^29.  The products are those of the gfx950 scaled fp8 matrix-core
+ * instruction, accumulated in fp32: each 64-step product is exact to about
+ * 2^-13 of the sum of its absolute terms, not to fp32 rounding.  The MX
+ * input gradient is the same call on dy and the weights transposed to
+ * [E, K, N] and quantized along N (each GEMM's operands are quantized along
+ * its own reduction axis, DeepGEMM issue #10).  M == 0 or N == 0 is a no-op;
+ * K == 0 writes zeros.  Allocates nothing.  max_m_per_e: launch-size hint, as
+ * for mgemm_fwd. */
+mg_status mgemm_fwd_mx(const void* x, const void* x_scale, const void* w, const void* w_scale,
+                       const int32_t* offsets, void* y, int64_t M, int64_t N, int64_t K, int32_t E,
+                       int64_t max_m_per_e, void* stream);
+
+/* Blocked layout of MXFP8 scales (the torchao PR #3416 "scale blocked format"
+ * step, for the layout above): scales: uint8 [batch][rows][K/32] (DEVICE);
+ * blocked: uint8 [batch][ceil(K/128)][rows][4] (DEVICE, 4-byte aligned,
+ * written; must not overlap scales), entry [b][t][r][j] = scales[b][r][4t + j],
+ * or 127 (the code of 1.0) where 4t + j >= K/32.  K a multiple of 32.
+ * Enqueued on `stream`; allocates nothing. */
+mg_status mg_mx_scales_blocked(const void* scales, void* blocked, int64_t rows, int64_t K,
+                               int64_t batch, void* stream);
+
 /* K-grouped weight gradient in FP32 (RapidGEMM README, "Kernels", Kgemm;
  * wgrad is x^T dy, DeepGEMM issue #10, laid out like w so it can update w):
  *   dw[e, n, k] (= or +=) sum_{offsets[e] <= i < offsets[e+1]} dy[i, n] * x[i, k]

@@ -231,6 +231,65 @@ def grouped_list(groups, outs=None):
     return outs
 
 
+def mx_scales_blocked(scales: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """E8M0 scales [..., rows, K/32] (uint8) -> the blocked layout
+    [..., ceil(K/128), rows, 4] that fwd_mx reads (absent blocks 127)."""
+    if not isinstance(scales, torch.Tensor) or scales.dtype != torch.uint8 or scales.dim() < 2:
+        raise TypeError("scales must be a uint8 tensor [..., rows, K/32]")
+    _need(scales, "scales", torch.uint8, scales.dim())
+    *lead, rows, nb = scales.shape
+    batch = 1
+    for d in lead:
+        batch *= d
+    shape = (*lead, (nb + 3) // 4, rows, 4)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.uint8, device=scales.device)
+    else:
+        _need(out, "out", torch.uint8, len(shape))
+        if tuple(out.shape) != shape:
+            raise ValueError(f"out must be {shape}")
+    with torch.cuda.device(scales.device):
+        st = LIB.mg_mx_scales_blocked(scales.data_ptr(), out.data_ptr(), rows, 32 * nb, batch,
+                                      _stream(scales))
+    check(st, "mg_mx_scales_blocked")
+    return out
+
+
+def fwd_mx(x8: torch.Tensor, x_scale: torch.Tensor, w8: torch.Tensor, w_scale: torch.Tensor,
+           offsets: torch.Tensor, max_m_per_e: int = 0,
+           out: torch.Tensor | None = None) -> torch.Tensor:
+    """MXFP8 M-grouped forward: out[i] = X[i] @ W[e].T with X, W the E4M3
+    codes x8 [M, K], w8 [E, N, K] (uint8) times their E8M0 block scales.
+
+    x_scale: blocked [ceil(K/128), M, 4]; w_scale: blocked [E, ceil(K/128), N, 4]
+    (mx_scales_blocked makes them from [M, K/32] and [E, N, K/32]).  out bf16
+    [M, N]; rows past offsets[E] are left untouched."""
+    _need(x8, "x8", torch.uint8, 2)
+    _need(w8, "w8", torch.uint8, 3)
+    M, K = x8.shape
+    E, N, K2 = w8.shape
+    if K2 != K:
+        raise ValueError(f"x8 is [M, {K}] but w8 is [E, N, {K2}]")
+    kt = (K + 127) // 128
+    _need(x_scale, "x_scale", torch.uint8, 3)
+    _need(w_scale, "w_scale", torch.uint8, 4)
+    if tuple(x_scale.shape) != (kt, M, 4) or tuple(w_scale.shape) != (E, kt, N, 4):
+        raise ValueError(f"blocked scales must be [{kt}, {M}, 4] and [{E}, {kt}, {N}, 4]")
+    _offsets(offsets, E, x8.device)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x8.device)
+    else:
+        _need(out, "out", torch.bfloat16, 2)
+        if tuple(out.shape) != (M, N):
+            raise ValueError(f"out must be [{M}, {N}]")
+    with torch.cuda.device(x8.device):
+        st = LIB.mgemm_fwd_mx(x8.data_ptr(), x_scale.data_ptr(), w8.data_ptr(), w_scale.data_ptr(),
+                              offsets.data_ptr(), out.data_ptr(), M, N, K, E, int(max_m_per_e),
+                              _stream(x8))
+    check(st, "mgemm_fwd_mx")
+    return out
+
+
 def Mgemm(x: torch.Tensor, w: torch.Tensor, cnt: torch.Tensor, max_M_per_E: int = 0,
           transpose_B: bool = True) -> torch.Tensor:
     """RapidGEMM-shaped M-grouped GEMM (README, "Kernels").

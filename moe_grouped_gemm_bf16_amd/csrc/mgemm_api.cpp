@@ -173,6 +173,56 @@ mg_status mgemm_list(const mg_gemm_desc* desc, int32_t G, void* stream) {
   return launch(mg::kList, a, 0, s);
 }
 
+mg_status mgemm_fwd_mx(const void* x, const void* x_scale, const void* w, const void* w_scale,
+                       const int32_t* offsets, void* y, int64_t M, int64_t N, int64_t K, int32_t E,
+                       int64_t max_m_per_e, void* stream) {
+  mg_status st = check_sizes(M, N, K, E);
+  if (st != MG_OK) return st;
+  if (max_m_per_e < 0 || (K & 31)) return MG_ERR_SHAPE;       // whole 32-element scale blocks
+  // blocked scales are addressed with 31-bit offsets
+  const int64_t ks = (K + 127) / 128;
+  constexpr int64_t k2G = int64_t(1) << 31;
+  if (ks * M * 4 >= k2G || ks * N * 4 >= k2G) return MG_ERR_SHAPE;
+  if (((M + 255) / 256 + E) * ((N + 255) / 256) > kMaxRows) return MG_ERR_SHAPE;
+  if (M == 0 || N == 0) return MG_OK;
+  if (!offsets || !y || (K > 0 && (!x || !w || !x_scale || !w_scale))) return MG_ERR_NULL;
+  if ((K > 0 && (!aligned16(x) || !aligned16(w) ||
+                 (reinterpret_cast<uintptr_t>(x_scale) & 3u) ||
+                 (reinterpret_cast<uintptr_t>(w_scale) & 3u))) ||
+      !aligned16(y) || (reinterpret_cast<uintptr_t>(offsets) & 3u))
+    return MG_ERR_ALIGN;
+  if ((st = check_device()) != MG_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = maybe_validate(offsets, E, M, s)) != MG_OK) return st;
+  mg::KernelArgs a{};
+  a.p_src = w;
+  a.q_src = x;
+  a.p_scale = static_cast<const uint8_t*>(w_scale);
+  a.q_scale = static_cast<const uint8_t*>(x_scale);
+  a.offsets = offsets;
+  a.out = y;
+  a.M = M; a.N = N; a.K = K; a.E = E;
+  return launch(mg::kFwdMx, a, max_m_per_e, s);
+}
+
+mg_status mg_mx_scales_blocked(const void* scales, void* blocked, int64_t rows, int64_t K,
+                               int64_t batch, void* stream) {
+  if (rows < 0 || K < 0 || batch < 0 || (K & 31) || rows > kMaxRows || K > kMaxDim ||
+      batch > kMaxRows)
+    return MG_ERR_SHAPE;
+  const int64_t total = batch * ((K + 127) / 128) * rows;    // output dwords
+  if (total >= (int64_t(1) << 40)) return MG_ERR_SHAPE;
+  if (total == 0) return MG_OK;
+  if (!scales || !blocked) return MG_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(blocked) & 3u) return MG_ERR_ALIGN;
+  mg_status st;
+  if ((st = check_device()) != MG_OK) return st;
+  const int err = mg::launch_mx_scales_blocked(static_cast<const uint8_t*>(scales),
+                                               static_cast<uint8_t*>(blocked), rows, K, batch,
+                                               static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? MG_OK : MG_ERR_LAUNCH;
+}
+
 mg_status kgemm_wgrad(const void* dy, const void* x, const int32_t* offsets, float* dw,
                       int64_t M, int64_t N, int64_t K, int32_t E, int32_t accumulate,
                       void* stream) {

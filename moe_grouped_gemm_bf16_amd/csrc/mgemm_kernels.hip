@@ -18,6 +18,9 @@
 //   FWD      n  from W[e] [n][k]           m from X [m][k]   k  (both R-contiguous)
 //   DGRAD    k  from W[e] [n][k]           m from dY[m][n]   n  (P is R-strided)
 //   WGRAD    k  from X  [i][k]             n from dY[i][n]   i  (both R-strided)
+//   FWD_MX   as FWD, with E4M3 operands and one E8M0 scale per 32 k (MXFP8;
+//            torchao PR #3416): the same 128-byte staged rows hold 128 k, and
+//            the scaled fp8 matrix-core product applies the scales
 //
 // Operand staging: HBM -> LDS by direct-to-LDS buffer loads (no registers),
 // in LDS stages of kBK reduction steps, the next stage in flight while one is
@@ -54,6 +57,7 @@
 #include <atomic>
 #include <cstdlib>
 #include <mutex>
+#include <type_traits>
 #include <vector>
 
 #include "mgemm_launch.h"
@@ -66,6 +70,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -128,6 +133,19 @@ __device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t lds_addr, uint
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %1\n\t"
       "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "s"(lds_addr), "v"(voff), "s"(rsrc)
+      : "memory");
+}
+
+// Direct-to-LDS 4-byte load: lane l's dword lands at lds_addr + 4 l.
+__device__ __forceinline__ void dma4(const i32x4& rsrc, uint32_t lds_addr, uint32_t voff) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(save)
       : "s"(lds_addr), "v"(voff), "s"(rsrc)
@@ -775,14 +793,18 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
                                           int Pdim, int Qdim) {
   constexpr bool SWI = MODE == kFwdSwiglu;
   constexpr bool LIST = MODE == kList;
+  constexpr bool MX = MODE == kFwdMx;
   constexpr bool P_RS = MODE == kDgrad || MODE == kWgrad;   // P is R-strided for dgrad and wgrad
   constexpr bool Q_RS = MODE == kWgrad;    // Q is R-strided for wgrad
   constexpr int SPW = C::SEGS_PER_WAVE;
+  // element bytes, and reduction steps per stage (a staged row is kRowB bytes)
+  constexpr int ES = MX ? 1 : 2;
+  constexpr int BKE = kRowB / ES;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
 
   int ldP, ldQ;
-  if (MODE == kFwd || SWI || LIST) { ldP = (int)a.K; ldQ = (int)a.K; }   // LIST: per tile
+  if (MODE == kFwd || SWI || LIST || MX) { ldP = (int)a.K; ldQ = (int)a.K; }   // LIST: per tile
   else if (MODE == kDgrad) { ldP = (int)a.K; ldQ = (int)a.N; }
   else { ldP = (int)a.K; ldQ = (int)a.N; }
 
@@ -823,31 +845,49 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
         orow[j] = 64 * wr + 32 * (blk & 1) + in;
         grow = (blk < 2 ? 0 : I2) + orow[j];
       }
-      voff[j] = (uint32_t)(grow * ld + 8 * c) * 2u;
-      col[j] = 8 * c;
+      voff[j] = (uint32_t)(grow * ld * ES + 16 * c);
+      col[j] = 16 * c / ES;
     }
   }
+  // MXFP8: every stage also carries the operands' scales, [BP][4] bytes of P
+  // then [BQ][4] of Q, behind the data stages; a wave loads the dwords of
+  // kScRows rows of its operand, 64 rows per 4-byte direct-to-LDS load, with
+  // the stage's first kScLoads loads.
+  constexpr int kScStage = MX ? (C::BP + C::BQ) * 4 : 0;
+  constexpr int kScRows = C::BP / (C::SEGS_P / SPW);
+  constexpr int kScLoads = MX ? kScRows / 64 : 0;
+  static_assert(!MX || (kScRows % 64 == 0 && kScLoads <= SPW &&
+                        C::BQ == kScRows * ((C::SEGS - C::SEGS_P) / SPW)), "scale rows per wave");
+  const int w4 = seg0 / SPW;                // wave index within its operand
+  // MXFP8 data loads, without per-load tables: load d of a wave covers rows
+  // 8 (seg0 + d) + lane / 8 of its operand tile, and with seg0 a multiple of
+  // 8 the swizzled chunk of that row is (lane % 8) ^ (lane / 8) ^ (d % 4).
+  static_assert(!MX || (SPW % 8 == 0 && kRowChunks == 8), "MXFP8 load plan");
+  const int mx_c0 = (lane & 7) ^ (lane >> 3);
+  const uint32_t mx_rowoff = (uint32_t)(seg0 * 8 + (lane >> 3)) * (uint32_t)a.K;
+  const uint32_t sc_base = lds_u32(lds) + (uint32_t)C::LDS +
+                           (wP ? 0u : (uint32_t)C::BP * 4u) + (uint32_t)(4 * kScRows) * w4;
 
   // Operand bases and valid extents of a tile.
-  auto tile_src = [&](const Tile& t, const uint16_t*& src, int& nouter) {
-    const uint16_t* P = reinterpret_cast<const uint16_t*>(a.p_src);
-    const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.q_src);
-    if (MODE == kFwd) {            // P = W[e] rows n (R = k), Q = X rows m (R = k)
-      P += ((int64_t)t.e * a.N + t.p0) * a.K;
-      Q += (int64_t)t.q0 * a.K;
+  auto tile_src = [&](const Tile& t, const char*& src, int& nouter) {
+    const char* P = reinterpret_cast<const char*>(a.p_src);
+    const char* Q = reinterpret_cast<const char*>(a.q_src);
+    if (MODE == kFwd || MX) {      // P = W[e] rows n (R = k), Q = X rows m (R = k)
+      P += ((int64_t)t.e * a.N + t.p0) * a.K * ES;
+      Q += (int64_t)t.q0 * a.K * ES;
     } else if (SWI) {              // P = W13[e] rows from p0 (gate; up at + I), Q = X rows
-      P += ((int64_t)t.e * a.N + t.p0) * a.K;
-      if (a.gather == nullptr) Q += (int64_t)t.q0 * a.K;
+      P += ((int64_t)t.e * a.N + t.p0) * a.K * 2;
+      if (a.gather == nullptr) Q += (int64_t)t.q0 * a.K * 2;
     } else if (LIST) {             // P = B_g rows n, Q = A_g rows m (R = k), own strides
       const ListDesc dg = list_desc(S.list, t.e);
-      P = reinterpret_cast<const uint16_t*>(dg.b) + (int64_t)t.p0 * dg.ldb;
-      Q = reinterpret_cast<const uint16_t*>(dg.a) + (int64_t)t.q0 * dg.lda;
+      P = reinterpret_cast<const char*>(dg.b) + (int64_t)t.p0 * dg.ldb * 2;
+      Q = reinterpret_cast<const char*>(dg.a) + (int64_t)t.q0 * dg.lda * 2;
     } else if (MODE == kDgrad) {   // P = W[e] [n][k] R-strided, Q = dY rows m (R = n)
-      P += (int64_t)t.e * a.N * a.K + t.p0;
-      Q += (int64_t)t.q0 * a.N;
+      P += ((int64_t)t.e * a.N * a.K + t.p0) * 2;
+      Q += (int64_t)t.q0 * a.N * 2;
     } else {                       // P = X [i][k] R-strided, Q = dY [i][n] R-strided
-      P += (int64_t)t.r_begin * a.K + t.p0;
-      Q += (int64_t)t.r_begin * a.N + t.q0;
+      P += ((int64_t)t.r_begin * a.K + t.p0) * 2;
+      Q += ((int64_t)t.r_begin * a.N + t.q0) * 2;
     }
     const int nP = (LIST ? list_desc(S.list, t.e).n : Pdim) - t.p0;
     const int nQ = MODE == kWgrad ? Qdim - t.q0 : t.q_end - t.q0;
@@ -858,12 +898,15 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
   // ---- producer state (wave-uniform)
   TileSeq<MODE, C::BP, C::BQ> pseq;
   pseq.init(S);
-  const uint16_t* p_src = nullptr;
+  const char* p_src = nullptr;
   int p_nouter = 0, p_red = 0, p_nk = 0, p_kt = 0;
   i32x4 p_rc = {0, 0, 0, 0};
   bool p_live = false;
   uint32_t tvoff[SPW];            // fused SwiGLU forward: this tile's row offsets
   uint32_t tmask = 0;             // and which of the lane's rows are valid
+  i32x4 sc_rc = {0, 0, 0, 0};     // MXFP8: the tile's scale descriptor,
+  uint32_t sc_off = 0, sc_stride = 0;   // the lane's first scale row at stage 0, bytes per stage,
+  uint32_t sc_ok = 0;                   // and which of the lane's rows (+ 64 i) are in the tile
 #pragma unroll
   for (int j = 0; j < SPW; ++j) tvoff[j] = voff[j];
   auto p_next_tile = [&]() {
@@ -871,7 +914,7 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
     p_live = false;
     while (pseq.next(S, t)) {
       const int red = t.r_end - t.r_begin;
-      const int nk = (red + kBK - 1) / kBK;
+      const int nk = (red + BKE - 1) / BKE;
       if (nk <= 0) continue;                  // nothing to stage: the consumer stores zeros
       if (LIST) {
         // the group's row stride, and the lanes' row offsets under it
@@ -886,7 +929,24 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
       p_nk = nk;
       p_kt = 0;
       const int rows = p_nouter < outer ? (p_nouter > 0 ? p_nouter : 0) : outer;
-      p_rc = make_rsrc(p_src, (uint32_t)rows * (uint32_t)ld * 2u);
+      p_rc = make_rsrc(p_src, (uint32_t)rows * (uint32_t)ld * (uint32_t)ES);
+      if (MX) {
+        // blocked scales: stage s of row r at (s rows_total + r) 4 bytes; W's
+        // per expert.  A row past the tile's valid rows reads zero.
+        const int row = kScRows * w4 + lane;
+        const int ks = nk;                    // stages of the whole reduction (red = K)
+        const int base = wP ? t.p0 : t.q0, end = wP ? Pdim : t.q_end;
+        if (wP)
+          sc_rc = make_rsrc(a.p_scale + (int64_t)t.e * ks * a.N * 4,
+                            (uint32_t)ks * (uint32_t)a.N * 4u);
+        else
+          sc_rc = make_rsrc(a.q_scale, (uint32_t)ks * (uint32_t)a.M * 4u);
+        sc_off = (uint32_t)(base + row) * 4u;
+        sc_stride = (uint32_t)(wP ? a.N : a.M) * 4u;
+        sc_ok = 0;
+#pragma unroll
+        for (int i = 0; i < kScLoads; ++i) sc_ok |= (base + row + 64 * i < end ? 1u : 0u) << i;
+      }
       if (SWI) {
         tmask = 0;
         if (wP) {
@@ -929,17 +989,31 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
     if (!rs) return p_rc;
     const int rr = min(p_red - r0, kBK), oc = min(p_nouter, outer);
     const uint32_t bytes = rr > 0 && oc > 0 ? ((uint32_t)(rr - 1) * ld + oc) * 2u : 0u;
-    return make_rsrc(p_src + (int64_t)r0 * ld, bytes);
+    return make_rsrc(p_src + (int64_t)r0 * ld * 2, bytes);
   };
-  auto dma_one = [&](const i32x4& rsrc, uint32_t dst, int d, int r0) {
+  // Load d of the stage whose data go to `dst` (and, MXFP8, whose scales go
+  // to `sdst`, loaded with the first loads); returns the vector-memory
+  // operations issued.
+  auto dma_one = [&](const i32x4& rsrc, uint32_t dst, uint32_t sdst, int d, int r0) {
     uint32_t off;
-    if (SWI || LIST)
+    if (MX) {
+      const int cj = 16 * (mx_c0 ^ (d & 3));
+      off = (mx_rowoff + (uint32_t)d * 8u * (uint32_t)a.K + (uint32_t)(cj + r0)) |
+            (r0 + cj < p_red ? 0u : kOOB);
+    } else if (SWI || LIST)
       off = (tvoff[d] + (uint32_t)r0 * 2u) |
             (r0 + col[d] < p_red && ((tmask >> d) & 1u) ? 0u : kOOB);
     else
       off = rs ? (voff[d] | (col[d] < p_nouter ? 0u : kOOB))
-               : ((voff[d] + (uint32_t)r0 * 2u) | (r0 + col[d] < p_red ? 0u : kOOB));
+               : ((voff[d] + (uint32_t)r0 * ES) | (r0 + col[d] < p_red ? 0u : kOOB));
     dma16(rsrc, dst + d * 1024u, off);
+    if (MX && d < kScLoads) {
+      const uint32_t so = (sc_off + 256u * d + (uint32_t)(r0 / BKE) * sc_stride) |
+                          ((sc_ok >> d) & 1u ? 0u : kOOB);
+      dma4(sc_rc, sdst + 256u * d, so);
+      return 2;
+    }
+    return 1;
   };
   auto p_advance = [&]() {
     after[gp % kStages] = issued;
@@ -949,21 +1023,24 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
   // Issue the producer's next stage in one go.
   auto produce = [&]() {
     if (!p_live) return;
-    const int r0 = p_kt * kBK;
+    const int r0 = p_kt * BKE;
     const uint32_t dst = lds_base + (uint32_t)((gp % kStages) * C::STAGE);
+    const uint32_t sdst = sc_base + (uint32_t)((gp % kStages) * kScStage);
     const i32x4 rsrc = stage_rsrc(r0);
 #pragma unroll
-    for (int d = 0; d < SPW; ++d) dma_one(rsrc, dst, d, r0);
-    issued += SPW;
+    for (int d = 0; d < SPW; ++d) issued += dma_one(rsrc, dst, sdst, d, r0);
     p_advance();
   };
 
   // ---- fragment addresses (byte offsets within an operand tile)
   const int wp = wave / C::WQ, wq = wave % C::WQ;
   const int l32 = lane & 31, h = lane >> 5, L = lane & 15, g16 = (lane >> 4) & 1;
-  constexpr int KK = kBK / 16;                 // 16-wide k-slices per stage
+  // k-slices per stage: 16 bf16 steps (one 16-byte read per lane), or, MXFP8,
+  // 64 fp8 steps (two 16-byte reads per lane)
+  constexpr int KR = kBK / 16;                 // 16-byte fragment reads per staged row and lane
+  constexpr int KK = MX ? KR / 2 : KR;
   static_assert(KK % 2 == 0, "fragment double buffer parity");
-  uint32_t offP[P_RS ? C::MP : KK], offQ[Q_RS ? C::MQ : KK];
+  uint32_t offP[P_RS ? C::MP : KR], offQ[Q_RS ? C::MQ : KR];
   // R-contiguous: row = base + 32 i + l32 (swizzle depends on l32 only),
   // chunk 2 kk + h; entry kk, then + 32 kRowB i.
   // R-strided: row 8 h + L/4 (+ 16 kk + 4 t), outer base + 32 i + 16 g16 + 4 (L % 4).
@@ -981,14 +1058,14 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
     for (int i = 0; i < C::MP; ++i) offP[i] = rs_off(wp * C::WTP, i, C::BP);
   } else {
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) offP[kk] = rc_off(wp * C::WTP, kk);
+    for (int kk = 0; kk < KR; ++kk) offP[kk] = rc_off(wp * C::WTP, kk);
   }
   if (Q_RS) {
 #pragma unroll
     for (int j = 0; j < C::MQ; ++j) offQ[j] = rs_off(wq * C::WTQ, j, C::BQ);
   } else {
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) offQ[kk] = rc_off(wq * C::WTQ, kk);
+    for (int kk = 0; kk < KR; ++kk) offQ[kk] = rc_off(wq * C::WTQ, kk);
   }
 
   f32x16 acc[C::MP][C::MQ];
@@ -997,12 +1074,42 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
 #pragma unroll
     for (int j = 0; j < C::MQ; ++j) acc[i][j] = f32x16{};
 
+  // MXFP8 fragments.  The scaled 32x32x64 fp8 product takes from lane l
+  // (outer index l % 32, h = l / 32) 32 bytes: bytes 0-15 are reduction
+  // steps 16 h + 0..15 and bytes 16-31 steps 32 + 16 h + 0..15, so the first
+  // 32 steps form one scale block and the last 32 the other; the scale of
+  // block b of outer index r comes from lane r + 32 b.  Slice kk of a staged
+  // row (bytes 64 kk .. 64 kk + 63 = MX blocks 2 kk, 2 kk + 1) is therefore
+  // read as chunks 4 kk + h and 4 kk + 2 + h -- the bf16 reads of slices 2 kk
+  // and 2 kk + 1 -- and lane l passes the scale byte 2 kk + h of its row.
+  typedef typename std::conditional<MX, i32x8, bf16x8>::type FragT;
   struct Frags {
-    bf16x8 p[C::MP], q[C::MQ];
+    FragT p[C::MP], q[C::MQ];
+    uint32_t sp[MX ? C::MP : 1], sq[MX ? C::MQ : 1];
   };
   auto read = [&](int g, int kk, Frags& f) {
     const char* tp = lds + (g % kStages) * C::STAGE;
     const char* tq = tp + C::P_BYTES;
+    if constexpr (MX) {
+      auto frag8 = [&](const char* tile, uint32_t off0, uint32_t off1) {
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(tile + off0);
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(tile + off1);
+        return (i32x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      const char* sc = lds + C::LDS + (g % kStages) * kScStage;
+      const int sh = 8 * (2 * kk + h);
+#pragma unroll
+      for (int i = 0; i < C::MP; ++i) {
+        f.p[i] = frag8(tp, offP[2 * kk] + i * 32 * kRowB, offP[2 * kk + 1] + i * 32 * kRowB);
+        f.sp[i] = *reinterpret_cast<const uint32_t*>(sc + (wp * C::WTP + 32 * i + l32) * 4) >> sh;
+      }
+#pragma unroll
+      for (int j = 0; j < C::MQ; ++j) {
+        f.q[j] = frag8(tq, offQ[2 * kk] + j * 32 * kRowB, offQ[2 * kk + 1] + j * 32 * kRowB);
+        f.sq[j] = *reinterpret_cast<const uint32_t*>(sc + C::BP * 4 + (wq * C::WTQ + 32 * j + l32) * 4) >> sh;
+      }
+      return;
+    } else {
 #pragma unroll
     for (int i = 0; i < C::MP; ++i)
       f.p[i] = P_RS ? frag_rs(tp, offP[i] + kk * 16 * C::BP * 2, 4 * C::BP * 2)
@@ -1011,6 +1118,7 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
     for (int j = 0; j < C::MQ; ++j)
       f.q[j] = Q_RS ? frag_rs(tq, offQ[j] + kk * 16 * C::BQ * 2, 4 * C::BQ * 2)
                     : frag_rc(tq, offQ[kk] + j * 32 * kRowB);
+    }
   };
   // wait until this wave's loads of stage g have landed
   auto wait_stage = [&](int g) {
@@ -1029,7 +1137,7 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
   // (of the stage set up in `sd`) spread evenly between them.
   struct StageDma {
     int r0;
-    uint32_t dst;
+    uint32_t dst, sdst;
     i32x4 rsrc;
     bool on;
   };
@@ -1038,10 +1146,12 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
     sd.on = p_live;
     sd.r0 = 0;
     sd.dst = 0;
+    sd.sdst = 0;
     sd.rsrc = p_rc;
     if (sd.on) {
-      sd.r0 = p_kt * kBK;
+      sd.r0 = p_kt * BKE;
       sd.dst = lds_base + (uint32_t)((gp % kStages) * C::STAGE);
+      sd.sdst = sc_base + (uint32_t)((gp % kStages) * kScStage);
       sd.rsrc = stage_rsrc(sd.r0);
     }
     return sd;
@@ -1051,13 +1161,16 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
 #pragma unroll
     for (int x = x0; x < x1; ++x) {
       const int i = x / C::MQ, j = x % C::MQ;
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.p[i], f.q[j], acc[i][j], 0, 0, 0);
+      if constexpr (MX)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            f.p[i], f.q[j], acc[i][j], 0, 0, 0, (int)f.sp[i], 0, (int)f.sq[j]);
+      else
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.p[i], f.q[j], acc[i][j], 0, 0, 0);
       // after product x, (x - x0 + 1) (d1 - d0) / (x1 - x0) loads are due
       while (d < d1 && (d - d0) * (x1 - x0) < (x - x0 + 1) * (d1 - d0)) {
         if (sd.on) {
           __builtin_amdgcn_sched_barrier(0);
-          dma_one(sd.rsrc, sd.dst, d, sd.r0);
-          ++issued;
+          issued += dma_one(sd.rsrc, sd.dst, sd.sdst, d, sd.r0);
           __builtin_amdgcn_sched_barrier(0);
         }
         ++d;
@@ -1291,7 +1404,7 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
   TileSeq<MODE, C::BP, C::BQ> cseq;
   cseq.init(S);
   Frags fr[2];
-  const StageDma sd_none = {0, 0u, p_rc, false};
+  const StageDma sd_none = {0, 0u, 0u, p_rc, false};
   int g = 0;
   if (gp > 0) {
     wait_stage(0);
@@ -1300,7 +1413,7 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
   }
   Tile ct;
   while (cseq.next(S, ct)) {
-    const int nk = (ct.r_end - ct.r_begin + kBK - 1) / kBK;
+    const int nk = (ct.r_end - ct.r_begin + BKE - 1) / BKE;
     for (int kt = 0; kt < nk; ++kt, ++g) {
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
@@ -1342,14 +1455,14 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
 template <int MODE, class C>
 __global__ __launch_bounds__(C::NT)
 void grouped_gemm_kernel(KernelArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[C::LDS];
+  __shared__ __attribute__((aligned(16))) char lds[C::LDS + (MODE == kFwdMx ? kStages * (C::BP + C::BQ) * 4 : 0)];
   // keys [64] | scan [16] | mine [2 kMaxExperts + 8] | pref [E+1] | offs [E+1] | inv [E]
   // (keys and mine 16-byte aligned: they are read four entries at a time)
   __shared__ __attribute__((aligned(16))) int sched[64 + 16 + 2 * kMaxExperts + 8 +
                                                    2 * (kMaxExperts + 1) + kMaxExperts];
 
   int Pdim, Qdim;
-  if (MODE == kFwd) {
+  if (MODE == kFwd || MODE == kFwdMx) {
     Pdim = (int)a.N; Qdim = (int)a.M;
   } else if (MODE == kFwdSwiglu) {
     Pdim = (int)(a.N / 2); Qdim = (int)a.M;      // outputs: I = N / 2 columns
@@ -1374,7 +1487,7 @@ void grouped_gemm_kernel(KernelArgs a) {
   S.tilesP = MODE == kList ? 1 : (Pdim + kPStep - 1) / kPStep;
   S.list = MODE == kList ? a.list : nullptr;
   S.tilesQ = (Qdim + C::BQ - 1) / C::BQ;
-  S.red = MODE == kFwd || MODE == kFwdSwiglu ? (int)a.K : (int)a.N;
+  S.red = MODE == kFwd || MODE == kFwdSwiglu || MODE == kFwdMx ? (int)a.K : (int)a.N;
   // raster group: about sqrt(nx) M-tiles, more when there are few P-tiles,
   // so that the nx tiles an XCD runs at once span ~gm x (nx / gm) panels
   const int nx = gridDim.x >> 3;
@@ -1406,6 +1519,11 @@ using Cfg = TileCfg<256, 256, 2, 4>;    // 8 waves (2 per SIMD), 128x64 per wave
 #else
 using Cfg = TileCfg<256, 256, 2, 2>;    // 4 waves (1 per SIMD), 128x128 per wave
 #endif
+// MXFP8: one wave per SIMD, 128x128 per wave.  Its 32-byte fp8 fragments,
+// double-buffered, and 16 accumulator blocks need more than the 256
+// registers a wave has when two share a SIMD; alone it has 512.
+using CfgMx = TileCfg<256, 256, 2, 2>;
+static_assert(CfgMx::BP == Cfg::BP && CfgMx::BQ == Cfg::BQ, "one tile size for the launch sizing");
 
 // Compute units of the current device (one resident workgroup each).
 static int device_cus() {
@@ -1487,7 +1605,7 @@ int launch_grouped(int mode, const KernelArgs& a_in, int64_t max_m_per_e, hipStr
     const int64_t tilesQ = (a.N + Cfg::BQ - 1) / Cfg::BQ;
     tiles = (int64_t)a.E * tilesQ * tilesP;
   } else {
-    const int64_t Pdim = mode == kFwd ? a.N : (mode == kFwdSwiglu ? a.N / 2 : a.K);
+    const int64_t Pdim = mode == kFwd || mode == kFwdMx ? a.N : (mode == kFwdSwiglu ? a.N / 2 : a.K);
     const int64_t pstep = mode == kFwdSwiglu ? Cfg::BP / 2 : Cfg::BP;
     const int64_t tilesP = (Pdim + pstep - 1) / pstep;
     int64_t mt = (a.M + Cfg::BQ - 1) / Cfg::BQ + a.E;       // sum_e ceil(m_e/BQ) <= this
@@ -1513,8 +1631,44 @@ int launch_grouped(int mode, const KernelArgs& a_in, int64_t max_m_per_e, hipStr
       hipLaunchKernelGGL((grouped_gemm_kernel<kFwdSwiglu, Cfg>), g, b, 0, s, a);
       break;
     case kList: hipLaunchKernelGGL((grouped_gemm_kernel<kList, Cfg>), g, b, 0, s, a); break;
+    case kFwdMx:
+      hipLaunchKernelGGL((grouped_gemm_kernel<kFwdMx, CfgMx>), g, dim3(CfgMx::NT), 0, s, a);
+      break;
     default: hipLaunchKernelGGL((grouped_gemm_kernel<kWgrad, Cfg>), g, b, 0, s, a); break;
   }
+  return (int)hipGetLastError();
+}
+
+// Blocked MXFP8 scales: one thread per output dword, the four scales of row r
+// for reduction steps 128 t .. 128 t + 127 (127, the code of 1.0, for
+// blocks past K / 32).  The torchao PR #3416 rearranges e8m0 scales into the
+// layout its grouped GEMM reads with a kernel of its own; this is that step
+// for the layout the MXFP8 forward above stages per LDS stage.
+__global__ __launch_bounds__(256) void mx_scales_blocked_kernel(const uint8_t* __restrict__ src,
+                                                                 uint32_t* __restrict__ dst,
+                                                                 int64_t rows, int64_t nb,
+                                                                 int64_t nt, int64_t total) {
+  const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (o >= total) return;
+  const int64_t r = o % rows, bt = o / rows, t = bt % nt, b = bt / nt;
+  const uint8_t* row = src + (b * rows + r) * nb;
+  uint32_t v = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t blk = 4 * t + j;
+    v |= (uint32_t)(blk < nb ? row[blk] : 127u) << (8 * j);
+  }
+  dst[o] = v;
+}
+
+int launch_mx_scales_blocked(const uint8_t* src, uint8_t* dst, int64_t rows, int64_t K,
+                             int64_t batch, hipStream_t s) {
+  const int64_t nb = K / 32, nt = (K + 127) / 128;
+  const int64_t total = batch * nt * rows;
+  if (total <= 0) return 0;
+  const int64_t blocks = (total + 255) / 256;
+  hipLaunchKernelGGL(mx_scales_blocked_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src,
+                     reinterpret_cast<uint32_t*>(dst), rows, nb, nt, total);
   return (int)hipGetLastError();
 }
 

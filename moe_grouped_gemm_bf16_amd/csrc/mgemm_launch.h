@@ -5,7 +5,7 @@
 
 namespace mg {
 
-enum { kFwd = 0, kDgrad = 1, kWgrad = 2, kFwdSwiglu = 3, kList = 4 };
+enum { kFwd = 0, kDgrad = 1, kWgrad = 2, kFwdSwiglu = 3, kList = 4, kFwdMx = 5 };
 
 // Largest expert count a launch accepts: the device-side scheduler keeps the
 // per-expert tile prefix in LDS, two entries per thread of a 512-thread block.
@@ -22,8 +22,10 @@ struct ListDesc {
 };
 
 struct KernelArgs {
-  const void* p_src;        // FWD/DGRAD: W [E,N,K]; FWD_SWIGLU: W13 [E,N=2I,K]; WGRAD: X [M,K]
-  const void* q_src;        // FWD: X [M,K]; FWD_SWIGLU: X [M or T,K]; DGRAD/WGRAD: dY [M,N]
+  const void* p_src;        // FWD/DGRAD: W [E,N,K]; FWD_SWIGLU: W13 [E,N=2I,K]; WGRAD: X [M,K];
+                            // FWD_MX: W8 [E,N,K] E4M3 codes
+  const void* q_src;        // FWD: X [M,K]; FWD_SWIGLU: X [M or T,K]; DGRAD/WGRAD: dY [M,N];
+                            // FWD_MX: X8 [M,K] E4M3 codes
   const int32_t* offsets;   // [E+1], device
   void* out;                // FWD: Y [M,N] bf16; FWD_SWIGLU: H [M,N/2] bf16; DGRAD: dX [M,K] bf16;
                             // WGRAD: dW [E,N,K] fp32
@@ -35,7 +37,14 @@ struct KernelArgs {
   int64_t T;                // FWD_SWIGLU with gather: rows of x
   float* ws;                // WGRAD token split: 2 slots of 256 x 256 fp32 per split tile
   uint32_t* tickets;        // one zeroed counter per split tile (every launch leaves them zeroed)
+  const uint8_t* p_scale;   // FWD_MX: W's E8M0 scales, blocked [E][ceil(K/128)][N][4]
+  const uint8_t* q_scale;   // FWD_MX: X's E8M0 scales, blocked [ceil(K/128)][M][4]
 };
+
+// Rearrange E8M0 scales [batch][rows][K/32] into the blocked layout
+// [batch][ceil(K/128)][rows][4] (absent blocks 127).  Returns a hipError_t value.
+int launch_mx_scales_blocked(const uint8_t* src, uint8_t* dst, int64_t rows, int64_t K,
+                             int64_t batch, hipStream_t s);
 
 // Enqueue one grouped GEMM on stream `s`.  Returns a hipError_t value.
 int launch_grouped(int mode, const KernelArgs& a, int64_t max_m_per_e, hipStream_t s);

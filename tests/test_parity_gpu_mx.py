@@ -1,0 +1,192 @@
+"""GPU parity of the MXFP8 grouped forward and its scale-layout kernel
+against the fp64 oracle (needs an MI355X).
+
+The GEMM gets the oracle's blocked scales (so its cases do not depend on the
+layout kernel); the layout kernel is compared bit for bit with the oracle's
+layout; one end-to-end case feeds the kernel-made layout to the GEMM.  bf16
+outputs pass the MX gate of oracle/gate.py (one bf16 ulp of the rounded
+exact value, or within the precision floor of the fp8 matrix-core products).
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_grouped_gemm_bf16_amd as mg
+from oracle import check_bf16_mx, grouped_fwd, grouped_fwd_mx, mx_dequant, mx_scales_blocked
+from oracle import sample_fwd_mx
+from parity import SENTINEL, dev_i32, host_bits, sentinel_bf16
+from workloads import make_workload, offsets_from_sizes
+from workloads.synth import mx_e4m3_codes, mx_e8m0_codes
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _u8(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).to("cuda")
+
+
+def _mx_inputs(sizes, N, K, spread, seed, extra_rows=0, center=121):
+    off = offsets_from_sizes(sizes)
+    M = int(off[-1]) + extra_rows
+    E = len(sizes)
+    x8 = mx_e4m3_codes((M, K), 8000, seed, 1)
+    w8 = mx_e4m3_codes((E, N, K), 8000, seed, 2)
+    xs = mx_e8m0_codes((M, K // 32), center, spread, 8000, seed, 3)
+    ws = mx_e8m0_codes((E, N, K // 32), center, spread, 8000, seed, 4)
+    return off, M, E, x8, w8, xs, ws
+
+
+def _run(off, M, N, x8, w8, xs, ws, hint=0):
+    y = mg.fwd_mx(_u8(x8), _u8(mx_scales_blocked(xs)), _u8(w8), _u8(mx_scales_blocked(ws)),
+                  dev_i32(off), hint, out=sentinel_bf16((M, N)))
+    torch.cuda.synchronize()
+    return host_bits(y)
+
+
+def _gate_full(off, x8, w8, xs, ws, got):
+    o = int(off[-1])
+    exact = grouped_fwd_mx(x8, xs, w8, ws, off)[:o]
+    mag = grouped_fwd(np.abs(mx_dequant(x8, xs)), np.abs(mx_dequant(w8, ws)), off)[:o]
+    return check_bf16_mx(got[:o], exact, mag)
+
+
+# (expert sizes, N, K, scale spread): ragged experts, empty ones, reductions
+# of one 32-block, of less than one 128-step stage, with a ragged last stage,
+# and of many stages
+MX_CASES = [
+    ([300, 0, 17, 513], 264, 256, 2),
+    ([1, 255, 257], 136, 96, 1),
+    ([700], 520, 416, 3),
+    ([0, 0, 129], 8, 32, 0),
+    ([64, 0, 100, 64, 300, 1, 64, 200], 256, 2048, 1),
+    ([513, 511], 1032, 160, 2),
+]
+
+
+@pytest.mark.parametrize("case", range(len(MX_CASES)))
+def test_fwd_mx(case):
+    sizes, N, K, spread = MX_CASES[case]
+    _say("fwd_mx", sizes, N, K, spread)
+    off, M, E, x8, w8, xs, ws = _mx_inputs(sizes, N, K, spread, case, extra_rows=3)
+    got = _run(off, M, N, x8, w8, xs, ws)
+    rep = _gate_full(off, x8, w8, xs, ws, got)
+    assert rep.passed, str(rep)
+    assert (got[int(off[-1]):] == SENTINEL).all(), "rows past offsets[E] were written"
+
+
+def test_fwd_mx_wide_scale_range_and_extreme_codes():
+    """Scales across 2^-40 .. 2^40 per operand and elements at +-448, the
+    subnormals and zeros: the exponent arithmetic of the scaled product."""
+    sizes, N, K = [130, 70], 136, 256
+    off, M, E, x8, w8, xs, ws = _mx_inputs(sizes, N, K, 40, 99, center=127)
+    x8 = x8.copy(); w8 = w8.copy()
+    x8[::7, ::5] = 0x7E; w8[:, ::3, 1::7] = 0xFE          # +448, -448
+    x8[1::9, 2::11] = 0x01; w8[:, 2::5, ::13] = 0x07      # subnormals
+    x8[3::4, 64:96] = 0                                   # a zero block
+    _say("fwd_mx extremes", sizes, N, K)
+    got = _run(off, M, N, x8, w8, xs, ws)
+    rep = _gate_full(off, x8, w8, xs, ws, got)
+    assert rep.passed, str(rep)
+
+
+def test_fwd_mx_unit_scales_equal_torch_fp8_matmul_values():
+    """With every scale 1.0 the result is the plain product of the decoded
+    E4M3 values (pinned in the oracle against torch's float8 cast)."""
+    sizes, N, K = [200, 56], 128, 512
+    off, M, E, x8, w8, _, _ = _mx_inputs(sizes, N, K, 0, 5)
+    xs = np.full((M, K // 32), 127, np.uint8)
+    ws = np.full((E, N, K // 32), 127, np.uint8)
+    _say("fwd_mx unit scales", sizes, N, K)
+    got = _run(off, M, N, x8, w8, xs, ws)
+    assert _gate_full(off, x8, w8, xs, ws, got).passed
+
+
+@pytest.mark.parametrize("rows,K,batch", [(1, 32, 1), (257, 96, 1), (300, 416, 3), (64, 2048, 2),
+                                          (1000, 160, 1)])
+def test_scales_blocked_kernel_bit_exact(rows, K, batch):
+    _say("mx_scales_blocked", rows, K, batch)
+    s = mx_e8m0_codes((batch, rows, K // 32), 127, 127, 8100, rows, K)
+    got = mg.mx_scales_blocked(_u8(s)).cpu().numpy()
+    want = mx_scales_blocked(s)
+    assert got.shape == want.shape
+    np.testing.assert_array_equal(got, want)
+
+
+def test_fwd_mx_end_to_end_with_layout_kernel():
+    sizes, N, K = [90, 0, 333], 264, 288
+    off, M, E, x8, w8, xs, ws = _mx_inputs(sizes, N, K, 2, 11)
+    _say("fwd_mx end to end", sizes, N, K)
+    bx = mg.mx_scales_blocked(_u8(xs))
+    bw = mg.mx_scales_blocked(_u8(ws))
+    y = mg.fwd_mx(_u8(x8), bx, _u8(w8), bw, dev_i32(off))
+    torch.cuda.synchronize()
+    assert _gate_full(off, x8, w8, xs, ws, host_bits(y)).passed
+
+
+def test_fwd_mx_zero_reduction_and_empty_experts():
+    M, N, E = 40, 64, 3
+    off = offsets_from_sizes([0, 25, 0])
+    _say("fwd_mx K=0 and empty experts")
+    x8 = torch.zeros((M, 0), dtype=torch.uint8, device="cuda")
+    w8 = torch.zeros((E, N, 0), dtype=torch.uint8, device="cuda")
+    bx = torch.zeros((0, M, 4), dtype=torch.uint8, device="cuda")
+    bw = torch.zeros((E, 0, N, 4), dtype=torch.uint8, device="cuda")
+    y = mg.fwd_mx(x8, bx, w8, bw, dev_i32(off), out=sentinel_bf16((M, N)))
+    got = host_bits(y)
+    assert (got[:25] == 0).all() and (got[25:] == SENTINEL).all()
+    # all experts empty: nothing is written
+    off0 = offsets_from_sizes([0, 0, 0])
+    K = 64
+    y = mg.fwd_mx(torch.zeros((M, K), dtype=torch.uint8, device="cuda"),
+                  torch.zeros((1, M, 4), dtype=torch.uint8, device="cuda"),
+                  torch.zeros((E, N, K), dtype=torch.uint8, device="cuda"),
+                  torch.zeros((E, 1, N, 4), dtype=torch.uint8, device="cuda"),
+                  dev_i32(off0), out=sentinel_bf16((M, N)))
+    assert (host_bits(y) == SENTINEL).all()
+
+
+def test_fwd_mx_rejects_bad_shapes():
+    x8 = torch.zeros((8, 48), dtype=torch.uint8, device="cuda")      # K not a multiple of 32
+    w8 = torch.zeros((1, 8, 48), dtype=torch.uint8, device="cuda")
+    bx = torch.zeros((1, 8, 4), dtype=torch.uint8, device="cuda")
+    bw = torch.zeros((1, 1, 8, 4), dtype=torch.uint8, device="cuda")
+    with pytest.raises(mg.MgemmError):
+        mg.fwd_mx(x8, bx, w8, bw, dev_i32(offsets_from_sizes([8])))
+
+
+@pytest.mark.parametrize("name", ["a3b_gate_up", "a3b_down"])
+def test_a3b_mx_sampled(name):
+    """The 30B-A3B expert shapes with MXFP8 operands, in the launch the bench
+    times: sampled elements against the oracle, untouched rows, and two runs
+    bit-identical."""
+    (wl,) = make_workload(4, name)
+    off = np.asarray(wl.offsets)
+    M, N, K, E = wl.M, wl.N, wl.K, wl.E
+    _say("a3b mx", name, M, N, K, E)
+    x8 = mx_e4m3_codes((M, K), 8200, 1)
+    w8 = mx_e4m3_codes((E, N, K), 8200, 2)
+    xs = mx_e8m0_codes((M, K // 32), 121, 1, 8200, 3)
+    ws = mx_e8m0_codes((E, N, K // 32), 121, 1, 8200, 4)
+    dx8, dw8 = _u8(x8), _u8(w8)
+    bx, bw = _u8(mx_scales_blocked(xs)), _u8(mx_scales_blocked(ws))
+    o = dev_i32(off)
+    y1 = mg.fwd_mx(dx8, bx, dw8, bw, o, out=sentinel_bf16((M, N)))
+    y2 = mg.fwd_mx(dx8, bx, dw8, bw, o, out=sentinel_bf16((M, N)))
+    g1, g2 = host_bits(y1), host_bits(y2)
+    assert (g1 == g2).all(), "not deterministic"
+    last = int(off[-1])
+    assert (g1[last:] == SENTINEL).all()
+    rng = np.random.default_rng(8201)
+    rows = rng.integers(0, last, 2048)
+    cols = rng.integers(0, N, 2048)
+    # the first and last rows and columns of every expert too
+    edges = np.concatenate([off[:-1][np.diff(off) > 0], off[1:][np.diff(off) > 0] - 1])
+    rows = np.concatenate([rows, edges, edges])
+    cols = np.concatenate([cols, np.zeros_like(edges), np.full_like(edges, N - 1)])
+    val, mag = sample_fwd_mx(x8, xs, w8, ws, off, rows, cols)
+    rep = check_bf16_mx(g1[rows, cols], val, mag)
+    assert rep.passed, str(rep)

@@ -227,20 +227,21 @@ def make_workload(cfg: int, name: Optional[str] = None) -> List[Workload]:
 
 def mx_e4m3_codes(shape: Sequence[int], *key: int) -> np.ndarray:
     """uint8 OCP E4M3 codes of roughly Gaussian values of the size MX blocks
-    hold (|v| mostly in [2^3, 2^8]): sign and 3-bit mantissa uniform, the
-    4-bit exponent field from floor(log2(64 |N(0, 1)|)) + 7 clipped to
-    [0, 15]; the NaN code S.1111.111 is never drawn."""
+    hold (|v| mostly in [2^3, 2^8]): sign and 3-bit mantissa from one uniform
+    random byte, the 4-bit exponent field floor(log2(64 |N(0, 1)|)) + 7
+    clipped to [0, 15]; the NaN code S.1111.111 is never drawn (it becomes
+    S.1111.110)."""
     n = int(np.prod(shape, dtype=np.int64))
     rng = _stream(*key)
     out = np.empty(n, dtype=np.uint8)
     for lo in range(0, n, _CHUNK):
         hi = min(n, lo + _CHUNK)
-        v = np.abs(rng.standard_normal(hi - lo)) * 64.0
-        ex = np.clip(np.floor(np.log2(np.maximum(v, 1e-30))) + 7, 0, 15).astype(np.int64)
-        m = rng.integers(0, 8, hi - lo)
-        m = np.where((ex == 15) & (m == 7), 6, m)
-        sg = rng.integers(0, 2, hi - lo)
-        out[lo:hi] = (sg << 7 | ex << 3 | m).astype(np.uint8)
+        v = np.abs(rng.standard_normal(hi - lo, dtype=np.float32)) * np.float32(64.0)
+        _, e = np.frexp(v)                        # v = f 2^e, f in [0.5, 1): floor(log2 v) = e - 1
+        ex = np.clip(e + 6, 0, 15).astype(np.uint8)
+        c = (rng.integers(0, 256, hi - lo, dtype=np.uint8) & np.uint8(0x87)) | (ex << np.uint8(3))
+        c[(c & np.uint8(0x7F)) == np.uint8(0x7F)] -= np.uint8(1)
+        out[lo:hi] = c
     return out.reshape(tuple(shape))
 
 
