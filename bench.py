@@ -33,10 +33,11 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0        # MI355X published dense bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5000.0         # MI355X published dense fp8 matrix-core peak
 KERNEL_SRC = os.path.join(ROOT, "moe_grouped_gemm_bf16_amd", "csrc", "mgemm_kernels.hip")
 KERNEL_NAMES = {"fwd": "grouped_gemm_kernel<0>", "dgrad": "grouped_gemm_kernel<1>",
                 "wgrad": "grouped_gemm_kernel<2>", "fwd_swiglu": "grouped_gemm_kernel<3>",
-                "list": "grouped_gemm_kernel<4>"}
+                "list": "grouped_gemm_kernel<4>", "fwd_mx": "grouped_gemm_kernel<5>"}
 
 
 def kernel_hash() -> str:
@@ -64,6 +65,9 @@ def parse_args():
     p.add_argument("--fusions", action="store_true",
                    help="also time the gate-up forward with gathered rows and fused SwiGLU "
                         "against the unfused sequence (reported only)")
+    p.add_argument("--mx", action="store_true",
+                   help="also time the MXFP8 grouped forward against the bf16 one on the same "
+                        "shapes (reported only)")
     return p.parse_args()
 
 
@@ -298,6 +302,63 @@ def lists(torch, mg, reps=20):
     return out
 
 
+# ----------------------------------------------------------------------- mx --
+
+def mx(torch, mg, reps=20):
+    """The MXFP8 grouped forward (E4M3 operands, E8M0 scales per 32 steps) on
+    the uniform g8 shape and the 30B-A3B share's two expert GEMMs, timed
+    interleaved with the bf16 forward of the same shape; plus the blocked
+    scale layout kernel on the gate-up operands.  Reported beside the step
+    only (`value` is the bf16 path)."""
+    import numpy as np
+    from workloads import make_workload
+    from workloads.synth import mx_e4m3_codes, mx_e8m0_codes
+    u8 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    up = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).cuda()
+    wls = [make_workload(2)[0]] + make_workload(4)
+    out = {}
+    for wl in wls:
+        M, N, K, E = wl.M, wl.N, wl.K, wl.E
+        off = torch.from_numpy(wl.offsets).cuda()
+        hint = int(wl.sizes().max())
+        x8 = u8(mx_e4m3_codes((M, K), 8300, wl.cfg, wl.tag, 1))
+        w8 = u8(mx_e4m3_codes((E, N, K), 8300, wl.cfg, wl.tag, 2))
+        xs = u8(mx_e8m0_codes((M, K // 32), 121, 1, 8300, wl.cfg, wl.tag, 3))
+        ws = u8(mx_e8m0_codes((E, N, K // 32), 121, 1, 8300, wl.cfg, wl.tag, 4))
+        bx, bw = mg.mx_scales_blocked(xs), mg.mx_scales_blocked(ws)
+        x, w = up(wl.x_bits()), up(wl.w_bits())
+        y8 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        y = torch.empty_like(y8)
+        fns = (lambda: mg.fwd_mx(x8, bx, w8, bw, off, hint, out=y8),
+               lambda: mg.fwd(x, w, off, hint, out=y),
+               lambda: (mg.mx_scales_blocked(xs, out=bx), mg.mx_scales_blocked(ws, out=bw)))
+        for _ in range(5):
+            for fn in fns:
+                fn()
+        torch.cuda.synchronize()
+        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in fns] for _ in range(reps)]
+        for row in ev:
+            for (a, b), fn in zip(row, fns):
+                a.record()
+                fn()
+                b.record()
+        torch.cuda.synchronize()
+        t = [statistics.median(r[i][0].elapsed_time(r[i][1]) for r in ev) * 1e3
+             for i in range(len(fns))]
+        flops = wl.flops()
+        sc_bytes = 2 * (xs.numel() + ws.numel())          # read plain, write blocked (same size)
+        out[f"fwd_mx:{wl.name}"] = {
+            "mx_us": round(t[0], 1), "tflops": round(flops / t[0] / 1e6, 1),
+            "pct_fp8_peak": round(100 * flops / t[0] / 1e6 / PEAK_FP8_TFLOPS, 1),
+            "bf16_us": round(t[1], 1), "speedup_vs_bf16": round(t[1] / t[0], 3),
+            "scale_layout_us": round(t[2], 1),
+            "scale_layout_GBps": round(sc_bytes / t[2] / 1e3, 1)}
+        del x8, w8, xs, ws, bx, bw, x, w, y8, y
+        torch.cuda.empty_cache()
+    return out
+
+
 # ------------------------------------------------------------- CPU baseline --
 
 def cpu_baseline(workload: str):
@@ -454,6 +515,11 @@ def main():
         print("[bench] timing the descriptor-list call", file=sys.stderr, flush=True)
         listed = lists(torch, mg)
 
+    mxr = None
+    if args.mx:
+        print("[bench] timing the MXFP8 forward", file=sys.stderr, flush=True)
+        mxr = mx(torch, mg)
+
     fused = None
     if args.fusions:
         print("[bench] timing the fused gate-up forward", file=sys.stderr, flush=True)
@@ -498,6 +564,8 @@ def main():
         line["fused_ops"] = fused
     if listed is not None:
         line["list_ops"] = listed
+    if mxr is not None:
+        line["mx_ops"] = mxr
     print(json.dumps(line), flush=True)
 
 

@@ -211,7 +211,8 @@ mg_status mg_mx_scales_blocked(const void* scales, void* blocked, int64_t rows, 
       batch > kMaxRows)
     return MG_ERR_SHAPE;
   const int64_t total = batch * ((K + 127) / 128) * rows;    // output dwords
-  if (total >= (int64_t(1) << 40)) return MG_ERR_SHAPE;
+  if (total >= (int64_t(1) << 40) || batch * ((rows + 63) / 64) >= (int64_t(1) << 31))
+    return MG_ERR_SHAPE;
   if (total == 0) return MG_OK;
   if (!scales || !blocked) return MG_ERR_NULL;
   if (reinterpret_cast<uintptr_t>(blocked) & 3u) return MG_ERR_ALIGN;

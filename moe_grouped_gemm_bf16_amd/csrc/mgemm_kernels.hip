@@ -784,6 +784,36 @@ __device__ __forceinline__ bf16x8 frag_rs(const char* tile, uint32_t off, uint32
   return __builtin_bit_cast(bf16x8, w);
 }
 
+// Scaled fp8 product whose A and B scales are bytes i and j of sa and sb (the
+// byte select is an immediate: i and j are constants once the caller's loops
+// are unrolled, and the switch folds).
+template <int I, int J>
+__device__ __forceinline__ f32x16 mfma_mx_ij(const i32x8& a, const i32x8& b, const f32x16& c,
+                                             uint32_t sa, uint32_t sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, I, (int)sa, J, (int)sb);
+}
+__device__ __forceinline__ f32x16 mfma_mx(int i, int j, const i32x8& a, const i32x8& b,
+                                          const f32x16& c, uint32_t sa, uint32_t sb) {
+  switch (4 * i + j) {
+    case 0: return mfma_mx_ij<0, 0>(a, b, c, sa, sb);
+    case 1: return mfma_mx_ij<0, 1>(a, b, c, sa, sb);
+    case 2: return mfma_mx_ij<0, 2>(a, b, c, sa, sb);
+    case 3: return mfma_mx_ij<0, 3>(a, b, c, sa, sb);
+    case 4: return mfma_mx_ij<1, 0>(a, b, c, sa, sb);
+    case 5: return mfma_mx_ij<1, 1>(a, b, c, sa, sb);
+    case 6: return mfma_mx_ij<1, 2>(a, b, c, sa, sb);
+    case 7: return mfma_mx_ij<1, 3>(a, b, c, sa, sb);
+    case 8: return mfma_mx_ij<2, 0>(a, b, c, sa, sb);
+    case 9: return mfma_mx_ij<2, 1>(a, b, c, sa, sb);
+    case 10: return mfma_mx_ij<2, 2>(a, b, c, sa, sb);
+    case 11: return mfma_mx_ij<2, 3>(a, b, c, sa, sb);
+    case 12: return mfma_mx_ij<3, 0>(a, b, c, sa, sb);
+    case 13: return mfma_mx_ij<3, 1>(a, b, c, sa, sb);
+    case 14: return mfma_mx_ij<3, 2>(a, b, c, sa, sb);
+    default: return mfma_mx_ij<3, 3>(a, b, c, sa, sb);
+  }
+}
+
 // The persistent body of one workgroup: a producer walks the tile list
 // issuing LDS stages (tiles with an empty reduction have none), a consumer
 // walks the same list consuming them and storing each tile's result.  Stage
@@ -1082,11 +1112,15 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
   // row (bytes 64 kk .. 64 kk + 63 = MX blocks 2 kk, 2 kk + 1) is therefore
   // read as chunks 4 kk + h and 4 kk + 2 + h -- the bf16 reads of slices 2 kk
   // and 2 kk + 1 -- and lane l passes the scale byte 2 kk + h of its row.
+  // The scales of a slice are packed one byte per block: byte i of sp is the
+  // scale of P block i, byte j of sq that of Q block j, and the product picks
+  // its byte with the instruction's scale byte select.
   typedef typename std::conditional<MX, i32x8, bf16x8>::type FragT;
   struct Frags {
     FragT p[C::MP], q[C::MQ];
-    uint32_t sp[MX ? C::MP : 1], sq[MX ? C::MQ : 1];
+    uint32_t sp, sq;
   };
+  static_assert(!MX || (C::MP == 4 && C::MQ == 4), "one scale byte per block in a dword");
   auto read = [&](int g, int kk, Frags& f) {
     const char* tp = lds + (g % kStages) * C::STAGE;
     const char* tq = tp + C::P_BYTES;
@@ -1098,16 +1132,25 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
       };
       const char* sc = lds + C::LDS + (g % kStages) * kScStage;
       const int sh = 8 * (2 * kk + h);
+      // chunk 2 kk' + h of a 128-byte row: offP[kk'] = offP[0] ^ (kk' << 5) (the
+      // row base has no low bits and (2 kk' + h) ^ swz = (h ^ swz) ^ 2 kk'), which
+      // keeps one address register per operand instead of four
+      const uint32_t p0 = offP[0] ^ (uint32_t)(64 * kk), p1 = offP[0] ^ (uint32_t)(64 * kk + 32);
+      const uint32_t q0 = offQ[0] ^ (uint32_t)(64 * kk), q1 = offQ[0] ^ (uint32_t)(64 * kk + 32);
+      // byte 0 of each row's scale dword, shifted by 8 (2 kk + h), packed
+      auto pack = [&](const char* rows) {
+        const uint32_t* r = reinterpret_cast<const uint32_t*>(rows);
+        const uint32_t r0 = r[0] >> sh, r1 = r[32] >> sh, r2 = r[64] >> sh, r3 = r[96] >> sh;
+        const uint32_t lo = __builtin_amdgcn_perm(r1, r0, 0x0c0c0400u);
+        const uint32_t hi = __builtin_amdgcn_perm(r3, r2, 0x0c0c0400u);
+        return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+      };
 #pragma unroll
-      for (int i = 0; i < C::MP; ++i) {
-        f.p[i] = frag8(tp, offP[2 * kk] + i * 32 * kRowB, offP[2 * kk + 1] + i * 32 * kRowB);
-        f.sp[i] = *reinterpret_cast<const uint32_t*>(sc + (wp * C::WTP + 32 * i + l32) * 4) >> sh;
-      }
+      for (int i = 0; i < C::MP; ++i) f.p[i] = frag8(tp, p0 + i * 32 * kRowB, p1 + i * 32 * kRowB);
 #pragma unroll
-      for (int j = 0; j < C::MQ; ++j) {
-        f.q[j] = frag8(tq, offQ[2 * kk] + j * 32 * kRowB, offQ[2 * kk + 1] + j * 32 * kRowB);
-        f.sq[j] = *reinterpret_cast<const uint32_t*>(sc + C::BP * 4 + (wq * C::WTQ + 32 * j + l32) * 4) >> sh;
-      }
+      for (int j = 0; j < C::MQ; ++j) f.q[j] = frag8(tq, q0 + j * 32 * kRowB, q1 + j * 32 * kRowB);
+      f.sp = pack(sc + (wp * C::WTP + l32) * 4);
+      f.sq = pack(sc + C::BP * 4 + (wq * C::WTQ + l32) * 4);
       return;
     } else {
 #pragma unroll
@@ -1124,9 +1167,11 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
   auto wait_stage = [&](int g) {
     int n = issued - after[g % kStages];
     n = n < 0 ? 0 : n;
+    // (the counts that occur are exact steps: the loads of the first half of
+    // a stage, 4 (bf16) or 10 (MXFP8: 8 data + 2 scale loads), or a whole one)
     if (n >= 24) wait_vmcnt<24>();
-    else if (n >= 16) { if (n >= 20) wait_vmcnt<20>(); else wait_vmcnt<16>(); }
-    else if (n >= 8) { if (n >= 12) wait_vmcnt<12>(); else wait_vmcnt<8>(); }
+    else if (n >= 16) { if (n >= 20) wait_vmcnt<20>(); else if (n >= 18) wait_vmcnt<18>(); else wait_vmcnt<16>(); }
+    else if (n >= 8) { if (n >= 12) wait_vmcnt<12>(); else if (n >= 10) wait_vmcnt<10>(); else wait_vmcnt<8>(); }
     else if (n >= 4) { if (n >= 6) wait_vmcnt<6>(); else wait_vmcnt<4>(); }
     else if (n >= 2) wait_vmcnt<2>();
     else wait_vmcnt<0>();
@@ -1162,8 +1207,7 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
     for (int x = x0; x < x1; ++x) {
       const int i = x / C::MQ, j = x % C::MQ;
       if constexpr (MX)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            f.p[i], f.q[j], acc[i][j], 0, 0, 0, (int)f.sp[i], 0, (int)f.sq[j]);
+        acc[i][j] = mfma_mx(i, j, f.p[i], f.q[j], acc[i][j], f.sp, f.sq);
       else
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.p[i], f.q[j], acc[i][j], 0, 0, 0);
       // after product x, (x - x0 + 1) (d1 - d0) / (x1 - x0) loads are due
@@ -1639,36 +1683,55 @@ int launch_grouped(int mode, const KernelArgs& a_in, int64_t max_m_per_e, hipStr
   return (int)hipGetLastError();
 }
 
-// Blocked MXFP8 scales: one thread per output dword, the four scales of row r
-// for reduction steps 128 t .. 128 t + 127 (127, the code of 1.0, for
+// Blocked MXFP8 scales: entry [b][t][r] (a dword) holds the four scales of
+// row r for reduction steps 128 t .. 128 t + 127 (127, the code of 1.0, for
 // blocks past K / 32).  The torchao PR #3416 rearranges e8m0 scales into the
 // layout its grouped GEMM reads with a kernel of its own; this is that step
-// for the layout the MXFP8 forward above stages per LDS stage.
+// for the layout the MXFP8 forward above stages per LDS stage.  A workgroup
+// moves a tile of 64 rows x 16 dwords through LDS, so that it reads each
+// row's bytes contiguously and writes each output row of dwords contiguously.
+constexpr int kScTileR = 64, kScTileT = 16;
 __global__ __launch_bounds__(256) void mx_scales_blocked_kernel(const uint8_t* __restrict__ src,
                                                                  uint32_t* __restrict__ dst,
                                                                  int64_t rows, int64_t nb,
-                                                                 int64_t nt, int64_t total) {
-  const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (o >= total) return;
-  const int64_t r = o % rows, bt = o / rows, t = bt % nt, b = bt / nt;
-  const uint8_t* row = src + (b * rows + r) * nb;
-  uint32_t v = 0;
+                                                                 int64_t nt, int64_t rblocks) {
+  __shared__ uint32_t tile[kScTileR][kScTileT + 1];
+  const int tid = threadIdx.x;
+  const int64_t b = blockIdx.x / rblocks;
+  const int64_t r0 = (blockIdx.x % rblocks) * kScTileR, t0 = (int64_t)blockIdx.y * kScTileT;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t blk = 4 * t + j;
-    v |= (uint32_t)(blk < nb ? row[blk] : 127u) << (8 * j);
+  for (int i = 0; i < 4; ++i) {
+    const int row = tid / kScTileT + 16 * i, tq = tid % kScTileT;
+    const int64_t r = r0 + row, t = t0 + tq;
+    uint32_t v = 0;
+    if (r < rows && t < nt) {
+      const uint8_t* p = src + (b * rows + r) * nb;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t blk = 4 * t + j;
+        v |= (uint32_t)(blk < nb ? p[blk] : 127u) << (8 * j);
+      }
+    }
+    tile[row][tq] = v;
   }
-  dst[o] = v;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tq = tid / kScTileR + 4 * i, row = tid % kScTileR;
+    const int64_t r = r0 + row, t = t0 + tq;
+    if (r < rows && t < nt) dst[(b * nt + t) * rows + r] = tile[row][tq];
+  }
 }
 
 int launch_mx_scales_blocked(const uint8_t* src, uint8_t* dst, int64_t rows, int64_t K,
                              int64_t batch, hipStream_t s) {
   const int64_t nb = K / 32, nt = (K + 127) / 128;
-  const int64_t total = batch * nt * rows;
-  if (total <= 0) return 0;
-  const int64_t blocks = (total + 255) / 256;
-  hipLaunchKernelGGL(mx_scales_blocked_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src,
-                     reinterpret_cast<uint32_t*>(dst), rows, nb, nt, total);
+  if (batch <= 0 || rows <= 0 || nt <= 0) return 0;
+  const int64_t rblocks = (rows + kScTileR - 1) / kScTileR;
+  const int64_t gx = batch * rblocks, gy = (nt + kScTileT - 1) / kScTileT;
+  if (gx >= (int64_t(1) << 31) || gy > 65535) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(mx_scales_blocked_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s,
+                     src, reinterpret_cast<uint32_t*>(dst), rows, nb, nt, rblocks);
   return (int)hipGetLastError();
 }
 
