@@ -97,6 +97,32 @@ def test_wgrad_argument_errors():
     assert f(None, None, None, None, 0, 0, 256, 4, 0, None) == OK       # empty dw
 
 
+def test_mx_argument_errors():
+    f = L.mgemm_fwd_mx
+    # (x, x_scale, w, w_scale, offsets, y, M, N, K, E, max_m_per_e, stream)
+    assert f(A, A, A, A, A, A, 512, 128, 256, 0, 0, None) == SHAPE        # E < 1
+    assert f(A, A, A, A, A, A, 512, 128, 48, 4, 0, None) == SHAPE         # K % 32
+    assert f(A, A, A, A, A, A, 512, 100, 256, 4, 0, None) == SHAPE        # N % 8
+    assert f(A, A, A, A, A, A, 512, 128, 256, 4, -1, None) == SHAPE       # bad hint
+    assert f(A, A, A, A, A, A, 1 << 30, 128, 4096, 4, 0, None) == SHAPE   # scale offsets > 2^31
+    assert f(None, A, A, A, A, A, 512, 128, 256, 4, 0, None) == NUL
+    assert f(A, None, A, A, A, A, 512, 128, 256, 4, 0, None) == NUL
+    assert f(A, A, A, None, A, A, 512, 128, 256, 4, 0, None) == NUL
+    assert f(A, A, A, A, None, A, 512, 128, 256, 4, 0, None) == NUL
+    assert f(A + 8, A, A, A, A, A, 512, 128, 256, 4, 0, None) == ALIGN
+    assert f(A, A + 2, A, A, A, A, 512, 128, 256, 4, 0, None) == ALIGN     # scales 4-byte aligned
+    assert f(A, A + 4, A, A, A, A + 8, 512, 128, 256, 4, 0, None) == ALIGN  # y 16-byte aligned
+    assert f(None, None, None, None, None, None, 0, 128, 256, 4, 0, None) == OK
+    g = L.mg_mx_scales_blocked
+    # (scales, blocked, rows, K, batch, stream)
+    assert g(A, A, 10, 48, 1, None) == SHAPE                             # K % 32
+    assert g(A, A, -1, 64, 1, None) == SHAPE
+    assert g(A, A, 10, 64, -1, None) == SHAPE
+    assert g(None, A, 10, 64, 1, None) == NUL
+    assert g(A, A + 2, 10, 64, 1, None) == ALIGN
+    assert g(None, None, 0, 64, 1, None) == OK                           # nothing to convert
+
+
 def test_python_binding_rejects_bad_tensors_on_host():
     torch = pytest.importorskip("torch")
     import moe_grouped_gemm_bf16_amd as mg
