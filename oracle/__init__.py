@@ -27,8 +27,10 @@ per expert; nothing blocked, fused or reordered):
   * MXFP8 M-grouped forward (torchao PR #3416: MXFP8 MoE grouped GEMMs with
     e8m0 block scales in a blocked layout; DeepGEMM issue #10: operands
     quantized along each GEMM's reduction axis): E4M3 elements, one E8M0
-    scale per 32 reduction steps, decoded exactly and summed in fp64; and the
-    blocked scale layout [ceil(K/128)][rows][4] the GEMM call reads.
+    scale per 32 reduction steps, decoded exactly and summed in fp64; the
+    MXFP8 K-grouped weight gradient on token-major-last (transposed) operands
+    quantized along the tokens; and the blocked scale layout
+    [ceil(K/128)][rows][4] the GEMM calls read.
   * bf16 outputs are the fp64 result rounded once, directly, to bf16 with
     round-to-nearest-even.
 
@@ -43,8 +45,10 @@ groups of mixed shapes (empty and zero-reduction ones included), a one-hot
 transpose check and the flattened LoRA x experts identity; for MXFP8, the
 element and scale decoders against torch's float8_e4m3fn / float8_e8m0fnu
 casts on every code, closed forms, exact rational brute force on tiny inputs,
-power-of-two scale shifts that move whole rows or experts exactly, and the
-blocked layout against an index-by-index brute force.  Every function here
+power-of-two scale shifts that move whole rows or experts exactly, the
+blocked layout against an index-by-index brute force, and for the MXFP8
+weight gradient exact rational brute force, the unit-scale reduction to the
+plain K-grouped wgrad and the adjoint identity with the MXFP8 forward.  Every function here
 is pinned; none is "parity
 unpinned".
 """
@@ -66,6 +70,9 @@ from .mx import (  # noqa: F401
     mx_dequant,
     grouped_fwd_mx,
     sample_fwd_mx,
+    grouped_wgrad_mx,
+    sample_wgrad_mx,
     mx_scales_blocked,
 )
-from .gate import check_bf16, check_bf16_swiglu, check_bf16_mx, check_fp32, GateReport  # noqa: F401
+from .gate import (check_bf16, check_bf16_swiglu, check_bf16_mx, check_fp32,  # noqa: F401
+                   check_fp32_mx, GateReport)

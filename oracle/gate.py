@@ -42,6 +42,11 @@ data) and K = 2048, some 20 times this floor.  A block far smaller than the
 largest ones of its sum is below it, as it is below the matrix cores' own
 precision.
 
+fp32 outputs of the MXFP8 weight gradient.  The same matrix-core precision
+floor, applied per element: |g - exact| <= 2^-12 S + 2^-24 (8 + 2 sqrt(K_red)) S;
+no Frobenius bound (a floor of 2^-12 of S is far above 1e-4 of the result's
+norm when K_red is large); empty experts exactly zero (or the prior).
+
 fp32 outputs (wgrad).  Relative Frobenius error <= 1e-4, over the whole
 tensor and per expert (a large expert would otherwise hide a wrong small
 one); an empty expert's block must be exactly zero (or exactly the prior
@@ -130,6 +135,27 @@ def check_bf16_mx(got_bits: np.ndarray, exact: np.ndarray, abs_sum: np.ndarray) 
         i = int(np.argmax(np.where(ok, -np.inf, np.abs(g - exact))))
         worst = f"worst@{i}: got={g.flat[i]!r} exact={exact.flat[i]!r}"
     return GateReport(int(g.size), fails == 0, fails, int((~strict).sum()), 0.0, worst)
+
+
+def check_fp32_mx(got: np.ndarray, exact: np.ndarray, abs_sum: np.ndarray, k_red,
+                  empty_mask=None, empty_expect=None) -> GateReport:
+    """Gate for the fp32 output of the MXFP8 weight gradient (see the header)."""
+    got = np.asarray(got, np.float64)
+    exact = np.asarray(exact, np.float64)
+    bound = (MX_FLOOR + U32 * (8.0 + 2.0 * np.sqrt(k_red))) * abs_sum
+    ok = (np.abs(got - exact) <= bound) & np.isfinite(got)
+    fails = int((~ok).sum())
+    worst = ""
+    if fails:
+        i = int(np.argmax(np.where(ok, -np.inf, np.abs(got - exact))))
+        worst = f"worst@{i}: got={got.flat[i]!r} exact={exact.flat[i]!r}"
+    passed = fails == 0
+    if empty_mask is not None:
+        exp = 0.0 if empty_expect is None else empty_expect
+        bad = int((got[empty_mask] != np.broadcast_to(exp, got.shape)[empty_mask]).sum())
+        fails += bad
+        passed = passed and bad == 0
+    return GateReport(int(got.size), passed, fails, 0, rel_frob(got, exact), worst)
 
 
 def rel_frob(got: np.ndarray, exact: np.ndarray) -> float:

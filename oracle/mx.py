@@ -1,4 +1,5 @@
-"""fp64 oracle of the MXFP8 M-grouped forward (test infrastructure only).
+"""fp64 oracle of the MXFP8 M-grouped forward and K-grouped weight gradient
+(test infrastructure only).
 
 The torchao PR #3416 ("[mxfp8 moe training] ... scale blocked format kernel
 for groups along K", its "Changes" list) trains MoE layers with MXFP8 grouped
@@ -126,3 +127,48 @@ def mx_scales_blocked(scales) -> np.ndarray:
 def blocked_bytes(rows: int, K: int) -> int:
     """Bytes of one blocked scale matrix of `rows` rows and reduction K."""
     return math.ceil(K / MX_STAGE) * rows * 4
+
+
+def grouped_wgrad_mx(dyt8, dyts, xt8, xts, offsets, E: int, prior=None) -> np.ndarray:
+    """MXFP8 K-grouped weight gradient (fp64, [E, N, K]).
+
+    The torchao PR #3416 names this case -- groups along K, the token axis of
+    the weight gradient -- and the DeepGEMM issue #10 thread the reason its
+    operands are quantized along the tokens: each GEMM's operands are blocked
+    along that GEMM's reduction axis.  So the operands come transposed, token
+    axis last:
+      dyt8 uint8 [N, M], dyts uint8 [N, M/32]   (dY^T and its scales),
+      xt8  uint8 [K, M], xts  uint8 [K, M/32]   (X^T and its scales),
+    and for the rows offsets[e] <= i < offsets[e+1] of expert e
+      dW[e, n, k] = sum_i DYT[n, i] XT[k, i]      (dequantized values),
+    plus `prior` when given; an expert with no rows gives zeros (or prior)."""
+    dyt = mx_dequant(dyt8, dyts)
+    xt = mx_dequant(xt8, xts)
+    N, M = dyt.shape
+    K, M2 = xt.shape
+    assert M == M2
+    o = _check_offsets(offsets, E, M)
+    dw = np.zeros((E, N, K))
+    for e in range(E):
+        lo, hi = o[e], o[e + 1]
+        if hi > lo:
+            dw[e] = dyt[:, lo:hi] @ xt[:, lo:hi].T
+    if prior is not None:
+        dw = dw + prior
+    return dw
+
+
+def sample_wgrad_mx(dyt8, dyts, xt8, xts, offsets, experts, ns, ks):
+    """dW[experts[j], ns[j], ks[j]] of grouped_wgrad_mx one element at a time,
+    fp64, with sum |products|; an empty expert gives exactly (0, 0)."""
+    o = np.asarray(offsets, dtype=np.int64)
+    val = np.zeros(len(experts)); mag = np.zeros(len(experts))
+    for j, (e, n, k) in enumerate(zip(experts, ns, ks)):
+        lo, hi = o[e], o[e + 1]
+        if hi <= lo:
+            continue
+        a = mx_dequant(np.asarray(dyt8)[n:n + 1], np.asarray(dyts)[n:n + 1])[0, lo:hi]
+        b = mx_dequant(np.asarray(xt8)[k:k + 1], np.asarray(xts)[k:k + 1])[0, lo:hi]
+        p = a * b
+        val[j] = p.sum(); mag[j] = np.abs(p).sum()
+    return val, mag

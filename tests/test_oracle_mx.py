@@ -203,3 +203,96 @@ def test_mx_gate_accepts_rounding_and_rejects_block_mistakes():
     ws_t = ws[:, :, ::-1].copy()
     bad = oracle.f64_to_bf16_bits(omx.grouped_fwd_mx(x8, xs, w8, ws_t, offs))
     assert oracle.check_bf16_mx(bad, y, S).fails > 0.9 * y.size
+
+
+# ------------------------------------------------------------ MXFP8 wgrad --
+
+def _wgrad_inputs(N, K, sizes, spread, seed, center=121):
+    offs = synth.offsets_from_sizes(sizes)
+    M = int(offs[-1])
+    dyt8 = synth.mx_e4m3_codes((N, M), 130, seed)
+    xt8 = synth.mx_e4m3_codes((K, M), 131, seed)
+    dyts = synth.mx_e8m0_codes((N, M // 32), center, spread, 132, seed)
+    xts = synth.mx_e8m0_codes((K, M // 32), center, spread, 133, seed)
+    return offs, M, dyt8, dyts, xt8, xts
+
+
+def test_wgrad_mx_brute_force_exact():
+    N, K = 3, 2
+    offs, M, dyt8, dyts, xt8, xts = _wgrad_inputs(N, K, [32, 0, 64], 4, 0)
+    E = 3
+    dw = omx.grouped_wgrad_mx(dyt8, dyts, xt8, xts, offs, E)
+    dv, xv = _torch_e4m3(dyt8), _torch_e4m3(xt8)
+    for e in range(E):
+        for n in range(N):
+            for k in range(K):
+                acc = Fraction(0)
+                for i in range(offs[e], offs[e + 1]):
+                    acc += (Fraction(dv[n, i]) * Fraction(2) ** (int(dyts[n, i // 32]) - 127) *
+                            Fraction(xv[k, i]) * Fraction(2) ** (int(xts[k, i // 32]) - 127))
+                assert dw[e, n, k] == float(acc)
+    assert (dw[1] == 0).all()
+    prior = np.arange(E * N * K, dtype=np.float64).reshape(E, N, K)
+    np.testing.assert_array_equal(omx.grouped_wgrad_mx(dyt8, dyts, xt8, xts, offs, E, prior),
+                                  dw + prior)
+
+
+def test_wgrad_mx_unit_scales_is_plain_wgrad_and_adjoint_of_fwd():
+    N, K = 16, 24
+    offs, M, dyt8, dyts, xt8, xts = _wgrad_inputs(N, K, [64, 0, 96, 32], 0, 1, center=127)
+    E = 4
+    dw = omx.grouped_wgrad_mx(dyt8, dyts, xt8, xts, offs, E)
+    dy = _torch_e4m3(dyt8).T.copy(); x = _torch_e4m3(xt8).T.copy()
+    np.testing.assert_array_equal(dw, oracle.grouped_wgrad(dy, x, offs, E))
+    # with scales: sum_e <dW_e, W_e> = <dY, Y(X, W)> for any W (the forward's adjoint)
+    offs, M, dyt8, dyts, xt8, xts = _wgrad_inputs(N, K, [64, 0, 96, 32], 3, 2)
+    dw = omx.grouped_wgrad_mx(dyt8, dyts, xt8, xts, offs, E)
+    dy = omx.mx_dequant(dyt8, dyts).T; x = omx.mx_dequant(xt8, xts).T
+    w = np.random.default_rng(3).standard_normal((E, N, K))
+    lhs = float((dw * w).sum())
+    rhs = float((dy * oracle.grouped_fwd(x, w, offs)).sum())
+    assert abs(lhs - rhs) <= 1e-12 * (np.abs(dw).sum() * np.abs(w).max())
+
+
+def test_wgrad_mx_scale_shifts():
+    N, K = 8, 12
+    offs, M, dyt8, dyts, xt8, xts = _wgrad_inputs(N, K, [64, 96], 3, 4)
+    E = 2
+    dw = omx.grouped_wgrad_mx(dyt8, dyts, xt8, xts, offs, E)
+    # all scales of X^T row 5 up by 2: column k = 5 of every expert times 4
+    xts2 = xts.copy(); xts2[5] += 2
+    dw2 = omx.grouped_wgrad_mx(dyt8, dyts, xt8, xts2, offs, E)
+    np.testing.assert_array_equal(dw2[:, :, 5], 4.0 * dw[:, :, 5])
+    np.testing.assert_array_equal(np.delete(dw2, 5, 2), np.delete(dw, 5, 2))
+    # token block 3 (rows 96..127, expert 1) of every dY^T row down by 1: expert 0 unchanged
+    dyts2 = dyts.copy(); dyts2[:, 3] -= 1
+    dw3 = omx.grouped_wgrad_mx(dyt8, dyts2, xt8, xts, offs, E)
+    np.testing.assert_array_equal(dw3[0], dw[0])
+    only = np.zeros_like(dyt8); only[:, 96:128] = dyt8[:, 96:128]
+    part = omx.grouped_wgrad_mx(only, dyts, xt8, xts, offs, E)
+    np.testing.assert_allclose(dw[1] - dw3[1], 0.5 * part[1], rtol=1e-13, atol=0)
+
+
+def test_sample_wgrad_mx_and_gate():
+    N, K = 32, 40
+    offs, M, dyt8, dyts, xt8, xts = _wgrad_inputs(N, K, [128, 0, 256], 1, 5)
+    E = 3
+    dw = omx.grouped_wgrad_mx(dyt8, dyts, xt8, xts, offs, E)
+    es, ns, ks = np.array([0, 1, 2, 2]), np.array([0, 3, 31, 7]), np.array([39, 1, 0, 20])
+    v, s = omx.sample_wgrad_mx(dyt8, dyts, xt8, xts, offs, es, ns, ks)
+    np.testing.assert_array_equal(v, dw[es, ns, ks])
+    assert s[1] == 0 and v[1] == 0
+    mag = omx.grouped_wgrad_mx(dyt8, dyts, xt8, xts, offs, E) * 0
+    dyv, xv = omx.mx_dequant(dyt8, dyts), omx.mx_dequant(xt8, xts)
+    for e in range(E):
+        lo, hi = offs[e], offs[e + 1]
+        mag[e] = np.abs(dyv[:, lo:hi]) @ np.abs(xv[:, lo:hi]).T
+    k_red = np.maximum(np.diff(offs), 1)[:, None, None]
+    empty = np.broadcast_to((np.diff(offs) == 0)[:, None, None], dw.shape)
+    assert oracle.check_fp32_mx(dw.astype(np.float32), dw, mag, k_red, empty_mask=empty).passed
+    # a dropped 32-token block of expert 2 and a wrong expert fail
+    d2 = dyt8.copy(); d2[:, 160:192] = 0
+    bad = omx.grouped_wgrad_mx(d2, dyts, xt8, xts, offs, E)
+    assert oracle.check_fp32_mx(bad, dw, mag, k_red, empty_mask=empty).fails > 0.8 * dw[2].size
+    swapped = dw[[2, 1, 0]]
+    assert not oracle.check_fp32_mx(swapped, dw, mag, k_red, empty_mask=empty).passed
