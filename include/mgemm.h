@@ -160,6 +160,28 @@ mg_status mgemm_fwd_mx(const void* x, const void* x_scale, const void* w, const 
                        const int32_t* offsets, void* y, int64_t M, int64_t N, int64_t K, int32_t E,
                        int64_t max_m_per_e, void* stream);
 
+/* MXFP8 K-grouped weight gradient in FP32 (torchao PR #3416: MXFP8 grouped
+ * GEMMs with groups along K, the token axis of the weight gradient; DeepGEMM
+ * issue #10: its operands are quantized along the tokens, and FP8 wgrad needs
+ * token counts that are multiples of 128):
+ *   dw[e, n, k] (= or +=) sum_{offsets[e] <= i < offsets[e+1]} DYT[n, i] XT[k, i]
+ * with DYT, XT the dequantized E4M3 codes times their E8M0 block scales.
+ * dyt: uint8 E4M3 [N, M] (dY transposed, token axis last); xt: uint8 E4M3 [K, M];
+ * dyt_scale: blocked [M/128][N][4] (entry [t][n][j] scales dyt[n, 128 t + 32 j
+ * .. + 31]); xt_scale: blocked [M/128][K][4]; dw: fp32 [E, N, K].
+ * M a multiple of 128, and every offsets[e] a multiple of 128 (experts padded
+ * to whole 128-token stages; checked only under MGEMM_VALIDATE=1 -- otherwise
+ * other offsets give wrong sums, never out-of-bounds accesses); N and K
+ * multiples of 8; 256 M < 2^32; M/128 N and M/128 K below 2^29.  Pointers:
+ * dyt, xt, dw 16-byte aligned, scales 4-byte aligned.  accumulate as for
+ * kgemm_wgrad; an expert with no rows gets zeros (or is left as it was).  The
+ * products are the scaled fp8 matrix-core products (about 2^-13 of the sum of
+ * the absolute terms per 64 tokens), accumulated in fp32.  N == 0 or K == 0 is
+ * a no-op.  Allocates nothing, and never splits a tile's token range. */
+mg_status kgemm_wgrad_mx(const void* dyt, const void* dyt_scale, const void* xt,
+                         const void* xt_scale, const int32_t* offsets, float* dw, int64_t M,
+                         int64_t N, int64_t K, int32_t E, int32_t accumulate, void* stream);
+
 /* Blocked layout of MXFP8 scales (the torchao PR #3416 "scale blocked format"
  * step, for the layout above): scales: uint8 [batch][rows][K/32] (DEVICE);
  * blocked: uint8 [batch][ceil(K/128)][rows][4] (DEVICE, 4-byte aligned,

@@ -290,6 +290,44 @@ def fwd_mx(x8: torch.Tensor, x_scale: torch.Tensor, w8: torch.Tensor, w_scale: t
     return out
 
 
+def wgrad_mx(dyt8: torch.Tensor, dyt_scale: torch.Tensor, xt8: torch.Tensor,
+             xt_scale: torch.Tensor, offsets: torch.Tensor, E: int | None = None,
+             out: torch.Tensor | None = None, accumulate: bool = False) -> torch.Tensor:
+    """MXFP8 K-grouped weight gradient: out[e] (=/+=) DYT[:, rows_e] @ XT[:, rows_e].T.
+
+    dyt8 [N, M], xt8 [K, M]: uint8 E4M3 codes quantized along the tokens (token
+    axis last); dyt_scale [M/128, N, 4], xt_scale [M/128, K, 4]: blocked E8M0
+    scales (mx_scales_blocked of [N, M/32] and [K, M/32]).  offsets int32 [E+1]
+    with every entry a multiple of 128.  out fp32 [E, N, K]."""
+    _need(dyt8, "dyt8", torch.uint8, 2)
+    _need(xt8, "xt8", torch.uint8, 2)
+    N, M = dyt8.shape
+    K, M2 = xt8.shape
+    if M2 != M:
+        raise ValueError(f"dyt8 is [N, {M}] but xt8 is [K, {M2}]")
+    if E is None:
+        E = offsets.numel() - 1
+    _need(dyt_scale, "dyt_scale", torch.uint8, 3)
+    _need(xt_scale, "xt_scale", torch.uint8, 3)
+    if tuple(dyt_scale.shape) != (M // 128, N, 4) or tuple(xt_scale.shape) != (M // 128, K, 4):
+        raise ValueError(f"blocked scales must be [{M // 128}, {N}, 4] and [{M // 128}, {K}, 4]")
+    _offsets(offsets, E, dyt8.device)
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs an `out` to add into")
+        out = torch.empty((E, N, K), dtype=torch.float32, device=dyt8.device)
+    else:
+        _need(out, "out", torch.float32, 3)
+        if tuple(out.shape) != (E, N, K):
+            raise ValueError(f"out must be [{E}, {N}, {K}]")
+    with torch.cuda.device(dyt8.device):
+        st = LIB.kgemm_wgrad_mx(dyt8.data_ptr(), dyt_scale.data_ptr(), xt8.data_ptr(),
+                                xt_scale.data_ptr(), offsets.data_ptr(), out.data_ptr(),
+                                M, N, K, E, 1 if accumulate else 0, _stream(dyt8))
+    check(st, "kgemm_wgrad_mx")
+    return out
+
+
 def Mgemm(x: torch.Tensor, w: torch.Tensor, cnt: torch.Tensor, max_M_per_E: int = 0,
           transpose_B: bool = True) -> torch.Tensor:
     """RapidGEMM-shaped M-grouped GEMM (README, "Kernels").

@@ -50,7 +50,8 @@ mg_status check_sizes(int64_t M, int64_t N, int64_t K, int32_t E) {
 
 // Optional debug validation of the device offsets (MGEMM_VALIDATE=1): copies
 // them to the host on the caller's stream and synchronises it.
-mg_status maybe_validate(const int32_t* offsets, int32_t E, int64_t M, hipStream_t s) {
+mg_status maybe_validate(const int32_t* offsets, int32_t E, int64_t M, hipStream_t s,
+                         int32_t multiple = 1) {
   static const bool on = [] {
     const char* v = std::getenv("MGEMM_VALIDATE");
     return v != nullptr && v[0] == '1';
@@ -61,7 +62,11 @@ mg_status maybe_validate(const int32_t* offsets, int32_t E, int64_t M, hipStream
           hipSuccess ||
       hipStreamSynchronize(s) != hipSuccess)
     return MG_ERR_DEVICE;
-  return mg_check_offsets_host(h.data(), E, M);
+  mg_status st = mg_check_offsets_host(h.data(), E, M);
+  if (st != MG_OK) return st;
+  for (int32_t e = 0; e <= E; ++e)
+    if (h[static_cast<size_t>(e)] % multiple != 0) return MG_ERR_OFFSETS;
+  return MG_OK;
 }
 
 static_assert(sizeof(mg_gemm_desc) == sizeof(mg::ListDesc) &&
@@ -203,6 +208,39 @@ mg_status mgemm_fwd_mx(const void* x, const void* x_scale, const void* w, const 
   a.out = y;
   a.M = M; a.N = N; a.K = K; a.E = E;
   return launch(mg::kFwdMx, a, max_m_per_e, s);
+}
+
+mg_status kgemm_wgrad_mx(const void* dyt, const void* dyt_scale, const void* xt,
+                         const void* xt_scale, const int32_t* offsets, float* dw, int64_t M,
+                         int64_t N, int64_t K, int32_t E, int32_t accumulate, void* stream) {
+  mg_status st = check_sizes(M, N, K, E);
+  if (st != MG_OK) return st;
+  // tokens in 128-step stages; 32-bit buffer offsets over a 256-row tile of
+  // M-byte rows and over the blocked scales
+  constexpr int64_t k2G = int64_t(1) << 31;
+  const int64_t ks = M / 128;
+  if ((M & 127) || 256 * M >= 2 * k2G || ks * N * 4 >= k2G || ks * K * 4 >= k2G)
+    return MG_ERR_SHAPE;
+  if (N == 0 || K == 0) return MG_OK;
+  if (!offsets || !dw || (M > 0 && (!dyt || !xt || !dyt_scale || !xt_scale))) return MG_ERR_NULL;
+  if ((M > 0 && (!aligned16(dyt) || !aligned16(xt) ||
+                 (reinterpret_cast<uintptr_t>(dyt_scale) & 3u) ||
+                 (reinterpret_cast<uintptr_t>(xt_scale) & 3u))) ||
+      !aligned16(dw) || (reinterpret_cast<uintptr_t>(offsets) & 3u))
+    return MG_ERR_ALIGN;
+  if ((st = check_device()) != MG_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = maybe_validate(offsets, E, M, s, 128)) != MG_OK) return st;
+  mg::KernelArgs a{};
+  a.p_src = xt;
+  a.q_src = dyt;
+  a.p_scale = static_cast<const uint8_t*>(xt_scale);
+  a.q_scale = static_cast<const uint8_t*>(dyt_scale);
+  a.offsets = offsets;
+  a.out = dw;
+  a.M = M; a.N = N; a.K = K; a.E = E;
+  a.accumulate = accumulate ? 1 : 0;
+  return launch(mg::kWgradMx, a, 0, s);
 }
 
 mg_status mg_mx_scales_blocked(const void* scales, void* blocked, int64_t rows, int64_t K,

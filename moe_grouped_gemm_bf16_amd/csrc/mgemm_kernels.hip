@@ -21,6 +21,9 @@
 //   FWD_MX   as FWD, with E4M3 operands and one E8M0 scale per 32 k (MXFP8;
 //            torchao PR #3416): the same 128-byte staged rows hold 128 k, and
 //            the scaled fp8 matrix-core product applies the scales
+//   WGRAD_MX K-grouped like WGRAD, on E4M3 operands quantized along the
+//            tokens and stored token axis last: P = k from X^T [k][i],
+//            Q = n from dY^T [n][i], R = i (both R-contiguous, as FWD_MX)
 //
 // Operand staging: HBM -> LDS by direct-to-LDS buffer loads (no registers),
 // in LDS stages of kBK reduction steps, the next stage in flight while one is
@@ -697,6 +700,8 @@ __device__ __forceinline__ void decode_kgrouped(int r, int k, int u_in_chunk, co
 template <int MODE, int BP, int BQ>
 struct TileSeq {
   int x, c, nx, count, lo, j, ie;
+  static constexpr bool KG = MODE == kWgrad || MODE == kWgradMx;   // K-grouped
+  static constexpr int SBK = MODE == kWgradMx ? 128 : kBK;         // reduction steps per stage
 
   __device__ __forceinline__ void init(const Sched& S) {
     x = blockIdx.x & 7;
@@ -704,7 +709,7 @@ struct TileSeq {
     nx = gridDim.x >> 3;
     j = 0;
     ie = 0;
-    if (MODE != kWgrad) {
+    if (!KG) {
       if (MODE == kList) {              // cost-balanced ranges from the set-up
         lo = S.keys[x];
         count = S.keys[x + 1] - lo;
@@ -719,7 +724,7 @@ struct TileSeq {
   // Next tile of this workgroup; false once the list is exhausted.
   __device__ __forceinline__ bool next(const Sched& S, Tile& t) {
     t.split = -1;
-    if (MODE == kWgrad) {
+    if (KG) {
       if (ie >= S.nmine) return false;
       // entry: rank (bits 0-9), rho (16-21), first split-tile index (22-26), split (27)
       const int rr = S.mine[2 * ie], cnt = S.mine[2 * ie + 1];
@@ -730,8 +735,8 @@ struct TileSeq {
       decode_kgrouped<BP, BQ>(r, (x - r) & 7, u, S, t);
       if (sp) {
         // halves of the token range, split at a stage boundary
-        const int st = (t.r_end - t.r_begin + kBK - 1) / kBK;
-        const int mid = t.r_begin + ((st + 1) / 2) * kBK;
+        const int st = (t.r_end - t.r_begin + SBK - 1) / SBK;
+        const int mid = t.r_begin + ((st + 1) / 2) * SBK;
         if (v & 1) t.r_begin = mid;
         else t.r_end = mid;
         t.split = ((x * kSplitPerXcd + sbase + u) << 1) | (v & 1);
@@ -823,7 +828,8 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
                                           int Pdim, int Qdim) {
   constexpr bool SWI = MODE == kFwdSwiglu;
   constexpr bool LIST = MODE == kList;
-  constexpr bool MX = MODE == kFwdMx;
+  constexpr bool MX = MODE == kFwdMx || MODE == kWgradMx;
+  constexpr bool KG = MODE == kWgrad || MODE == kWgradMx;   // K-grouped, fp32 out
   constexpr bool P_RS = MODE == kDgrad || MODE == kWgrad;   // P is R-strided for dgrad and wgrad
   constexpr bool Q_RS = MODE == kWgrad;    // Q is R-strided for wgrad
   constexpr int SPW = C::SEGS_PER_WAVE;
@@ -834,7 +840,8 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
 
   int ldP, ldQ;
-  if (MODE == kFwd || SWI || LIST || MX) { ldP = (int)a.K; ldQ = (int)a.K; }   // LIST: per tile
+  if (MODE == kWgradMx) { ldP = (int)a.M; ldQ = (int)a.M; }   // X^T, dY^T rows of M tokens
+  else if (MODE == kFwd || SWI || LIST || MX) { ldP = (int)a.K; ldQ = (int)a.K; }   // LIST: per tile
   else if (MODE == kDgrad) { ldP = (int)a.K; ldQ = (int)a.N; }
   else { ldP = (int)a.K; ldQ = (int)a.N; }
 
@@ -894,7 +901,7 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
   // 8 the swizzled chunk of that row is (lane % 8) ^ (lane / 8) ^ (d % 4).
   static_assert(!MX || (SPW % 8 == 0 && kRowChunks == 8), "MXFP8 load plan");
   const int mx_c0 = (lane & 7) ^ (lane >> 3);
-  const uint32_t mx_rowoff = (uint32_t)(seg0 * 8 + (lane >> 3)) * (uint32_t)a.K;
+  const uint32_t mx_rowoff = (uint32_t)(seg0 * 8 + (lane >> 3)) * (uint32_t)ld;
   const uint32_t sc_base = lds_u32(lds) + (uint32_t)C::LDS +
                            (wP ? 0u : (uint32_t)C::BP * 4u) + (uint32_t)(4 * kScRows) * w4;
 
@@ -902,7 +909,10 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
   auto tile_src = [&](const Tile& t, const char*& src, int& nouter) {
     const char* P = reinterpret_cast<const char*>(a.p_src);
     const char* Q = reinterpret_cast<const char*>(a.q_src);
-    if (MODE == kFwd || MX) {      // P = W[e] rows n (R = k), Q = X rows m (R = k)
+    if (MODE == kWgradMx) {        // P = X^T rows k (R = i), Q = dY^T rows n (R = i)
+      P += (int64_t)t.p0 * a.M + t.r_begin;
+      Q += (int64_t)t.q0 * a.M + t.r_begin;
+    } else if (MODE == kFwd || MX) {   // P = W[e] rows n (R = k), Q = X rows m (R = k)
       P += ((int64_t)t.e * a.N + t.p0) * a.K * ES;
       Q += (int64_t)t.q0 * a.K * ES;
     } else if (SWI) {              // P = W13[e] rows from p0 (gate; up at + I), Q = X rows
@@ -920,7 +930,7 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
       Q += ((int64_t)t.r_begin * a.N + t.q0) * 2;
     }
     const int nP = (LIST ? list_desc(S.list, t.e).n : Pdim) - t.p0;
-    const int nQ = MODE == kWgrad ? Qdim - t.q0 : t.q_end - t.q0;
+    const int nQ = KG ? Qdim - t.q0 : t.q_end - t.q0;
     src = wP ? P : Q;
     nouter = wP ? nP : nQ;
   };
@@ -964,8 +974,22 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
         // blocked scales: stage s of row r at (s rows_total + r) 4 bytes; W's
         // per expert.  A row past the tile's valid rows reads zero.
         const int row = kScRows * w4 + lane;
+        const int base = wP ? t.p0 : t.q0;
+        if (MODE == kWgradMx) {
+          // X^T's and dY^T's scales over all M tokens: the tile's stages start
+          // at token stage r_begin / 128 (expert boundaries are multiples of 128)
+          const int rows_total = wP ? Pdim : Qdim, ks = (int)((a.M + 127) / 128);
+          const int end = rows_total;
+          sc_rc = make_rsrc(wP ? a.p_scale : a.q_scale,
+                            (uint32_t)ks * (uint32_t)rows_total * 4u);
+          sc_off = (uint32_t)((t.r_begin >> 7) * rows_total + base + row) * 4u;
+          sc_stride = (uint32_t)rows_total * 4u;
+          sc_ok = 0;
+#pragma unroll
+          for (int i = 0; i < kScLoads; ++i) sc_ok |= (base + row + 64 * i < end ? 1u : 0u) << i;
+        } else {
         const int ks = nk;                    // stages of the whole reduction (red = K)
-        const int base = wP ? t.p0 : t.q0, end = wP ? Pdim : t.q_end;
+        const int end = wP ? Pdim : t.q_end;
         if (wP)
           sc_rc = make_rsrc(a.p_scale + (int64_t)t.e * ks * a.N * 4,
                             (uint32_t)ks * (uint32_t)a.N * 4u);
@@ -976,6 +1000,7 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
         sc_ok = 0;
 #pragma unroll
         for (int i = 0; i < kScLoads; ++i) sc_ok |= (base + row + 64 * i < end ? 1u : 0u) << i;
+        }
       }
       if (SWI) {
         tmask = 0;
@@ -1028,7 +1053,7 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
     uint32_t off;
     if (MX) {
       const int cj = 16 * (mx_c0 ^ (d & 3));
-      off = (mx_rowoff + (uint32_t)d * 8u * (uint32_t)a.K + (uint32_t)(cj + r0)) |
+      off = (mx_rowoff + (uint32_t)d * 8u * (uint32_t)ld + (uint32_t)(cj + r0)) |
             (r0 + cj < p_red ? 0u : kOOB);
     } else if (SWI || LIST)
       off = (tvoff[d] + (uint32_t)r0 * 2u) |
@@ -1270,7 +1295,7 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
   };
   // Result block (i, j) held in `blk` (the register layout of acc[i][j]).
   auto store_block = [&](const Tile& t, const OutView& ov, int i, int j, const f32x16& blk) {
-    if (MODE == kWgrad) {
+    if (KG) {
       float* out = reinterpret_cast<float*>(a.out) + (int64_t)t.e * a.N * a.K;
       const int c = pb + 2 * pa;                          // chunk of groups 0 and 1
       // (each element goes through a named float: this compiler lowers
@@ -1351,7 +1376,7 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
     return h;
   };
   auto store_tile = [&](const Tile& t) {
-    if (MODE == kWgrad && a.accumulate && t.r_end <= t.r_begin) return;   // adds nothing
+    if (KG && a.accumulate && t.r_end <= t.r_begin) return;   // adds nothing
     const OutView ov = out_view(t);
     if (SWI) {
 #pragma unroll
@@ -1499,7 +1524,9 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
 template <int MODE, class C>
 __global__ __launch_bounds__(C::NT)
 void grouped_gemm_kernel(KernelArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[C::LDS + (MODE == kFwdMx ? kStages * (C::BP + C::BQ) * 4 : 0)];
+  constexpr bool KG = MODE == kWgrad || MODE == kWgradMx;
+  constexpr bool MXM = MODE == kFwdMx || MODE == kWgradMx;
+  __shared__ __attribute__((aligned(16))) char lds[C::LDS + (MXM ? kStages * (C::BP + C::BQ) * 4 : 0)];
   // keys [64] | scan [16] | mine [2 kMaxExperts + 8] | pref [E+1] | offs [E+1] | inv [E]
   // (keys and mine 16-byte aligned: they are read four entries at a time)
   __shared__ __attribute__((aligned(16))) int sched[64 + 16 + 2 * kMaxExperts + 8 +
@@ -1543,8 +1570,9 @@ void grouped_gemm_kernel(KernelArgs a) {
   int bw = 1;
   while (bw < S.tilesP && 2 * (2 * bw + 1) * (2 * bw + 1) <= S.per) ++bw;
   S.bw = bw;
+  // (the MXFP8 weight gradient does not split: its registers are all taken)
   S.split = MODE == kWgrad && a.ws != nullptr && a.tickets != nullptr;
-  if (MODE == kWgrad) {
+  if (KG) {
     setup_kgrouped<C::NT>(a.offsets, E, (int)a.M, S);
     balance_kgrouped<C::NT>(blockIdx.x & 7, blockIdx.x >> 3, nx, S);
   } else if (MODE == kList) {
@@ -1634,7 +1662,8 @@ int launch_grouped(int mode, const KernelArgs& a_in, int64_t max_m_per_e, hipStr
   KernelArgs a = a_in;
   a.ws = nullptr;
   a.tickets = nullptr;
-  if (mode == kWgrad && a.M > 0 && split_enabled()) {
+  const bool kg = mode == kWgrad || mode == kWgradMx;
+  if (kg && a.M > 0 && split_enabled()) {
     char* w = stream_workspace(s);
     if (w != nullptr) {
       a.tickets = reinterpret_cast<uint32_t*>(w);
@@ -1644,7 +1673,7 @@ int launch_grouped(int mode, const KernelArgs& a_in, int64_t max_m_per_e, hipStr
   int64_t tiles;
   if (mode == kList) {
     tiles = int64_t(1) << 30;                 // unknown on the host: one workgroup per CU
-  } else if (mode == kWgrad) {
+  } else if (kg) {
     const int64_t tilesP = (a.K + Cfg::BP - 1) / Cfg::BP;
     const int64_t tilesQ = (a.N + Cfg::BQ - 1) / Cfg::BQ;
     tiles = (int64_t)a.E * tilesQ * tilesP;
@@ -1677,6 +1706,9 @@ int launch_grouped(int mode, const KernelArgs& a_in, int64_t max_m_per_e, hipStr
     case kList: hipLaunchKernelGGL((grouped_gemm_kernel<kList, Cfg>), g, b, 0, s, a); break;
     case kFwdMx:
       hipLaunchKernelGGL((grouped_gemm_kernel<kFwdMx, CfgMx>), g, dim3(CfgMx::NT), 0, s, a);
+      break;
+    case kWgradMx:
+      hipLaunchKernelGGL((grouped_gemm_kernel<kWgradMx, CfgMx>), g, dim3(CfgMx::NT), 0, s, a);
       break;
     default: hipLaunchKernelGGL((grouped_gemm_kernel<kWgrad, Cfg>), g, b, 0, s, a); break;
   }

@@ -5,7 +5,7 @@
 
 namespace mg {
 
-enum { kFwd = 0, kDgrad = 1, kWgrad = 2, kFwdSwiglu = 3, kList = 4, kFwdMx = 5 };
+enum { kFwd = 0, kDgrad = 1, kWgrad = 2, kFwdSwiglu = 3, kList = 4, kFwdMx = 5, kWgradMx = 6 };
 
 // Largest expert count a launch accepts: the device-side scheduler keeps the
 // per-expert tile prefix in LDS, two entries per thread of a 512-thread block.
@@ -23,12 +23,12 @@ struct ListDesc {
 
 struct KernelArgs {
   const void* p_src;        // FWD/DGRAD: W [E,N,K]; FWD_SWIGLU: W13 [E,N=2I,K]; WGRAD: X [M,K];
-                            // FWD_MX: W8 [E,N,K] E4M3 codes
+                            // FWD_MX: W8 [E,N,K] E4M3 codes; WGRAD_MX: X^T [K,M] E4M3 codes
   const void* q_src;        // FWD: X [M,K]; FWD_SWIGLU: X [M or T,K]; DGRAD/WGRAD: dY [M,N];
-                            // FWD_MX: X8 [M,K] E4M3 codes
+                            // FWD_MX: X8 [M,K] E4M3 codes; WGRAD_MX: dY^T [N,M] E4M3 codes
   const int32_t* offsets;   // [E+1], device
   void* out;                // FWD: Y [M,N] bf16; FWD_SWIGLU: H [M,N/2] bf16; DGRAD: dX [M,K] bf16;
-                            // WGRAD: dW [E,N,K] fp32
+                            // WGRAD, WGRAD_MX: dW [E,N,K] fp32
   int64_t M, N, K;
   int32_t E;
   int32_t accumulate;       // WGRAD only: add into `out`
@@ -37,8 +37,10 @@ struct KernelArgs {
   int64_t T;                // FWD_SWIGLU with gather: rows of x
   float* ws;                // WGRAD token split: 2 slots of 256 x 256 fp32 per split tile
   uint32_t* tickets;        // one zeroed counter per split tile (every launch leaves them zeroed)
-  const uint8_t* p_scale;   // FWD_MX: W's E8M0 scales, blocked [E][ceil(K/128)][N][4]
-  const uint8_t* q_scale;   // FWD_MX: X's E8M0 scales, blocked [ceil(K/128)][M][4]
+  const uint8_t* p_scale;   // FWD_MX: W's E8M0 scales, blocked [E][ceil(K/128)][N][4];
+                            // WGRAD_MX: X^T's, blocked [M/128][K][4]
+  const uint8_t* q_scale;   // FWD_MX: X's E8M0 scales, blocked [ceil(K/128)][M][4];
+                            // WGRAD_MX: dY^T's, blocked [M/128][N][4]
 };
 
 // Rearrange E8M0 scales [batch][rows][K/32] into the blocked layout

@@ -1,11 +1,14 @@
-"""GPU parity of the MXFP8 grouped forward and its scale-layout kernel
-against the fp64 oracle (needs an MI355X).
+"""GPU parity of the MXFP8 grouped forward, the MXFP8 K-grouped weight
+gradient and the scale-layout kernel against the fp64 oracle (needs an
+MI355X).
 
 The GEMM gets the oracle's blocked scales (so its cases do not depend on the
 layout kernel); the layout kernel is compared bit for bit with the oracle's
 layout; one end-to-end case feeds the kernel-made layout to the GEMM.  bf16
 outputs pass the MX gate of oracle/gate.py (one bf16 ulp of the rounded
-exact value, or within the precision floor of the fp8 matrix-core products).
+exact value, or within the precision floor of the fp8 matrix-core products);
+fp32 weight gradients pass the per-element MX fp32 gate, empty experts exactly
+zero (or the prior contents when accumulating).
 """
 import numpy as np
 import pytest
@@ -189,4 +192,113 @@ def test_a3b_mx_sampled(name):
     cols = np.concatenate([cols, np.zeros_like(edges), np.full_like(edges, N - 1)])
     val, mag = sample_fwd_mx(x8, xs, w8, ws, off, rows, cols)
     rep = check_bf16_mx(g1[rows, cols], val, mag)
+    assert rep.passed, str(rep)
+
+
+# ------------------------------------------------------------ MXFP8 wgrad --
+
+from oracle import check_fp32_mx, grouped_wgrad, grouped_wgrad_mx, sample_wgrad_mx  # noqa: E402
+
+
+def _wg_inputs(sizes, N, K, spread, seed, center=121):
+    off = offsets_from_sizes(sizes)
+    M = int(off[-1]) + 128                       # one stage of rows owned by no expert
+    dyt8 = mx_e4m3_codes((N, M), 8400, seed, 1)
+    xt8 = mx_e4m3_codes((K, M), 8400, seed, 2)
+    dyts = mx_e8m0_codes((N, M // 32), center, spread, 8400, seed, 3)
+    xts = mx_e8m0_codes((K, M // 32), center, spread, 8400, seed, 4)
+    return off, M, dyt8, dyts, xt8, xts
+
+
+def _wg_gate(off, dyt8, dyts, xt8, xts, got, prior=None):
+    E = len(off) - 1
+    exact = grouped_wgrad_mx(dyt8, dyts, xt8, xts, off, E, prior=prior)
+    mag = grouped_wgrad(np.abs(mx_dequant(dyt8, dyts)).T, np.abs(mx_dequant(xt8, xts)).T, off, E)
+    sizes = np.diff(np.asarray(off, np.int64))
+    k_red = np.broadcast_to(np.maximum(sizes, 1)[:, None, None], exact.shape)
+    empty = np.broadcast_to((sizes == 0)[:, None, None], exact.shape)
+    return check_fp32_mx(got, exact, mag, k_red, empty_mask=empty,
+                         empty_expect=None if prior is None else prior)
+
+
+# (expert sizes in multiples of 128, N, K, scale spread)
+WG_MX_CASES = [
+    ([128, 0, 384, 256], 264, 136, 2),
+    ([1024], 520, 264, 1),
+    ([0, 128], 8, 8, 0),
+    ([128, 128, 128, 128, 128, 0, 640], 256, 256, 1),
+    ([2048, 128, 0, 256], 136, 520, 3),
+]
+
+
+@pytest.mark.parametrize("case", range(len(WG_MX_CASES)))
+@pytest.mark.parametrize("accumulate", [False, True])
+def test_wgrad_mx(case, accumulate):
+    sizes, N, K, spread = WG_MX_CASES[case]
+    _say("wgrad_mx", sizes, N, K, spread, "accumulate" if accumulate else "")
+    off, M, dyt8, dyts, xt8, xts = _wg_inputs(sizes, N, K, spread, case)
+    E = len(sizes)
+    prior = None
+    if accumulate:
+        prior = np.random.default_rng(case).standard_normal((E, N, K)).astype(np.float32)
+        out = torch.from_numpy(prior.copy()).cuda()
+    else:
+        out = torch.full((E, N, K), float("nan"), dtype=torch.float32, device="cuda")
+    mg.wgrad_mx(_u8(dyt8), _u8(mx_scales_blocked(dyts)), _u8(xt8), _u8(mx_scales_blocked(xts)),
+                dev_i32(off), E, out=out, accumulate=accumulate)
+    got = out.cpu().numpy()
+    rep = _wg_gate(off, dyt8, dyts, xt8, xts, got,
+                   prior=None if prior is None else prior.astype(np.float64))
+    assert rep.passed, str(rep)
+
+
+def test_wgrad_mx_is_deterministic_and_layout_kernel_end_to_end():
+    sizes, N, K = [256, 0, 512], 136, 264
+    off, M, dyt8, dyts, xt8, xts = _wg_inputs(sizes, N, K, 2, 77)
+    _say("wgrad_mx end to end", sizes, N, K)
+    a = (_u8(dyt8), mg.mx_scales_blocked(_u8(dyts)), _u8(xt8), mg.mx_scales_blocked(_u8(xts)))
+    o = dev_i32(off)
+    r1 = mg.wgrad_mx(*a, o).cpu().numpy()
+    r2 = mg.wgrad_mx(*a, o).cpu().numpy()
+    assert (r1 == r2).all()
+    assert _wg_gate(off, dyt8, dyts, xt8, xts, r1).passed
+
+
+def test_wgrad_mx_rejects_bad_shapes():
+    z = lambda *s: torch.zeros(s, dtype=torch.uint8, device="cuda")
+    with pytest.raises(mg.MgemmError):                    # M not a multiple of 128
+        mg.LIB and mg.check(mg.LIB.kgemm_wgrad_mx(z(8, 96).data_ptr(), z(1, 8, 4).data_ptr(),
+                                                   z(8, 96).data_ptr(), z(1, 8, 4).data_ptr(),
+                                                   dev_i32(offsets_from_sizes([96])).data_ptr(),
+                                                   torch.zeros(1, 8, 8, device="cuda").data_ptr(),
+                                                   96, 8, 8, 1, 0, None), "kgemm_wgrad_mx")
+
+
+@pytest.mark.parametrize("name", ["a3b_zipf_gw13", "a3b_zipf_gw2"])
+def test_a3b_zipf_wgrad_mx_sampled(name):
+    """The skewed 30B-A3B weight gradients with MXFP8 operands, experts padded
+    to whole 128-token stages: sampled elements against the oracle, empty
+    experts exactly zero."""
+    (wl,) = make_workload(5, name)
+    sizes = [((int(s) + 127) // 128) * 128 for s in wl.sizes()]
+    off = offsets_from_sizes(sizes)
+    M, N, K, E = int(off[-1]), wl.N, wl.K, wl.E
+    _say("a3b wgrad mx", name, M, N, K, E)
+    dyt8 = mx_e4m3_codes((N, M), 8500, wl.tag, 1)
+    xt8 = mx_e4m3_codes((K, M), 8500, wl.tag, 2)
+    dyts = mx_e8m0_codes((N, M // 32), 121, 1, 8500, wl.tag, 3)
+    xts = mx_e8m0_codes((K, M // 32), 121, 1, 8500, wl.tag, 4)
+    dw = mg.wgrad_mx(_u8(dyt8), _u8(mx_scales_blocked(dyts)), _u8(xt8),
+                     _u8(mx_scales_blocked(xts)), dev_i32(off), E)
+    got = dw.cpu().numpy()
+    sz = np.asarray(sizes)
+    assert (got[sz == 0] == 0).all()
+    rng = np.random.default_rng(8501)
+    live = np.flatnonzero(sz > 0)
+    es = np.concatenate([rng.choice(live, 384), live, live])
+    ns = np.concatenate([rng.integers(0, N, 384), np.zeros_like(live), np.full_like(live, N - 1)])
+    ks = np.concatenate([rng.integers(0, K, 384), np.full_like(live, K - 1), np.zeros_like(live)])
+    val, mag = sample_wgrad_mx(dyt8, dyts, xt8, xts, off, es, ns, ks)
+    k_red = np.maximum(sz[es], 1)
+    rep = check_fp32_mx(got[es, ns, ks], val, mag, k_red)
     assert rep.passed, str(rep)
