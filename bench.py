@@ -37,7 +37,8 @@ PEAK_FP8_TFLOPS = 5000.0         # MI355X published dense fp8 matrix-core peak
 KERNEL_SRC = os.path.join(ROOT, "moe_grouped_gemm_bf16_amd", "csrc", "mgemm_kernels.hip")
 KERNEL_NAMES = {"fwd": "grouped_gemm_kernel<0>", "dgrad": "grouped_gemm_kernel<1>",
                 "wgrad": "grouped_gemm_kernel<2>", "fwd_swiglu": "grouped_gemm_kernel<3>",
-                "list": "grouped_gemm_kernel<4>", "fwd_mx": "grouped_gemm_kernel<5>"}
+                "list": "grouped_gemm_kernel<4>", "fwd_mx": "grouped_gemm_kernel<5>",
+                "wgrad_mx": "grouped_gemm_kernel<6>"}
 
 
 def kernel_hash() -> str:
@@ -355,6 +356,46 @@ def mx(torch, mg, reps=20):
             "scale_layout_us": round(t[2], 1),
             "scale_layout_GBps": round(sc_bytes / t[2] / 1e3, 1)}
         del x8, w8, xs, ws, bx, bw, x, w, y8, y
+        torch.cuda.empty_cache()
+    # weight gradients: uniform g8 and the skewed 30B-A3B ones, experts padded to
+    # whole 128-token stages (the MXFP8 call's requirement), the bf16 call on the
+    # same offsets
+    from workloads import offsets_from_sizes
+    for wl in [make_workload(2)[0]] + make_workload(5):
+        sizes = [((int(v) + 127) // 128) * 128 for v in wl.sizes()]
+        offn = offsets_from_sizes(sizes)
+        M, N, K, E = int(offn[-1]), wl.N, wl.K, wl.E
+        off = torch.from_numpy(offn).cuda()
+        dyt8 = u8(mx_e4m3_codes((N, M), 8310, wl.cfg, wl.tag, 1))
+        xt8 = u8(mx_e4m3_codes((K, M), 8310, wl.cfg, wl.tag, 2))
+        bd = mg.mx_scales_blocked(u8(mx_e8m0_codes((N, M // 32), 121, 1, 8310, wl.cfg, wl.tag, 3)))
+        bx = mg.mx_scales_blocked(u8(mx_e8m0_codes((K, M // 32), 121, 1, 8310, wl.cfg, wl.tag, 4)))
+        dy = torch.randn((M, N), device="cuda").to(torch.bfloat16)
+        x = torch.randn((M, K), device="cuda").to(torch.bfloat16)
+        d8 = torch.empty((E, N, K), dtype=torch.float32, device="cuda")
+        d16 = torch.empty_like(d8)
+        fns = (lambda: mg.wgrad_mx(dyt8, bd, xt8, bx, off, E, out=d8),
+               lambda: mg.wgrad(dy, x, off, E, out=d16))
+        for _ in range(3):
+            for fn in fns:
+                fn()
+        torch.cuda.synchronize()
+        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in fns] for _ in range(reps)]
+        for row in ev:
+            for (a, b), fn in zip(row, fns):
+                a.record()
+                fn()
+                b.record()
+        torch.cuda.synchronize()
+        t = [statistics.median(r[i][0].elapsed_time(r[i][1]) for r in ev) * 1e3
+             for i in range(len(fns))]
+        flops = 2 * M * N * K
+        out[f"wgrad_mx:{wl.name}"] = {
+            "rows": M, "mx_us": round(t[0], 1), "tflops": round(flops / t[0] / 1e6, 1),
+            "pct_fp8_peak": round(100 * flops / t[0] / 1e6 / PEAK_FP8_TFLOPS, 1),
+            "bf16_us": round(t[1], 1), "speedup_vs_bf16": round(t[1] / t[0], 3)}
+        del dyt8, xt8, bd, bx, dy, x, d8, d16
         torch.cuda.empty_cache()
     return out
 
