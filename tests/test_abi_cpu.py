@@ -123,6 +123,23 @@ def test_mx_argument_errors():
     assert g(None, None, 0, 64, 1, None) == OK                           # nothing to convert
 
 
+def test_wgrad_mx_argument_errors():
+    f = L.kgemm_wgrad_mx
+    # (dyt, dyt_scale, xt, xt_scale, offsets, dw, M, N, K, E, accumulate, stream)
+    assert f(A, A, A, A, A, A, 512, 128, 256, 0, 0, None) == SHAPE        # E < 1
+    assert f(A, A, A, A, A, A, 500, 128, 256, 4, 0, None) == SHAPE        # M % 128
+    assert f(A, A, A, A, A, A, 512, 100, 256, 4, 0, None) == SHAPE        # N % 8
+    assert f(A, A, A, A, A, A, 1 << 24, 128, 256, 4, 0, None) == SHAPE    # 256 M >= 2^32
+    assert f(None, A, A, A, A, A, 512, 128, 256, 4, 0, None) == NUL
+    assert f(A, A, A, None, A, A, 512, 128, 256, 4, 0, None) == NUL
+    assert f(A, A, A, A, None, A, 512, 128, 256, 4, 0, None) == NUL
+    assert f(A, A, A, A, A, None, 512, 128, 256, 4, 0, None) == NUL
+    assert f(A + 8, A, A, A, A, A, 512, 128, 256, 4, 0, None) == ALIGN
+    assert f(A, A + 2, A, A, A, A, 512, 128, 256, 4, 0, None) == ALIGN
+    assert f(A, A, A, A, A, A + 8, 512, 128, 256, 4, 0, None) == ALIGN
+    assert f(None, None, None, None, None, None, 512, 0, 256, 4, 0, None) == OK   # empty dw
+
+
 def test_python_binding_rejects_bad_tensors_on_host():
     torch = pytest.importorskip("torch")
     import moe_grouped_gemm_bf16_amd as mg
