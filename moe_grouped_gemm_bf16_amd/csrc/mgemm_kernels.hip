@@ -1146,6 +1146,44 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
     uint32_t sp, sq;
   };
   static_assert(!MX || (C::MP == 4 && C::MQ == 4), "one scale byte per block in a dword");
+  // MXFP8 reads in two parts, so that the products can run between them: the
+  // scale dwords of the rows (32 apart) ...
+  auto mx_read_sc = [&](int g, uint32_t (&raw)[8]) {
+    const char* sc = lds + C::LDS + (g % kStages) * kScStage;
+    const uint32_t* rp = reinterpret_cast<const uint32_t*>(sc + (wp * C::WTP + l32) * 4);
+    const uint32_t* rq = reinterpret_cast<const uint32_t*>(sc + C::BP * 4 + (wq * C::WTQ + l32) * 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      raw[i] = rp[32 * i];
+      raw[4 + i] = rq[32 * i];
+    }
+  };
+  // ... then their bytes 2 kk + h packed one per block, and the fragments
+  auto mx_pack_read_fr = [&](int g, int kk, const uint32_t (&raw)[8], Frags& f) {
+    if constexpr (MX) {
+      const int sh = 8 * (2 * kk + h);
+      auto pk = [&](int o) {
+        const uint32_t lo = __builtin_amdgcn_perm(raw[o + 1] >> sh, raw[o] >> sh, 0x0c0c0400u);
+        const uint32_t hi = __builtin_amdgcn_perm(raw[o + 3] >> sh, raw[o + 2] >> sh, 0x0c0c0400u);
+        return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+      };
+      f.sp = pk(0);
+      f.sq = pk(4);
+      const char* tp = lds + (g % kStages) * C::STAGE;
+      const char* tq = tp + C::P_BYTES;
+      const uint32_t p0 = offP[0] ^ (uint32_t)(64 * kk), p1 = offP[0] ^ (uint32_t)(64 * kk + 32);
+      const uint32_t q0 = offQ[0] ^ (uint32_t)(64 * kk), q1 = offQ[0] ^ (uint32_t)(64 * kk + 32);
+      auto frag8 = [&](const char* tile, uint32_t off0, uint32_t off1) {
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(tile + off0);
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(tile + off1);
+        return (i32x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+#pragma unroll
+      for (int i = 0; i < C::MP; ++i) f.p[i] = frag8(tp, p0 + i * 32 * kRowB, p1 + i * 32 * kRowB);
+#pragma unroll
+      for (int j = 0; j < C::MQ; ++j) f.q[j] = frag8(tq, q0 + j * 32 * kRowB, q1 + j * 32 * kRowB);
+    }
+  };
   auto read = [&](int g, int kk, Frags& f) {
     const char* tp = lds + (g % kStages) * C::STAGE;
     const char* tq = tp + C::P_BYTES;
@@ -1488,6 +1526,46 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
       for (int kk = 0; kk < KK; ++kk) {
         Frags& cur = fr[kk & 1];
         Frags& nxt = fr[(kk + 1) & 1];
+        if constexpr (MX) {
+          // The next slice's scale reads go first; they are packed after two
+          // products, when they have landed, and only then are the fragment
+          // reads issued (a pack right behind all the reads would wait for
+          // most of them: the LDS counter tracks at most 15 in order, and one
+          // wave per SIMD leaves the matrix core idle meanwhile).
+          constexpr int X2 = 2;
+          uint32_t raw[8];
+          if (kk + 1 < KK) {
+            mx_read_sc(g, raw);
+            __builtin_amdgcn_sched_barrier(0);
+            mma_part(cur, 0, X2, sd_none, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            mx_pack_read_fr(g, kk + 1, raw, nxt);
+            __builtin_amdgcn_sched_barrier(0);
+            mma_part(cur, X2, kMM, sd_none, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+          } else {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __syncthreads();
+            const bool more = g + 1 < gp;
+            const StageDma sd = dma_begin();
+            __builtin_amdgcn_sched_barrier(0);
+            mma_part(cur, 0, kMM / 2, sd, 0, SPW / 2);
+            __builtin_amdgcn_sched_barrier(0);
+            if (more) {
+              wait_stage(g + 1);
+              __syncthreads();
+              mx_read_sc(g + 1, raw);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            mma_part(cur, kMM / 2, kMM / 2 + X2, sd, SPW / 2, SPW / 2 + X2);
+            __builtin_amdgcn_sched_barrier(0);
+            if (more) mx_pack_read_fr(g + 1, 0, raw, nxt);
+            __builtin_amdgcn_sched_barrier(0);
+            mma_part(cur, kMM / 2 + X2, kMM, sd, SPW / 2 + X2, SPW);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          continue;
+        }
         if (kk + 1 < KK) {
           read(g, kk + 1, nxt);
           __builtin_amdgcn_sched_barrier(0);
