@@ -302,3 +302,28 @@ def test_a3b_zipf_wgrad_mx_sampled(name):
     k_red = np.maximum(sz[es], 1)
     rep = check_fp32_mx(got[es, ns, ks], val, mag, k_red)
     assert rep.passed, str(rep)
+
+
+def test_mx_dgrad_is_forward_on_requantized_transposed_weights():
+    """The MXFP8 input gradient dX = dY W_e as the forward call: dY quantized
+    along N, the weights stored transposed [E, K, N] and quantized along N.
+    Checked against the oracle's grouped dgrad definition on the dequantized
+    values (W_e = the transpose of the dequantized [K, N] matrix)."""
+    from oracle import grouped_dgrad
+    sizes, N, K = [200, 0, 137, 300], 256, 264
+    off = offsets_from_sizes(sizes)
+    M, E = int(off[-1]), len(sizes)
+    _say("mx dgrad via forward", sizes, N, K)
+    dy8 = mx_e4m3_codes((M, N), 8600, 1)
+    dys = mx_e8m0_codes((M, N // 32), 121, 1, 8600, 2)
+    wt8 = mx_e4m3_codes((E, K, N), 8600, 3)
+    wts = mx_e8m0_codes((E, K, N // 32), 121, 1, 8600, 4)
+    dx = mg.fwd_mx(_u8(dy8), _u8(mx_scales_blocked(dys)), _u8(wt8), _u8(mx_scales_blocked(wts)),
+                   dev_i32(off), out=sentinel_bf16((M, K)))
+    got = host_bits(dx)
+    dyv = mx_dequant(dy8, dys)
+    w = np.ascontiguousarray(np.transpose(mx_dequant(wt8, wts), (0, 2, 1)))   # [E, N, K]
+    exact = grouped_dgrad(dyv, w, off)
+    mag = grouped_dgrad(np.abs(dyv), np.abs(w), off)
+    rep = check_bf16_mx(got, exact, mag)
+    assert rep.passed, str(rep)
