@@ -171,7 +171,8 @@ mg_status mgemm_fwd_mx(const void* x, const void* x_scale, const void* w, const 
  * .. + 31]); xt_scale: blocked [M/128][K][4]; dw: fp32 [E, N, K].
  * M a multiple of 128, and every offsets[e] a multiple of 128 (experts padded
  * to whole 128-token stages; checked only under MGEMM_VALIDATE=1 -- otherwise
- * other offsets give wrong sums, never out-of-bounds accesses); N and K
+ * each expert's range is widened to whole stages: wrong sums, but never
+ * misaligned or out-of-bounds accesses); N and K
  * multiples of 8; 256 M < 2^32; M/128 N and M/128 K below 2^29.  Pointers:
  * dyt, xt, dw 16-byte aligned, scales 4-byte aligned.  accumulate as for
  * kgemm_wgrad; an expert with no rows gets zeros (or is left as it was).  The

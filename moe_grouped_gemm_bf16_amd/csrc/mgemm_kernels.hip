@@ -733,6 +733,13 @@ struct TileSeq {
       const int v = rho + j * nx;                 // piece of the chunk
       const int u = sp ? v >> 1 : v;
       decode_kgrouped<BP, BQ>(r, (x - r) & 7, u, S, t);
+      if (MODE == kWgradMx) {
+        // whole 128-token stages (a no-op for offsets that are multiples of
+        // 128, as documented; others give wrong sums but only aligned,
+        // in-bounds loads: M is a multiple of 128)
+        t.r_begin &= ~(SBK - 1);
+        t.r_end = (t.r_end + SBK - 1) & ~(SBK - 1);
+      }
       if (sp) {
         // halves of the token range, split at a stage boundary
         const int st = (t.r_end - t.r_begin + SBK - 1) / SBK;
