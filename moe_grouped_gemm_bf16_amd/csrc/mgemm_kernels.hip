@@ -1178,6 +1178,9 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
       f.sq = pk(4);
       const char* tp = lds + (g % kStages) * C::STAGE;
       const char* tq = tp + C::P_BYTES;
+      // chunk 2 kk' + h of a 128-byte row: offP[kk'] = offP[0] ^ (kk' << 5) (the
+      // row base has no low bits and (2 kk' + h) ^ swz = (h ^ swz) ^ 2 kk'), which
+      // keeps one address register per operand instead of four
       const uint32_t p0 = offP[0] ^ (uint32_t)(64 * kk), p1 = offP[0] ^ (uint32_t)(64 * kk + 32);
       const uint32_t q0 = offQ[0] ^ (uint32_t)(64 * kk), q1 = offQ[0] ^ (uint32_t)(64 * kk + 32);
       auto frag8 = [&](const char* tile, uint32_t off0, uint32_t off1) {
@@ -1195,32 +1198,9 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
     const char* tp = lds + (g % kStages) * C::STAGE;
     const char* tq = tp + C::P_BYTES;
     if constexpr (MX) {
-      auto frag8 = [&](const char* tile, uint32_t off0, uint32_t off1) {
-        const i32x4 lo = *reinterpret_cast<const i32x4*>(tile + off0);
-        const i32x4 hi = *reinterpret_cast<const i32x4*>(tile + off1);
-        return (i32x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      };
-      const char* sc = lds + C::LDS + (g % kStages) * kScStage;
-      const int sh = 8 * (2 * kk + h);
-      // chunk 2 kk' + h of a 128-byte row: offP[kk'] = offP[0] ^ (kk' << 5) (the
-      // row base has no low bits and (2 kk' + h) ^ swz = (h ^ swz) ^ 2 kk'), which
-      // keeps one address register per operand instead of four
-      const uint32_t p0 = offP[0] ^ (uint32_t)(64 * kk), p1 = offP[0] ^ (uint32_t)(64 * kk + 32);
-      const uint32_t q0 = offQ[0] ^ (uint32_t)(64 * kk), q1 = offQ[0] ^ (uint32_t)(64 * kk + 32);
-      // byte 0 of each row's scale dword, shifted by 8 (2 kk + h), packed
-      auto pack = [&](const char* rows) {
-        const uint32_t* r = reinterpret_cast<const uint32_t*>(rows);
-        const uint32_t r0 = r[0] >> sh, r1 = r[32] >> sh, r2 = r[64] >> sh, r3 = r[96] >> sh;
-        const uint32_t lo = __builtin_amdgcn_perm(r1, r0, 0x0c0c0400u);
-        const uint32_t hi = __builtin_amdgcn_perm(r3, r2, 0x0c0c0400u);
-        return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-      };
-#pragma unroll
-      for (int i = 0; i < C::MP; ++i) f.p[i] = frag8(tp, p0 + i * 32 * kRowB, p1 + i * 32 * kRowB);
-#pragma unroll
-      for (int j = 0; j < C::MQ; ++j) f.q[j] = frag8(tq, q0 + j * 32 * kRowB, q1 + j * 32 * kRowB);
-      f.sp = pack(sc + (wp * C::WTP + l32) * 4);
-      f.sq = pack(sc + C::BP * 4 + (wq * C::WTQ + l32) * 4);
+      uint32_t raw[8];
+      mx_read_sc(g, raw);
+      mx_pack_read_fr(g, kk, raw, f);
       return;
     } else {
 #pragma unroll
