@@ -182,7 +182,7 @@ def comparators(ops, torch, reps=20):
                 us = timed(grp)
                 rec["torch_grouped_mm"] = {"us": round(us, 1),
                                            "tflops": round(op.flops / us / 1e6, 1)}
-            except Exception as exc:                       # not supported on this build
+            except Exception as exc:                       # not supported by this PyTorch
                 rec["torch_grouped_mm"] = {"error": f"{type(exc).__name__}: {str(exc)[:120]}"}
         if op.kind == "wgrad":
             rec["note"] = "comparators write bf16 dW; the kernel writes fp32"
@@ -463,7 +463,7 @@ def load_traffic(workload: str, kernel: str):
 def main():
     args = parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
     import torch
