@@ -21,6 +21,10 @@ per expert; nothing blocked, fused or reordered):
     stacked gate/up weight gw13 refers to): row i reads token row gather[i],
     h[i, j] = silu(x . w1[e, j]) * (x . w3[e, j]) with w1, w3 the two halves of
     the expert's [2I, K] weight.
+  * Its backward through the down projection: dh = dy W2[e] (the grouped input
+    gradient), then the SwiGLU backward dg = dh u silu'(g), du = dh silu(g) on
+    the saved pre-activation g | u (the DeepGEMM issue #10 thread: a kernel
+    fused with SwiGLU is part of a weight-gradient path).
   * A list of independent GEMMs D_g = A_g B_g^T with per-group shapes (the
     TransformerEngine PR #2045 review: one C API over lists of tensors; the
     CUTLASS discussion #1452: nested grouped GEMMs flattened into one list).
@@ -40,7 +44,9 @@ adjoint identity tying fwd/dgrad/wgrad together, empty-group insertion,
 exhaustive codec round trips and tie cases; for the SwiGLU forward, scalar
 brute force with math.exp, one-hot closed forms that tell the gate half from
 the up half, gather-as-permutation identities, and a gate that rejects a wrong
-expert or a dropped term; for the descriptor list, exact rational brute force on
+expert or a dropped term; for the SwiGLU backward, central finite
+differences of silu(g) u and the chain-rule identity <dgu, [dg0, du0]> =
+<dh, d(silu(g) u)> for a perturbation; for the descriptor list, exact rational brute force on
 groups of mixed shapes (empty and zero-reduction ones included), a one-hot
 transpose check and the flattened LoRA x experts identity; for MXFP8, the
 element and scale decoders against torch's float8_e4m3fn / float8_e8m0fnu
@@ -62,6 +68,8 @@ from .grouped_gemm import (  # noqa: F401
     sample_wgrad,
     grouped_fwd_swiglu,
     sample_fwd_swiglu,
+    grouped_dgrad_swiglu,
+    sample_dgrad_swiglu,
     grouped_list,
 )
 from .mx import (  # noqa: F401
@@ -75,4 +83,4 @@ from .mx import (  # noqa: F401
     mx_scales_blocked,
 )
 from .gate import (check_bf16, check_bf16_swiglu, check_bf16_mx, check_fp32,  # noqa: F401
-                   check_fp32_mx, GateReport)
+                   check_fp32_mx, check_bf16_factor, GateReport)

@@ -25,6 +25,13 @@ multiply:
     dg = 2^-24 sqrt(K) S_g,  du = 2^-24 sqrt(K) S_u,
     silu'(g) = s (1 + g (1 - s)),  s = 1 / (1 + exp(-g)).
 
+bf16 outputs of the SwiGLU backward, dg = dh u silu'(g) and du = dh silu(g)
+with dh an fp32-accumulated sum and g, u given: the same strict gate, the
+floor carrying dh's summation error through the factor f (u silu'(g) or
+silu(g)) plus a few fp32 roundings:
+
+    |got - exact| <= ulp(got) / 2 + |f| 2^-24 sqrt(K) S + 2^-20 |exact|.
+
 bf16 outputs of the MXFP8 forward.  Same strict gate; the floor is that of
 the fp8 dot products of gfx950's scaled matrix-core instruction, which do not
 sum in fp32: measured on random E4M3 operands with random E8M0 scales, one
@@ -115,6 +122,24 @@ def check_bf16_swiglu(got_bits: np.ndarray, h: np.ndarray, g: np.ndarray, u: np.
     if fails:
         i = int(np.argmax(np.where(ok, -np.inf, np.abs(got - h))))
         worst = f"worst@{i}: got={got.flat[i]!r} exact={h.flat[i]!r}"
+    return GateReport(int(got.size), fails == 0, fails, int((~strict).sum()), 0.0, worst)
+
+
+def check_bf16_factor(got_bits: np.ndarray, exact: np.ndarray, factor: np.ndarray,
+                      abs_sum: np.ndarray, k_red) -> GateReport:
+    """Gate for bf16 outputs f * dh with dh an fp32 sum (see the header)."""
+    got = bf16_bits_to_f64(got_bits)
+    exact = np.asarray(exact, np.float64)
+    b = f64_round_bf16(exact)
+    strict = np.abs(got - b) <= bf16_ulp(b)
+    bound = (0.5 * bf16_ulp(got) + np.abs(factor) * U32 * np.sqrt(k_red) * abs_sum
+             + 2.0 ** -20 * np.abs(exact))
+    ok = (strict | (np.abs(got - exact) <= bound)) & np.isfinite(got)
+    fails = int((~ok).sum())
+    worst = ""
+    if fails:
+        i = int(np.argmax(np.where(ok, -np.inf, np.abs(got - exact))))
+        worst = f"worst@{i}: got={got.flat[i]!r} exact={exact.flat[i]!r}"
     return GateReport(int(got.size), fails == 0, fails, int((~strict).sum()), 0.0, worst)
 
 

@@ -108,6 +108,50 @@ def grouped_fwd_swiglu(x: np.ndarray, gather, w13: np.ndarray, offsets) -> np.nd
     return h
 
 
+def _sigmoid(g: np.ndarray) -> np.ndarray:
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-g))
+
+
+def grouped_dgrad_swiglu(dy: np.ndarray, w2: np.ndarray, gu: np.ndarray, offsets):
+    """Down-projection input gradient with the SwiGLU backward (fp64).
+
+    The DeepGEMM issue #10 thread counts a kernel fused with SwiGLU among what a
+    weight-gradient path needs besides the GEMMs.  With the forward
+    h = silu(g) u (grouped_fwd_swiglu) followed by the down projection
+    y = h W2[e]^T (W2 [E, N, I]), the backward takes dy [M, N] and the saved
+    pre-activation gu [M, 2I] (g in columns 0..I-1, u in I..2I-1) and returns
+    dgu [M, 2I]:
+        dh = dy @ W2[e]                           (the grouped input gradient)
+        dg = dh u silu'(g),  silu'(g) = s (1 + g (1 - s)),  s = 1 / (1 + exp(-g))
+        du = dh silu(g)
+    for the rows of expert e; rows at or past offsets[E] are NaN.  Also
+    returns dh."""
+    M, N = dy.shape
+    E, N2, I = w2.shape
+    assert N == N2 and gu.shape == (M, 2 * I)
+    dh = grouped_dgrad(dy, w2, offsets)
+    g, u = gu[:, :I], gu[:, I:]
+    s = _sigmoid(g)
+    dgu = np.concatenate([dh * u * s * (1.0 + g * (1.0 - s)), dh * g * s], axis=1)
+    return dgu, dh
+
+
+def sample_dgrad_swiglu(dy, w2, gu, offsets, rows, cols):
+    """dg and du at (rows[j], cols[j]) (cols < I) one element at a time, fp64.
+
+    Returns (dg, du, dh, sum |dy w2|) for the parity gate."""
+    rows = np.asarray(rows); cols = np.asarray(cols)
+    e = expert_of_rows(offsets, rows)
+    assert (e >= 0).all()
+    I = w2.shape[2]
+    p = _f64(dy[rows]) * _f64(w2[e, :, cols])         # [S, N]
+    dh = p.sum(axis=1)
+    g = _f64(gu[rows, cols]); u = _f64(gu[rows, I + cols])
+    s = _sigmoid(g)
+    return dh * u * s * (1.0 + g * (1.0 - s)), dh * g * s, dh, np.abs(p).sum(axis=1)
+
+
 def sample_fwd_swiglu(x: np.ndarray, gather, w13: np.ndarray, offsets, rows, cols):
     """h[rows[j], cols[j]] of grouped_fwd_swiglu one element at a time, fp64.
 
