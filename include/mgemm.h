@@ -106,6 +106,34 @@ mg_status mgemm_fwd_swiglu(const void* x, const int32_t* gather, const void* w13
                            const int32_t* offsets, void* h, int64_t M, int64_t T, int64_t I,
                            int64_t K, int32_t E, int64_t max_m_per_e, void* stream);
 
+/* mgemm_fwd_swiglu that also writes the pre-activation the backward needs:
+ * gu: bf16 [M, 2I] (written when not NULL): gu[i, j] = g, gu[i, I + j] = u,
+ * each the fp32 accumulator rounded to nearest even (the values h was computed
+ * from, before that rounding).  16-byte aligned.  Otherwise exactly
+ * mgemm_fwd_swiglu, which is this call with gu == NULL. */
+mg_status mgemm_fwd_swiglu_gu(const void* x, const int32_t* gather, const void* w13,
+                              const int32_t* offsets, void* h, void* gu, int64_t M, int64_t T,
+                              int64_t I, int64_t K, int32_t E, int64_t max_m_per_e,
+                              void* stream);
+
+/* Down-projection input gradient fused with the SwiGLU backward (DeepGEMM
+ * issue #10: a kernel fused with SwiGLU is part of a weight-gradient path).
+ * With the forward h = silu(g) u (mgemm_fwd_swiglu_gu) and y = h W2[e]^T:
+ *   dh[i, j]  = sum_n dy[i, n] w2[e, n, j]        (fp32, not stored)
+ *   dgu[i, j]     = dh u silu'(g),  silu'(g) = s (1 + g (1 - s)),  s = 1/(1 + e^-g)
+ *   dgu[i, I + j] = dh silu(g)
+ * with g = gu[i, j], u = gu[i, I + j], for offsets[e] <= i < offsets[e+1].
+ * dy: bf16 [M, N]; w2: bf16 [E, N, I] (the down weights, N = model width);
+ * gu: bf16 [M, 2I] (the saved pre-activation); dgu: bf16 [M, 2I] (written,
+ * the gradient of gu, ready for the gate-up weight and input gradients).
+ * The activation backward in fp32, one rounding to bf16.  Rows i >=
+ * offsets[E] of dgu are not touched.  I and N multiples of 8; all pointers
+ * 16-byte aligned.  M == 0 or I == 0 is a no-op; N == 0 writes zeros.
+ * Allocates nothing.  max_m_per_e: launch-size hint, as for mgemm_fwd. */
+mg_status mgemm_dgrad_swiglu(const void* dy, const void* w2, const void* gu,
+                             const int32_t* offsets, void* dgu, int64_t M, int64_t N, int64_t I,
+                             int32_t E, int64_t max_m_per_e, void* stream);
+
 /* One group of mgemm_list: D [m, n] = A [m, k] B [n, k]^T (bf16 in and out,
  * fp32 accumulation, round to nearest even), row-major with row strides in
  * elements.  All three pointers are DEVICE pointers, 16-byte aligned; k, n and

@@ -133,7 +133,8 @@ def wgrad(dy: torch.Tensor, x: torch.Tensor, offsets: torch.Tensor, E: int | Non
 
 def fwd_swiglu(x: torch.Tensor, w13: torch.Tensor, offsets: torch.Tensor,
                gather: torch.Tensor | None = None, max_m_per_e: int = 0,
-               out: torch.Tensor | None = None) -> torch.Tensor:
+               out: torch.Tensor | None = None, gu_out: torch.Tensor | None = None
+               ) -> torch.Tensor:
     """Gate-up forward with SwiGLU fused, on rows gathered through an index.
 
     w13 bf16 [E, 2I, K] stacks each expert's gate (rows 0..I-1) and up
@@ -141,7 +142,8 @@ def fwd_swiglu(x: torch.Tensor, w13: torch.Tensor, offsets: torch.Tensor,
     expert-grouped problem is x[gather[i]] of the token-major x bf16 [T, K];
     without it x is bf16 [M, K], already grouped.  Returns h bf16 [M, I]:
     h[i, j] = silu(g) * u, g = x[r] . w13[e, j], u = x[r] . w13[e, I + j].
-    Rows past offsets[E] of `out` are left untouched."""
+    With `gu_out` (bf16 [M, 2I]) the pre-activation g | u is written too, for
+    dgrad_swiglu.  Rows past offsets[E] of `out` are left untouched."""
     _need(x, "x", torch.bfloat16, 2)
     _need(w13, "w13", torch.bfloat16, 3)
     T, K = x.shape
@@ -167,10 +169,48 @@ def fwd_swiglu(x: torch.Tensor, w13: torch.Tensor, offsets: torch.Tensor,
         _need(out, "out", torch.bfloat16, 2)
         if tuple(out.shape) != (M, I):
             raise ValueError(f"out must be [{M}, {I}]")
+    guptr = 0
+    if gu_out is not None:
+        _need(gu_out, "gu_out", torch.bfloat16, 2)
+        if tuple(gu_out.shape) != (M, 2 * I):
+            raise ValueError(f"gu_out must be [{M}, {2 * I}]")
+        guptr = gu_out.data_ptr()
     with torch.cuda.device(x.device):
-        st = LIB.mgemm_fwd_swiglu(x.data_ptr(), gptr, w13.data_ptr(), offsets.data_ptr(),
-                                  out.data_ptr(), M, T, I, K, E, int(max_m_per_e), _stream(x))
-    check(st, "mgemm_fwd_swiglu")
+        st = LIB.mgemm_fwd_swiglu_gu(x.data_ptr(), gptr, w13.data_ptr(), offsets.data_ptr(),
+                                     out.data_ptr(), guptr, M, T, I, K, E, int(max_m_per_e),
+                                     _stream(x))
+    check(st, "mgemm_fwd_swiglu_gu")
+    return out
+
+
+def dgrad_swiglu(dy: torch.Tensor, w2: torch.Tensor, gu: torch.Tensor, offsets: torch.Tensor,
+                 max_m_per_e: int = 0, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Down-projection input gradient fused with the SwiGLU backward.
+
+    dy bf16 [M, N], w2 bf16 [E, N, I] (the down weights), gu bf16 [M, 2I] (the
+    saved pre-activation g | u).  Returns dgu bf16 [M, 2I]: with
+    dh = dy[i] @ w2[e], dgu[i, j] = dh u silu'(g), dgu[i, I + j] = dh silu(g)."""
+    _need(dy, "dy", torch.bfloat16, 2)
+    _need(w2, "w2", torch.bfloat16, 3)
+    _need(gu, "gu", torch.bfloat16, 2)
+    M, N = dy.shape
+    E, N2, I = w2.shape
+    if N2 != N:
+        raise ValueError(f"dy is [M, {N}] but w2 is [E, {N2}, I]")
+    if tuple(gu.shape) != (M, 2 * I):
+        raise ValueError(f"gu must be [{M}, {2 * I}]")
+    _offsets(offsets, E, dy.device)
+    if out is None:
+        out = torch.empty((M, 2 * I), dtype=torch.bfloat16, device=dy.device)
+    else:
+        _need(out, "out", torch.bfloat16, 2)
+        if tuple(out.shape) != (M, 2 * I):
+            raise ValueError(f"out must be [{M}, {2 * I}]")
+    with torch.cuda.device(dy.device):
+        st = LIB.mgemm_dgrad_swiglu(dy.data_ptr(), w2.data_ptr(), gu.data_ptr(),
+                                    offsets.data_ptr(), out.data_ptr(), M, N, I, E,
+                                    int(max_m_per_e), _stream(dy))
+    check(st, "mgemm_dgrad_swiglu")
     return out
 
 

@@ -20,6 +20,9 @@ SIGNATURES = {
     "mgemm_dgrad": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i64, _vp]),
     "kgemm_wgrad": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp]),
     "mgemm_fwd_swiglu": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32, _i64, _vp]),
+    "mgemm_fwd_swiglu_gu": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32, _i64,
+                                   _vp]),
+    "mgemm_dgrad_swiglu": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i64, _vp]),
     "mgemm_list": (_i32, [_vp, _i32, _vp]),
     "mgemm_fwd_mx": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i64, _vp]),
     "mg_mx_scales_blocked": (_i32, [_vp, _vp, _i64, _i64, _i64, _vp]),

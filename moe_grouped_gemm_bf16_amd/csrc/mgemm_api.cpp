@@ -122,9 +122,10 @@ mg_status mgemm_dgrad(const void* dy, const void* w, const int32_t* offsets, voi
   return mgrouped(mg::kDgrad, dy, w, offsets, dx, M, N, K, E, max_m_per_e, stream);
 }
 
-mg_status mgemm_fwd_swiglu(const void* x, const int32_t* gather, const void* w13,
-                           const int32_t* offsets, void* h, int64_t M, int64_t T, int64_t I,
-                           int64_t K, int32_t E, int64_t max_m_per_e, void* stream) {
+mg_status mgemm_fwd_swiglu_gu(const void* x, const int32_t* gather, const void* w13,
+                              const int32_t* offsets, void* h, void* gu, int64_t M, int64_t T,
+                              int64_t I, int64_t K, int32_t E, int64_t max_m_per_e,
+                              void* stream) {
   mg_status st = check_sizes(M, 2 * I, K, E);
   if (st != MG_OK) return st;
   if (max_m_per_e < 0 || I < 0 || (I & 7)) return MG_ERR_SHAPE;   // h rows 16-byte aligned
@@ -135,7 +136,7 @@ mg_status mgemm_fwd_swiglu(const void* x, const int32_t* gather, const void* w13
   if (((M + 255) / 256 + E) * ((I + 127) / 128) > kMaxRows) return MG_ERR_SHAPE;
   if (M == 0 || I == 0) return MG_OK;
   if (!offsets || !h || (K > 0 && (!x || !w13))) return MG_ERR_NULL;
-  if ((K > 0 && (!aligned16(x) || !aligned16(w13))) || !aligned16(h) ||
+  if ((K > 0 && (!aligned16(x) || !aligned16(w13))) || !aligned16(h) || !aligned16(gu) ||
       (reinterpret_cast<uintptr_t>(offsets) & 3u) || (reinterpret_cast<uintptr_t>(gather) & 3u))
     return MG_ERR_ALIGN;
   if ((st = check_device()) != MG_OK) return st;
@@ -146,11 +147,45 @@ mg_status mgemm_fwd_swiglu(const void* x, const int32_t* gather, const void* w13
   a.q_src = x;
   a.offsets = offsets;
   a.out = h;
+  a.aux = gu;
   a.M = M; a.N = 2 * I; a.K = K; a.E = E;
   a.accumulate = 0;
   a.gather = gather;
   a.T = gather != nullptr ? T : M;
   return launch(mg::kFwdSwiglu, a, max_m_per_e, s);
+}
+
+mg_status mgemm_fwd_swiglu(const void* x, const int32_t* gather, const void* w13,
+                           const int32_t* offsets, void* h, int64_t M, int64_t T, int64_t I,
+                           int64_t K, int32_t E, int64_t max_m_per_e, void* stream) {
+  return mgemm_fwd_swiglu_gu(x, gather, w13, offsets, h, nullptr, M, T, I, K, E, max_m_per_e,
+                             stream);
+}
+
+mg_status mgemm_dgrad_swiglu(const void* dy, const void* w2, const void* gu,
+                             const int32_t* offsets, void* dgu, int64_t M, int64_t N, int64_t I,
+                             int32_t E, int64_t max_m_per_e, void* stream) {
+  mg_status st = check_sizes(M, N, I, E);      // the down projection: K = I
+  if (st != MG_OK) return st;
+  if (max_m_per_e < 0) return MG_ERR_SHAPE;
+  if (((M + 255) / 256 + E) * ((I + 255) / 256) > kMaxRows) return MG_ERR_SHAPE;
+  if (M == 0 || I == 0) return MG_OK;
+  if (!offsets || !dgu || !gu || (N > 0 && (!dy || !w2))) return MG_ERR_NULL;
+  if ((N > 0 && (!aligned16(dy) || !aligned16(w2))) || !aligned16(gu) || !aligned16(dgu) ||
+      (reinterpret_cast<uintptr_t>(offsets) & 3u))
+    return MG_ERR_ALIGN;
+  if ((st = check_device()) != MG_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = maybe_validate(offsets, E, M, s)) != MG_OK) return st;
+  mg::KernelArgs a{};
+  a.p_src = w2;
+  a.q_src = dy;
+  a.offsets = offsets;
+  a.out = dgu;
+  a.aux = const_cast<void*>(gu);
+  a.M = M; a.N = N; a.K = I; a.E = E;
+  a.accumulate = 0;
+  return launch(mg::kDgradSwiglu, a, max_m_per_e, s);
 }
 
 mg_status mgemm_list(const mg_gemm_desc* desc, int32_t G, void* stream) {

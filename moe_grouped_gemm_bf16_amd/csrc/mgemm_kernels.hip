@@ -21,6 +21,10 @@
 //   FWD_MX   as FWD, with E4M3 operands and one E8M0 scale per 32 k (MXFP8;
 //            torchao PR #3416): the same 128-byte staged rows hold 128 k, and
 //            the scaled fp8 matrix-core product applies the scales
+//   DGRAD_SWIGLU as DGRAD (down projection: dH = dY W2[e]), the epilogue applying
+//            the SwiGLU backward on the saved pre-activation g | u: dg = dh u
+//            silu'(g), du = dh silu(g) (DeepGEMM issue #10: a kernel fused with
+//            SwiGLU is part of a weight-gradient path)
 //   WGRAD_MX K-grouped like WGRAD, on E4M3 operands quantized along the
 //            tokens and stored token axis last: P = k from X^T [k][i],
 //            Q = n from dY^T [n][i], R = i (both R-contiguous, as FWD_MX)
@@ -837,7 +841,8 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
   constexpr bool LIST = MODE == kList;
   constexpr bool MX = MODE == kFwdMx || MODE == kWgradMx;
   constexpr bool KG = MODE == kWgrad || MODE == kWgradMx;   // K-grouped, fp32 out
-  constexpr bool P_RS = MODE == kDgrad || MODE == kWgrad;   // P is R-strided for dgrad and wgrad
+  constexpr bool DG = MODE == kDgrad || MODE == kDgradSwiglu;
+  constexpr bool P_RS = DG || MODE == kWgrad;   // P is R-strided for dgrad and wgrad
   constexpr bool Q_RS = MODE == kWgrad;    // Q is R-strided for wgrad
   constexpr int SPW = C::SEGS_PER_WAVE;
   // element bytes, and reduction steps per stage (a staged row is kRowB bytes)
@@ -849,7 +854,7 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
   int ldP, ldQ;
   if (MODE == kWgradMx) { ldP = (int)a.M; ldQ = (int)a.M; }   // X^T, dY^T rows of M tokens
   else if (MODE == kFwd || SWI || LIST || MX) { ldP = (int)a.K; ldQ = (int)a.K; }   // LIST: per tile
-  else if (MODE == kDgrad) { ldP = (int)a.K; ldQ = (int)a.N; }
+  else if (DG) { ldP = (int)a.K; ldQ = (int)a.N; }
   else { ldP = (int)a.K; ldQ = (int)a.N; }
 
   // ---- direct-to-LDS plan: each stage is C::SEGS 1-KiB segments (the P tile
@@ -929,7 +934,7 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
       const ListDesc dg = list_desc(S.list, t.e);
       P = reinterpret_cast<const char*>(dg.b) + (int64_t)t.p0 * dg.ldb * 2;
       Q = reinterpret_cast<const char*>(dg.a) + (int64_t)t.q0 * dg.lda * 2;
-    } else if (MODE == kDgrad) {   // P = W[e] [n][k] R-strided, Q = dY rows m (R = n)
+    } else if (DG) {               // P = W[e] [n][k] R-strided, Q = dY rows m (R = n)
       P += ((int64_t)t.e * a.N * a.K + t.p0) * 2;
       Q += (int64_t)t.q0 * a.N * 2;
     } else {                       // P = X [i][k] R-strided, Q = dY [i][n] R-strided
@@ -1400,7 +1405,74 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
     }
     return h;
   };
+  // SwiGLU backward on result block (i, j) (dh, fp32): the lanes are regrouped
+  // as for the bf16 store, but on the fp32 values, so that each lane holds 8
+  // consecutive columns of two rows; it loads those columns of g and u (16
+  // bytes each) and stores dg and du.
+  auto store_dswiglu = [&](const Tile& t, int i, int j, const f32x16& blk) {
+    const int I = (int)a.K;
+    uint32_t v[4][4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float f = blk[4 * g + e];
+        v[g][e] = __builtin_bit_cast(uint32_t, f);
+      }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      swap16(v[0][e], v[2][e]);
+      swap16(v[1][e], v[3][e]);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      swap32(v[0][e], v[1][e]);
+      swap32(v[2][e], v[3][e]);
+    }
+    const int c = 4 * pa + 2 * pb;
+    const int m0 = t.q0 + wq * C::WTQ + j * 32 + l16;
+    const int col = t.p0 + wp * C::WTP + i * 32 + 4 * c;
+    if (col >= I) return;
+    const uint16_t* gu = reinterpret_cast<const uint16_t*>(a.aux);
+    uint16_t* dgu = reinterpret_cast<uint16_t*>(a.out);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int m = m0 + 16 * half;
+      if (m >= t.q_end) continue;
+      const int64_t row = (int64_t)m * (2 * I);
+      const u32x4 gw = *reinterpret_cast<const u32x4*>(gu + row + col);
+      const u32x4 uw = *reinterpret_cast<const u32x4*>(gu + row + I + col);
+      u32x4 dg, du;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        // columns 2q, 2q + 1: fp32 dh from v[2 half + q / 2][2 (q % 2) + 0..1]
+        const float dh0 = __builtin_bit_cast(float, v[2 * half + q / 2][2 * (q % 2)]);
+        const float dh1 = __builtin_bit_cast(float, v[2 * half + q / 2][2 * (q % 2) + 1]);
+        const float g0 = __builtin_bit_cast(float, gw[q] << 16);
+        const float g1 = __builtin_bit_cast(float, gw[q] & 0xFFFF0000u);
+        const float u0 = __builtin_bit_cast(float, uw[q] << 16);
+        const float u1 = __builtin_bit_cast(float, uw[q] & 0xFFFF0000u);
+        const float s0 = 1.0f / (1.0f + __builtin_amdgcn_exp2f(-g0 * 1.4426950408889634f));
+        const float s1 = 1.0f / (1.0f + __builtin_amdgcn_exp2f(-g1 * 1.4426950408889634f));
+        const bf16x2 a2 = __builtin_convertvector(
+            (f32x2){dh0 * u0 * (s0 * (1.0f + g0 * (1.0f - s0))), dh1 * u1 * (s1 * (1.0f + g1 * (1.0f - s1)))},
+            bf16x2);
+        const bf16x2 b2 = __builtin_convertvector((f32x2){dh0 * (g0 * s0), dh1 * (g1 * s1)}, bf16x2);
+        dg[q] = __builtin_bit_cast(uint32_t, a2);
+        du[q] = __builtin_bit_cast(uint32_t, b2);
+      }
+      *reinterpret_cast<u32x4*>(dgu + row + col) = dg;
+      *reinterpret_cast<u32x4*>(dgu + row + I + col) = du;
+    }
+  };
   auto store_tile = [&](const Tile& t) {
+    if (MODE == kDgradSwiglu) {
+#pragma unroll
+      for (int j = 0; j < C::MQ; ++j)
+#pragma unroll
+        for (int i = 0; i < C::MP; ++i) store_dswiglu(t, i, j, acc[i][j]);
+      return;
+    }
     if (KG && a.accumulate && t.r_end <= t.r_begin) return;   // adds nothing
     const OutView ov = out_view(t);
     if (SWI) {
@@ -1409,6 +1481,19 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
 #pragma unroll
         for (int i = 0; i < C::MP / 2; ++i)
           store_block(t, ov, i, j, swiglu(acc[i][j], acc[i + C::MP / 2][j]));
+      if (a.aux != nullptr) {
+        // the pre-activation g | u for the backward: gu [M, 2I]
+        const int I2 = Pdim;
+        const OutView og = {reinterpret_cast<uint16_t*>(a.aux), 2 * I2, I2};
+        const OutView ou = {reinterpret_cast<uint16_t*>(a.aux) + I2, 2 * I2, I2};
+#pragma unroll
+        for (int j = 0; j < C::MQ; ++j)
+#pragma unroll
+          for (int i = 0; i < C::MP / 2; ++i) {
+            store_block(t, og, i, j, acc[i][j]);
+            store_block(t, ou, i, j, acc[i + C::MP / 2][j]);
+          }
+      }
       return;
     }
 #pragma unroll
@@ -1604,7 +1689,7 @@ void grouped_gemm_kernel(KernelArgs a) {
     Pdim = (int)(a.N / 2); Qdim = (int)a.M;      // outputs: I = N / 2 columns
   } else if (MODE == kList) {
     Pdim = 0; Qdim = 0;                          // per group, from the descriptors
-  } else if (MODE == kDgrad) {
+  } else if (MODE == kDgrad || MODE == kDgradSwiglu) {
     Pdim = (int)a.K; Qdim = (int)a.M;
   } else {
     Pdim = (int)a.K; Qdim = (int)a.N;
@@ -1774,6 +1859,9 @@ int launch_grouped(int mode, const KernelArgs& a_in, int64_t max_m_per_e, hipStr
       break;
     case kWgradMx:
       hipLaunchKernelGGL((grouped_gemm_kernel<kWgradMx, CfgMx>), g, dim3(CfgMx::NT), 0, s, a);
+      break;
+    case kDgradSwiglu:
+      hipLaunchKernelGGL((grouped_gemm_kernel<kDgradSwiglu, Cfg>), g, b, 0, s, a);
       break;
     default: hipLaunchKernelGGL((grouped_gemm_kernel<kWgrad, Cfg>), g, b, 0, s, a); break;
   }

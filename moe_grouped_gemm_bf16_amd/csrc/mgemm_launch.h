@@ -5,7 +5,8 @@
 
 namespace mg {
 
-enum { kFwd = 0, kDgrad = 1, kWgrad = 2, kFwdSwiglu = 3, kList = 4, kFwdMx = 5, kWgradMx = 6 };
+enum { kFwd = 0, kDgrad = 1, kWgrad = 2, kFwdSwiglu = 3, kList = 4, kFwdMx = 5, kWgradMx = 6,
+       kDgradSwiglu = 7 };
 
 // Largest expert count a launch accepts: the device-side scheduler keeps the
 // per-expert tile prefix in LDS, two entries per thread of a 512-thread block.
@@ -28,6 +29,7 @@ struct KernelArgs {
                             // FWD_MX: X8 [M,K] E4M3 codes; WGRAD_MX: dY^T [N,M] E4M3 codes
   const int32_t* offsets;   // [E+1], device
   void* out;                // FWD: Y [M,N] bf16; FWD_SWIGLU: H [M,N/2] bf16; DGRAD: dX [M,K] bf16;
+                            // DGRAD_SWIGLU: dGU [M,2K] bf16 (dg | du);
                             // WGRAD, WGRAD_MX: dW [E,N,K] fp32
   int64_t M, N, K;
   int32_t E;
@@ -41,6 +43,8 @@ struct KernelArgs {
                             // WGRAD_MX: X^T's, blocked [M/128][K][4]
   const uint8_t* q_scale;   // FWD_MX: X's E8M0 scales, blocked [ceil(K/128)][M][4];
                             // WGRAD_MX: dY^T's, blocked [M/128][N][4]
+  void* aux;                // FWD_SWIGLU: optional gu [M, N] bf16 out (pre-activation g | u);
+                            // DGRAD_SWIGLU: gu [M, 2K] bf16 in
 };
 
 // Rearrange E8M0 scales [batch][rows][K/32] into the blocked layout
