@@ -140,6 +140,25 @@ def test_wgrad_mx_argument_errors():
     assert f(None, None, None, None, None, None, 512, 0, 256, 4, 0, None) == OK   # empty dw
 
 
+def test_swiglu_backward_and_saving_forward_argument_errors():
+    f = L.mgemm_dgrad_swiglu
+    # (dy, w2, gu, offsets, dgu, M, N, I, E, max_m_per_e, stream)
+    assert f(A, A, A, A, A, 512, 256, 128, 0, 0, None) == SHAPE          # E < 1
+    assert f(A, A, A, A, A, 512, 250, 128, 4, 0, None) == SHAPE          # N % 8
+    assert f(A, A, A, A, A, 512, 256, 100, 4, 0, None) == SHAPE          # I % 8
+    assert f(A, A, A, A, A, 512, 256, 128, 4, -1, None) == SHAPE         # bad hint
+    assert f(A, A, None, A, A, 512, 256, 128, 4, 0, None) == NUL          # gu
+    assert f(A, A, A, A, None, 512, 256, 128, 4, 0, None) == NUL          # dgu
+    assert f(A, A, A + 8, A, A, 512, 256, 128, 4, 0, None) == ALIGN
+    assert f(A, A, A, A, A + 8, 512, 256, 128, 4, 0, None) == ALIGN
+    assert f(None, None, None, None, None, 0, 256, 128, 4, 0, None) == OK
+    g = L.mgemm_fwd_swiglu_gu
+    # (x, gather, w13, offsets, h, gu, M, T, I, K, E, max_m_per_e, stream)
+    assert g(A, None, A, A, A, A, 512, 0, 100, 256, 4, 0, None) == SHAPE   # I % 8
+    assert g(A, None, A, A, A, A + 8, 512, 0, 128, 256, 4, 0, None) == ALIGN
+    assert g(A, None, A, A, A, None, 0, 0, 128, 256, 4, 0, None) == OK
+
+
 def test_python_binding_rejects_bad_tensors_on_host():
     torch = pytest.importorskip("torch")
     import moe_grouped_gemm_bf16_amd as mg
