@@ -38,7 +38,7 @@ KERNEL_SRC = os.path.join(ROOT, "moe_grouped_gemm_bf16_amd", "csrc", "mgemm_kern
 KERNEL_NAMES = {"fwd": "grouped_gemm_kernel<0>", "dgrad": "grouped_gemm_kernel<1>",
                 "wgrad": "grouped_gemm_kernel<2>", "fwd_swiglu": "grouped_gemm_kernel<3>",
                 "list": "grouped_gemm_kernel<4>", "fwd_mx": "grouped_gemm_kernel<5>",
-                "wgrad_mx": "grouped_gemm_kernel<6>"}
+                "wgrad_mx": "grouped_gemm_kernel<6>", "dgrad_swiglu": "grouped_gemm_kernel<7>"}
 
 
 def kernel_hash() -> str:
@@ -241,11 +241,59 @@ def fusions(torch, mg, reps=20):
     tf = statistics.median(p[0][0].elapsed_time(p[0][1]) for p in ev) * 1e3
     tu = statistics.median(p[1][0].elapsed_time(p[1][1]) for p in ev) * 1e3
     flops = 2 * M * (2 * I) * K
-    return {"fwd_swiglu_gathered:a3b_gate_up": {
+    out = {"fwd_swiglu_gathered:a3b_gate_up": {
         "rows": M, "tokens": T, "fused_us": round(tf, 1), "tflops": round(flops / tf / 1e6, 1),
         "pct_peak": round(100 * flops / tf / 1e6 / PEAK_BF16_TFLOPS, 1),
         "unfused_us": round(tu, 1), "speedup": round(tu / tf, 3),
         "unfused": "torch index_select + mgemm_fwd [M, 2560] + torch silu(g) * u"}}
+
+    # the backward through the down projection: dh = dy W2[e] with the SwiGLU
+    # backward fused (dgu [M, 2I]) against mgemm_dgrad to dh and the same
+    # activation backward in torch; and the fused forward saving g | u
+    (wd,) = [w for w in make_workload(4) if w.name == "a3b_down"]
+    N = wd.N
+    dy = up(normal_bf16_bits((M, N), 1.0, 4, 9, 2))
+    w2 = up(wd.w_bits())
+    gu = torch.empty((M, 2 * I), dtype=torch.bfloat16, device="cuda")
+    mg.fwd_swiglu(x, w13, off, gather=gi, max_m_per_e=hint, out=h, gu_out=gu)
+    dgu = torch.empty_like(gu)
+    dh = torch.empty((M, I), dtype=torch.bfloat16, device="cuda")
+
+    def bfused():
+        mg.dgrad_swiglu(dy, w2, gu, off, hint, out=dgu)
+
+    def bunfused():
+        mg.dgrad(dy, w2, off, hint, out=dh)
+        g = gu[:, :I].float(); u = gu[:, I:].float(); d = dh.float()
+        sg = torch.sigmoid(g)
+        torch.cat([d * u * sg * (1 + g * (1 - sg)), d * g * sg], dim=1).to(torch.bfloat16)
+
+    def fsave():
+        mg.fwd_swiglu(x, w13, off, gather=gi, max_m_per_e=hint, out=h, gu_out=gu)
+
+    pairs = (("dgrad_swiglu:a3b_down", bfused, bunfused, 2 * M * N * I,
+              "mgemm_dgrad to dh [M, 1280] + torch SwiGLU backward"),
+             ("fwd_swiglu_saving_gu:a3b_gate_up", fsave, fused, flops,
+              "the same fused forward without saving g | u"))
+    for name, fa, fb, fl, what in pairs:
+        for _ in range(5):
+            fa(); fb()
+        torch.cuda.synchronize()
+        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(2)] for _ in range(reps)]
+        for pair in ev:
+            for (a, b), fn in zip(pair, (fa, fb)):
+                a.record()
+                fn()
+                b.record()
+        torch.cuda.synchronize()
+        ta = statistics.median(p[0][0].elapsed_time(p[0][1]) for p in ev) * 1e3
+        tb = statistics.median(p[1][0].elapsed_time(p[1][1]) for p in ev) * 1e3
+        out[name] = {"fused_us": round(ta, 1), "tflops": round(fl / ta / 1e6, 1),
+                     "pct_peak": round(100 * fl / ta / 1e6 / PEAK_BF16_TFLOPS, 1),
+                     "reference_us": round(tb, 1), "ratio": round(tb / ta, 3),
+                     "reference": what}
+    return out
 
 
 # -------------------------------------------------------------------- lists --
