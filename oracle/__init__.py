@@ -25,6 +25,9 @@ per expert; nothing blocked, fused or reordered):
     gradient), then the SwiGLU backward dg = dh u silu'(g), du = dh silu(g) on
     the saved pre-activation g | u (the DeepGEMM issue #10 thread: a kernel
     fused with SwiGLU is part of a weight-gradient path).
+  * The token-order combine that inverts the gather: out[t] = sum_j w[t, j]
+    rows[token_rows[t, j]] (the backward of the dispatch gather, or the
+    layer's weighted output combine).
   * A list of independent GEMMs D_g = A_g B_g^T with per-group shapes (the
     TransformerEngine PR #2045 review: one C API over lists of tensors; the
     CUTLASS discussion #1452: nested grouped GEMMs flattened into one list).
@@ -46,7 +49,8 @@ brute force with math.exp, one-hot closed forms that tell the gate half from
 the up half, gather-as-permutation identities, and a gate that rejects a wrong
 expert or a dropped term; for the SwiGLU backward, central finite
 differences of silu(g) u and the chain-rule identity <dgu, [dg0, du0]> =
-<dh, d(silu(g) u)> for a perturbation; for the descriptor list, exact rational brute force on
+<dh, d(silu(g) u)> for a perturbation; for the combine, the adjoint identity
+with the gather (<combine(R), X> = <R, X[gather]>) and a plain loop; for the descriptor list, exact rational brute force on
 groups of mixed shapes (empty and zero-reduction ones included), a one-hot
 transpose check and the flattened LoRA x experts identity; for MXFP8, the
 element and scale decoders against torch's float8_e4m3fn / float8_e8m0fnu
@@ -70,6 +74,7 @@ from .grouped_gemm import (  # noqa: F401
     sample_fwd_swiglu,
     grouped_dgrad_swiglu,
     sample_dgrad_swiglu,
+    moe_combine,
     grouped_list,
 )
 from .mx import (  # noqa: F401

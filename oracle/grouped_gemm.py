@@ -229,3 +229,24 @@ def sample_wgrad(dy: np.ndarray, x: np.ndarray, offsets, experts, ns, ks):
         p = _f64(dy[lo:hi, n]) * _f64(x[lo:hi, k])
         val[j] = p.sum(); mag[j] = np.abs(p).sum()
     return val, mag
+
+
+def moe_combine(rows: np.ndarray, token_rows, weights=None) -> np.ndarray:
+    """Token-order sum of routed rows (fp64): the inverse of the gather.
+
+    The forward reads token t's activations into the rows i with gather[i] = t
+    (one per routed expert, the MoE layout of the DeepGEMM issue #10 thread);
+    the backward of that gather sums those rows' gradients back per token, and
+    the output combine of the layer sums the experts' outputs per token with
+    the router's weights.  token_rows int [T, k]: the rows of token t (-1 =
+    none); weights [T, k] or None (all 1):
+        out[t, :] = sum_j weights[t, j] rows[token_rows[t, j], :]."""
+    tr = np.asarray(token_rows, dtype=np.int64)
+    T, k = tr.shape
+    D = rows.shape[1]
+    w = np.ones((T, k)) if weights is None else np.asarray(weights, np.float64)
+    out = np.zeros((T, D))
+    for j in range(k):
+        ok = tr[:, j] >= 0
+        out[ok] += w[ok, j][:, None] * np.asarray(rows, np.float64)[tr[ok, j]]
+    return out

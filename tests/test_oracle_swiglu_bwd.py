@@ -100,3 +100,44 @@ def test_sampler_and_gate():
     assert not oracle.check_bf16_factor(swapped, dgu, fac, S2, N).passed
     wrong = oracle.grouped_dgrad_swiglu(dy, w2[[2, 1, 0]], gu, off)[0]
     assert oracle.check_bf16_factor(f64_to_bf16_bits(wrong), dgu, fac, S2, N).fails > 0.8 * dgu[:40].size
+
+
+# ---------------------------------------------------------------- combine --
+
+def _router_maps(T, k, M_rows, seed):
+    """A gather index (row -> token) with k rows per token, and its inverse."""
+    rng = np.random.default_rng(seed)
+    gather = np.repeat(np.arange(T), k)
+    perm = rng.permutation(T * k)[:M_rows]
+    gather = gather[perm]
+    token_rows = -np.ones((T, k), np.int64)
+    fill = np.zeros(T, np.int64)
+    for i, t in enumerate(gather):
+        token_rows[t, fill[t]] = i
+        fill[t] += 1
+    return gather, token_rows
+
+
+def test_combine_is_the_adjoint_of_the_gather():
+    """<combine(R), X> = <R, X[gather]>: the combine is the backward of the gather."""
+    rng = np.random.default_rng(10)
+    T, k, D = 50, 4, 24
+    gather, token_rows = _router_maps(T, k, 170, 11)      # some tokens keep fewer than k rows
+    R = rng.standard_normal((len(gather), D))
+    X = rng.standard_normal((T, D))
+    lhs = float((oracle.moe_combine(R, token_rows) * X).sum())
+    rhs = float((R * X[gather]).sum())
+    assert abs(lhs - rhs) <= 1e-12 * np.abs(R).sum() * np.abs(X).max()
+
+
+def test_combine_plain_loop_with_weights():
+    rng = np.random.default_rng(12)
+    T, k, D = 7, 3, 5
+    gather, token_rows = _router_maps(T, k, 18, 13)
+    R = rng.standard_normal((len(gather), D))
+    w = rng.random((T, k))
+    out = oracle.moe_combine(R, token_rows, w)
+    for t in range(T):
+        for d in range(D):
+            ref = sum(w[t, j] * R[token_rows[t, j], d] for j in range(k) if token_rows[t, j] >= 0)
+            assert math.isclose(out[t, d], ref, rel_tol=1e-13, abs_tol=1e-15)
