@@ -293,6 +293,36 @@ def fusions(torch, mg, reps=20):
                      "pct_peak": round(100 * fl / ta / 1e6 / PEAK_BF16_TFLOPS, 1),
                      "reference_us": round(tb, 1), "ratio": round(tb / ta, 3),
                      "reference": what}
+    # the token-order combine (the gather's inverse): the gate-up input gradient
+    # rows [M, 3072] summed back per token, unweighted and with router weights;
+    # HBM-bound, reported against the 8 TB/s roofline
+    tr = -np.ones((T, 8), np.int32)
+    fill = np.zeros(T, np.int64)
+    for i, t in enumerate(tok):
+        tr[t, fill[t]] = i
+        fill[t] += 1
+    trd = torch.from_numpy(tr).cuda()
+    wts = torch.rand((T, 8), device="cuda")
+    rows = up(normal_bf16_bits((M, K), 1.0, 4, 9, 3))
+    xo = torch.empty((T, K), dtype=torch.bfloat16, device="cuda")
+    for name, fn, extra in (("moe_combine:a3b_dx", lambda: mg.moe_combine(rows, trd, out=xo), 0),
+                            ("moe_combine_weighted:a3b_y",
+                             lambda: mg.moe_combine(rows, trd, wts, out=xo), T * 8 * 4)):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        tc = statistics.median(a.elapsed_time(b) for a, b in ev) * 1e3
+        nbytes = M * K * 2 + T * 8 * 4 + T * K * 2 + extra
+        out[name] = {"us": round(tc, 1), "algo_GBps": round(nbytes / tc / 1e3, 1),
+                     "pct_hbm": round(100 * nbytes / tc / 1e3 / PEAK_HBM_GBS, 1),
+                     "rows": M, "tokens": T}
     return out
 
 

@@ -134,6 +134,20 @@ mg_status mgemm_dgrad_swiglu(const void* dy, const void* w2, const void* gu,
                              const int32_t* offsets, void* dgu, int64_t M, int64_t N, int64_t I,
                              int32_t E, int64_t max_m_per_e, void* stream);
 
+/* Token-order combine of routed rows, the inverse of the gather of
+ * mgemm_fwd_swiglu (the MoE layout of the DeepGEMM issue #10 thread): the
+ * backward of the dispatch gather sums each token's row gradients, the
+ * layer's output combine sums its experts' outputs with the router weights:
+ *   out[t, :] = sum_{j < k} weights[t, j] rows[token_rows[t, j], :]
+ * rows: bf16 [M, D]; token_rows: int32 [T, k] DEVICE array, entry -1 (or any
+ * index outside [0, M)) = no row; weights: fp32 [T, k] DEVICE or NULL (all
+ * 1); out: bf16 [T, D] (written; must not overlap rows).  fp32 accumulation in
+ * ascending j (bitwise reproducible), one rounding to nearest even.  D a
+ * multiple of 8, 1 <= k <= 64; rows and out 16-byte aligned, token_rows and
+ * weights 4-byte aligned.  T == 0 or D == 0 is a no-op.  Allocates nothing. */
+mg_status mg_moe_combine(const void* rows, const int32_t* token_rows, const float* weights,
+                         void* out, int64_t M, int64_t T, int32_t k, int64_t D, void* stream);
+
 /* One group of mgemm_list: D [m, n] = A [m, k] B [n, k]^T (bf16 in and out,
  * fp32 accumulation, round to nearest even), row-major with row strides in
  * elements.  All three pointers are DEVICE pointers, 16-byte aligned; k, n and

@@ -368,6 +368,37 @@ def wgrad_mx(dyt8: torch.Tensor, dyt_scale: torch.Tensor, xt8: torch.Tensor,
     return out
 
 
+def moe_combine(rows: torch.Tensor, token_rows: torch.Tensor,
+                weights: torch.Tensor | None = None, out: torch.Tensor | None = None
+                ) -> torch.Tensor:
+    """out[t] = sum_j weights[t, j] rows[token_rows[t, j]] (bf16 [T, D]).
+
+    rows bf16 [M, D]; token_rows int32 [T, k] (-1 = no row); weights fp32
+    [T, k] or None (all 1).  The backward of the row gather of fwd_swiglu, or
+    the layer's weighted output combine."""
+    _need(rows, "rows", torch.bfloat16, 2)
+    _need(token_rows, "token_rows", torch.int32, 2)
+    M, D = rows.shape
+    T, k = token_rows.shape
+    wptr = 0
+    if weights is not None:
+        _need(weights, "weights", torch.float32, 2)
+        if tuple(weights.shape) != (T, k):
+            raise ValueError(f"weights must be [{T}, {k}]")
+        wptr = weights.data_ptr()
+    if out is None:
+        out = torch.empty((T, D), dtype=torch.bfloat16, device=rows.device)
+    else:
+        _need(out, "out", torch.bfloat16, 2)
+        if tuple(out.shape) != (T, D):
+            raise ValueError(f"out must be [{T}, {D}]")
+    with torch.cuda.device(rows.device):
+        st = LIB.mg_moe_combine(rows.data_ptr(), token_rows.data_ptr(), wptr, out.data_ptr(),
+                                M, T, k, D, _stream(rows))
+    check(st, "mg_moe_combine")
+    return out
+
+
 def Mgemm(x: torch.Tensor, w: torch.Tensor, cnt: torch.Tensor, max_M_per_E: int = 0,
           transpose_B: bool = True) -> torch.Tensor:
     """RapidGEMM-shaped M-grouped GEMM (README, "Kernels").

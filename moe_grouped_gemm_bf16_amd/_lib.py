@@ -23,6 +23,7 @@ SIGNATURES = {
     "mgemm_fwd_swiglu_gu": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32, _i64,
                                    _vp]),
     "mgemm_dgrad_swiglu": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i64, _vp]),
+    "mg_moe_combine": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _i64, _vp]),
     "mgemm_list": (_i32, [_vp, _i32, _vp]),
     "mgemm_fwd_mx": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i64, _vp]),
     "mg_mx_scales_blocked": (_i32, [_vp, _vp, _i64, _i64, _i64, _vp]),

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmgemm.so")
-SOURCES = ["mgemm_kernels.hip", "mgemm_api.cpp"]
+SOURCES = ["mgemm_kernels.hip", "mgemm_combine.hip", "mgemm_api.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

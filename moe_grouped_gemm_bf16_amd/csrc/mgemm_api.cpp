@@ -278,6 +278,25 @@ mg_status kgemm_wgrad_mx(const void* dyt, const void* dyt_scale, const void* xt,
   return launch(mg::kWgradMx, a, 0, s);
 }
 
+mg_status mg_moe_combine(const void* rows, const int32_t* token_rows, const float* weights,
+                         void* out, int64_t M, int64_t T, int32_t k, int64_t D, void* stream) {
+  if (M < 0 || T < 0 || D < 0 || k < 1 || k > 64 || (D & 7) || M > kMaxRows || T > kMaxRows ||
+      D > kMaxDim)
+    return MG_ERR_SHAPE;
+  if (T == 0 || D == 0) return MG_OK;
+  if (!token_rows || !out || (M > 0 && !rows)) return MG_ERR_NULL;
+  if ((M > 0 && !aligned16(rows)) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(token_rows) & 3u) ||
+      (reinterpret_cast<uintptr_t>(weights) & 3u))
+    return MG_ERR_ALIGN;
+  mg_status st;
+  if ((st = check_device()) != MG_OK) return st;
+  const int err = mg::launch_moe_combine(static_cast<const uint16_t*>(rows), token_rows, weights,
+                                         static_cast<uint16_t*>(out), M, T, k, D,
+                                         static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? MG_OK : MG_ERR_LAUNCH;
+}
+
 mg_status mg_mx_scales_blocked(const void* scales, void* blocked, int64_t rows, int64_t K,
                                int64_t batch, void* stream) {
   if (rows < 0 || K < 0 || batch < 0 || (K & 31) || rows > kMaxRows || K > kMaxDim ||

@@ -47,6 +47,12 @@ struct KernelArgs {
                             // DGRAD_SWIGLU: gu [M, 2K] bf16 in
 };
 
+// Token-order combine: out[t, :] = sum_j w[t, j] rows[token_rows[t, j], :]
+// (bf16 rows [M, D], token_rows int32 [T, k], weights fp32 [T, k] or NULL, out
+// bf16 [T, D]).  Returns a hipError_t value.
+int launch_moe_combine(const uint16_t* rows, const int32_t* token_rows, const float* weights,
+                       uint16_t* out, int64_t M, int64_t T, int32_t k, int64_t D, hipStream_t s);
+
 // Rearrange E8M0 scales [batch][rows][K/32] into the blocked layout
 // [batch][ceil(K/128)][rows][4] (absent blocks 127).  Returns a hipError_t value.
 int launch_mx_scales_blocked(const uint8_t* src, uint8_t* dst, int64_t rows, int64_t K,

@@ -159,6 +159,21 @@ def test_swiglu_backward_and_saving_forward_argument_errors():
     assert g(A, None, A, A, A, None, 0, 0, 128, 256, 4, 0, None) == OK
 
 
+def test_moe_combine_argument_errors():
+    f = L.mg_moe_combine
+    # (rows, token_rows, weights, out, M, T, k, D, stream)
+    assert f(A, A, None, A, 100, 10, 0, 64, None) == SHAPE          # k < 1
+    assert f(A, A, None, A, 100, 10, 65, 64, None) == SHAPE         # k > 64
+    assert f(A, A, None, A, 100, 10, 4, 60, None) == SHAPE          # D % 8
+    assert f(A, A, None, A, -1, 10, 4, 64, None) == SHAPE
+    assert f(A, None, None, A, 100, 10, 4, 64, None) == NUL
+    assert f(A, A, None, None, 100, 10, 4, 64, None) == NUL
+    assert f(A + 8, A, None, A, 100, 10, 4, 64, None) == ALIGN
+    assert f(A, A + 2, None, A, 100, 10, 4, 64, None) == ALIGN
+    assert f(A, A, A + 2, A, 100, 10, 4, 64, None) == ALIGN
+    assert f(None, None, None, None, 100, 0, 4, 64, None) == OK      # no tokens
+
+
 def test_python_binding_rejects_bad_tensors_on_host():
     torch = pytest.importorskip("torch")
     import moe_grouped_gemm_bf16_amd as mg

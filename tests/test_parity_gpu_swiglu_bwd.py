@@ -114,3 +114,78 @@ def test_fwd_swiglu_saves_the_plain_forward(gathered):
     y = mg.fwd(xg, w, o)
     assert (host_bits(h1) == host_bits(h2)).all()
     assert (host_bits(gu) == host_bits(y)).all()
+
+
+# ---------------------------------------------------------------- combine --
+
+from oracle import check_bf16, moe_combine  # noqa: E402
+
+
+def _inverse(tok: np.ndarray, T: int, k: int) -> np.ndarray:
+    """token -> its rows (row i carries token tok[i]), -1 padded, rows ascending."""
+    tr = -np.ones((T, k), np.int32)
+    fill = np.zeros(T, np.int64)
+    for i, t in enumerate(tok):
+        tr[t, fill[t]] = i
+        fill[t] += 1
+    return tr
+
+
+def _combine_gate(rows_bits, token_rows, weights, got_bits, sample=None):
+    tr = np.asarray(token_rows, np.int64)
+    if sample is not None:
+        tr = tr[sample]
+        got_bits = got_bits[sample]
+    used = np.unique(tr[tr >= 0])
+    remap = -np.ones(int(rows_bits.shape[0]), np.int64)
+    remap[used] = np.arange(len(used))
+    tr2 = np.where(tr >= 0, remap[np.maximum(tr, 0)], -1)
+    R = bf16_bits_to_f64(rows_bits[used])
+    w = None if weights is None else (weights if sample is None else weights[sample])
+    exact = moe_combine(R, tr2, w)
+    mag = moe_combine(np.abs(R), tr2, None if w is None else np.abs(w))
+    return check_bf16(got_bits, exact, mag, tr.shape[1])
+
+
+@pytest.mark.parametrize("weighted", [False, True])
+def test_moe_combine_small(weighted):
+    rng = np.random.default_rng(970 + weighted)
+    T, k, M, D = 100, 4, 300, 264
+    _say("moe_combine", T, k, M, D, "weighted" if weighted else "")
+    rows = normal_bf16_bits((M, D), 1.0, 970, 1)
+    tr = rng.integers(-1, M, (T, k)).astype(np.int32)     # -1: no row
+    tr[3] = -1                                             # a token with no rows at all
+    tr[5, 0] = M + 7                                       # an index out of range: skipped
+    w = rng.random((T, k)).astype(np.float32) if weighted else None
+    out = mg.moe_combine(dev_bf16(rows), dev_i32(tr),
+                         None if w is None else torch.from_numpy(w).cuda())
+    got = host_bits(out)
+    tr_ok = np.where((tr >= 0) & (tr < M), tr, -1)
+    rep = _combine_gate(rows, tr_ok, None if w is None else w.astype(np.float64), got)
+    assert rep.passed, str(rep)
+    assert (got[3] == 0).all()
+
+
+def test_moe_combine_a3b_routing():
+    """The 30B-A3B routing of one GPU's share: 16384 tokens, up to 8 local rows
+    each, D = 3072 (the gate-up input gradient back to token order), with and
+    without router weights; sampled tokens, and bitwise reproducible."""
+    from workloads.synth import router_offsets
+    off, tok = router_offsets(16384, 128, 8, 32, seed=4)
+    T, k, D = 16384, 8, 3072
+    M = int(off[-1])
+    tr = _inverse(np.asarray(tok), T, k)
+    _say("moe_combine a3b", T, k, M, D)
+    rows = normal_bf16_bits((M, D), 1.0, 975, 1)
+    w = np.random.default_rng(976).random((T, k)).astype(np.float32)
+    r_d, t_d = dev_bf16(rows), dev_i32(tr)
+    o1 = host_bits(mg.moe_combine(r_d, t_d))
+    o2 = host_bits(mg.moe_combine(r_d, t_d))
+    ow = host_bits(mg.moe_combine(r_d, t_d, torch.from_numpy(w).cuda()))
+    assert (o1 == o2).all()
+    sample = np.random.default_rng(977).choice(T, 512, replace=False)
+    r1 = _combine_gate(rows, tr, None, o1, sample)
+    r2 = _combine_gate(rows, tr, w.astype(np.float64), ow, sample)
+    assert r1.passed, str(r1)
+    assert r2.passed, str(r2)
+    assert (o1[(tr < 0).all(axis=1)] == 0).all()           # tokens routed to no local expert
