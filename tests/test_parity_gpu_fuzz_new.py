@@ -1,0 +1,124 @@
+"""Seeded random-shape fuzz of the MXFP8 forward and weight gradient, the
+SwiGLU backward and the token-order combine against the oracle (needs an
+MI355X).  Ragged and empty experts, reductions of one block to several
+stages, widths that are not multiples of the tile."""
+import numpy as np
+import pytest
+import torch
+
+import moe_grouped_gemm_bf16_amd as mg
+from oracle import (bf16_bits_to_f64, check_bf16, check_bf16_factor, check_bf16_mx,
+                    check_fp32_mx, grouped_dgrad, grouped_dgrad_swiglu, grouped_fwd,
+                    grouped_fwd_mx, grouped_wgrad, grouped_wgrad_mx, moe_combine, mx_dequant,
+                    mx_scales_blocked)
+from parity import SENTINEL, dev_bf16, dev_i32, host_bits, sentinel_bf16
+from workloads import normal_bf16_bits, offsets_from_sizes
+from workloads.synth import mx_e4m3_codes, mx_e8m0_codes
+
+pytestmark = pytest.mark.gpu
+SEEDS = range(6)
+
+
+def _u8(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).cuda()
+
+
+def _sizes(rng, E, hi, multiple=1):
+    s = rng.integers(0, hi, E) * multiple
+    s[rng.random(E) < 0.25] = 0
+    return s.tolist()
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_fuzz_fwd_mx(seed):
+    rng = np.random.default_rng(1000 + seed)
+    E = int(rng.integers(1, 7))
+    sizes = _sizes(rng, E, 400)
+    N = 8 * int(rng.integers(1, 70))
+    K = 32 * int(rng.integers(1, 20))
+    print("[case] fuzz fwd_mx", seed, sizes, N, K, flush=True)
+    off = offsets_from_sizes(sizes)
+    M = int(off[-1]) + 2
+    x8 = mx_e4m3_codes((M, K), 1100, seed, 1); w8 = mx_e4m3_codes((E, N, K), 1100, seed, 2)
+    xs = mx_e8m0_codes((M, K // 32), 121, 2, 1100, seed, 3)
+    ws = mx_e8m0_codes((E, N, K // 32), 121, 2, 1100, seed, 4)
+    y = mg.fwd_mx(_u8(x8), _u8(mx_scales_blocked(xs)), _u8(w8), _u8(mx_scales_blocked(ws)),
+                  dev_i32(off), out=sentinel_bf16((M, N)))
+    got = host_bits(y)
+    o = int(off[-1])
+    exact = grouped_fwd_mx(x8, xs, w8, ws, off)[:o]
+    mag = grouped_fwd(np.abs(mx_dequant(x8, xs)), np.abs(mx_dequant(w8, ws)), off)[:o]
+    rep = check_bf16_mx(got[:o], exact, mag)
+    assert rep.passed, str(rep)
+    assert (got[o:] == SENTINEL).all()
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_fuzz_wgrad_mx(seed):
+    rng = np.random.default_rng(2000 + seed)
+    E = int(rng.integers(1, 6))
+    sizes = _sizes(rng, E, 5, multiple=128)
+    N = 8 * int(rng.integers(1, 50)); K = 8 * int(rng.integers(1, 50))
+    print("[case] fuzz wgrad_mx", seed, sizes, N, K, flush=True)
+    off = offsets_from_sizes(sizes)
+    M = int(off[-1]) + 128
+    dyt8 = mx_e4m3_codes((N, M), 2100, seed, 1); xt8 = mx_e4m3_codes((K, M), 2100, seed, 2)
+    dyts = mx_e8m0_codes((N, M // 32), 121, 2, 2100, seed, 3)
+    xts = mx_e8m0_codes((K, M // 32), 121, 2, 2100, seed, 4)
+    out = mg.wgrad_mx(_u8(dyt8), _u8(mx_scales_blocked(dyts)), _u8(xt8),
+                      _u8(mx_scales_blocked(xts)), dev_i32(off), E)
+    got = out.cpu().numpy()
+    exact = grouped_wgrad_mx(dyt8, dyts, xt8, xts, off, E)
+    mag = grouped_wgrad(np.abs(mx_dequant(dyt8, dyts)).T, np.abs(mx_dequant(xt8, xts)).T, off, E)
+    sz = np.diff(np.asarray(off, np.int64))
+    k_red = np.broadcast_to(np.maximum(sz, 1)[:, None, None], exact.shape)
+    empty = np.broadcast_to((sz == 0)[:, None, None], exact.shape)
+    rep = check_fp32_mx(got, exact, mag, k_red, empty_mask=empty)
+    assert rep.passed, str(rep)
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_fuzz_dgrad_swiglu(seed):
+    rng = np.random.default_rng(3000 + seed)
+    E = int(rng.integers(1, 6))
+    sizes = _sizes(rng, E, 500)
+    N = 8 * int(rng.integers(1, 100)); I = 8 * int(rng.integers(1, 60))
+    print("[case] fuzz dgrad_swiglu", seed, sizes, N, I, flush=True)
+    off = offsets_from_sizes(sizes)
+    M = int(off[-1]) + 1
+    dyb = normal_bf16_bits((M, N), 1.0, 3100, seed, 1)
+    w2b = normal_bf16_bits((E, N, I), N ** -0.5, 3100, seed, 2)
+    gub = normal_bf16_bits((M, 2 * I), 2.0, 3100, seed, 3)
+    out = mg.dgrad_swiglu(dev_bf16(dyb), dev_bf16(w2b), dev_bf16(gub), dev_i32(off),
+                          out=sentinel_bf16((M, 2 * I)))
+    got = host_bits(out)
+    o = int(off[-1])
+    dy, w2, gu = bf16_bits_to_f64(dyb), bf16_bits_to_f64(w2b), bf16_bits_to_f64(gub)
+    exact, _ = grouped_dgrad_swiglu(dy, w2, gu, off)
+    S = grouped_dgrad(np.abs(dy), np.abs(w2), off)
+    g, u = gu[:, :I], gu[:, I:]
+    s = 1 / (1 + np.exp(-g))
+    fac = np.concatenate([u * s * (1 + g * (1 - s)), g * s], axis=1)
+    rep = check_bf16_factor(got[:o], exact[:o], fac[:o], np.concatenate([S, S], axis=1)[:o], N)
+    assert rep.passed, str(rep)
+    assert (got[o:] == SENTINEL).all()
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_fuzz_moe_combine(seed):
+    rng = np.random.default_rng(4000 + seed)
+    T = int(rng.integers(1, 400)); k = int(rng.integers(1, 10)); M = int(rng.integers(1, 900))
+    D = 8 * int(rng.integers(1, 100))
+    print("[case] fuzz moe_combine", seed, T, k, M, D, flush=True)
+    rows = normal_bf16_bits((M, D), 1.0, 4100, seed, 1)
+    tr = rng.integers(-1, M, (T, k)).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32) if seed % 2 else None
+    out = mg.moe_combine(dev_bf16(rows), dev_i32(tr),
+                         None if w is None else torch.from_numpy(w).cuda())
+    got = host_bits(out)
+    R = bf16_bits_to_f64(rows)
+    wf = None if w is None else w.astype(np.float64)
+    exact = moe_combine(R, tr, wf)
+    mag = moe_combine(np.abs(R), tr, None if wf is None else np.abs(wf))
+    rep = check_bf16(got, exact, mag, k)
+    assert rep.passed, str(rep)
