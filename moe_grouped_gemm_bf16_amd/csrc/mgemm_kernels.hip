@@ -1065,7 +1065,13 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
     uint32_t off;
     if (MX) {
       const int cj = 16 * (mx_c0 ^ (d & 3));
-      off = (mx_rowoff + (uint32_t)d * 8u * (uint32_t)ld + (uint32_t)(cj + r0)) |
+      uint32_t ro = mx_rowoff;
+      // The weight gradient runs at the register limit: left alone, the
+      // compiler keeps all SPW sums ro + d 8 ld live through the tile, they
+      // spill, and every refill then waits on the reloads (vmcnt down to 0,
+      // draining the stage in flight).  An opaque copy keeps them per load.
+      if constexpr (MODE == kWgradMx) asm volatile("" : "+v"(ro));
+      off = (ro + (uint32_t)d * 8u * (uint32_t)ld + (uint32_t)(cj + r0)) |
             (r0 + cj < p_red ? 0u : kOOB);
     } else if (SWI || LIST)
       off = (tvoff[d] + (uint32_t)r0 * 2u) |
