@@ -110,6 +110,10 @@ WG_CASES = [
     # halves (odd stage count, ragged last stage, ragged N and K, empty experts)
     ([2017, 33, 65, 129, 0, 0, 0, 700], 1544, 776),
     ([2500, 1, 0, 300, 0, 77, 1030, 5], 264, 1032),
+    # near-uniform long experts whose tiles fill most but not all workgroups
+    # (ragged N, K and token counts)
+    ([3000, 2900, 3100, 2990, 3050, 2950, 3011, 2987], 760, 2000),
+    ([2000 + 7 * i for i in range(17)], 256, 2048),
 ]
 
 
