@@ -333,7 +333,11 @@ def lists(torch, mg, reps=20):
     on the 30B-A3B share: (1) the gate-up forward as 32 per-expert groups
     against the M-grouped call on the same data; (2) gate-up and down forwards
     of all 32 experts mixed in one 64-group launch against two M-grouped
-    launches.  Timed interleaved; reported beside the step only."""
+    launches; (3) on uniform_g8, M- and K-grouped problems in one launch: the
+    8 experts' forwards and their weight gradients (dW_e = dY_e^T X_e on
+    token-axis-last copies of dY and X, made before the timed region; bf16
+    results) against the M-grouped forward plus the K-grouped weight gradient
+    (fp32 results).  Timed interleaved; reported beside the step only."""
     import numpy as np
     from workloads import make_workload
     wls = {w.name: w for w in make_workload(4)}
@@ -351,6 +355,19 @@ def lists(torch, mg, reps=20):
     gu, dn = ins["a3b_gate_up"], ins["a3b_down"]
     d_gu = mg.list_descriptors(gu[5], gu[6])
     d_mix = mg.list_descriptors(gu[5] + dn[5], gu[6] + dn[6])
+    (wu,) = make_workload(2)
+    ou = [int(v) for v in wu.offsets]
+    xu, wwu, dyu = up(wu.x_bits()), up(wu.w_bits()), up(wu.dy_bits())
+    xut, dyut = xu.t().contiguous(), dyu.t().contiguous()
+    yu = torch.empty((wu.M, wu.N), dtype=torch.bfloat16, device="cuda")
+    dwu = torch.empty((wu.E, wu.N, wu.K), dtype=torch.bfloat16, device="cuda")
+    dwu32 = torch.empty((wu.E, wu.N, wu.K), dtype=torch.float32, device="cuda")
+    offu = torch.from_numpy(wu.offsets).cuda()
+    mk_groups, mk_outs = [], []
+    for e in range(wu.E):
+        mk_groups += [(xu[ou[e]:ou[e + 1]], wwu[e]), (dyut[:, ou[e]:ou[e + 1]], xut[:, ou[e]:ou[e + 1]])]
+        mk_outs += [yu[ou[e]:ou[e + 1]], dwu[e]]
+    d_mk = mg.list_descriptors(mk_groups, mk_outs)
     cases = {
         "gate_up_32_groups": (lambda: mg.grouped_list_desc(d_gu, 32),
                               lambda: mg.fwd(gu[1], gu[2], gu[3], gu[7], out=gu[4]),
@@ -359,6 +376,10 @@ def lists(torch, mg, reps=20):
                                        lambda: (mg.fwd(gu[1], gu[2], gu[3], gu[7], out=gu[4]),
                                                 mg.fwd(dn[1], dn[2], dn[3], dn[7], out=dn[4])),
                                        gu[0].flops() + dn[0].flops()),
+        "uniform_g8_fwd_and_wgrad_16_groups": (
+            lambda: mg.grouped_list_desc(d_mk, 2 * wu.E),
+            lambda: (mg.fwd(xu, wwu, offu, out=yu), mg.wgrad(dyu, xu, offu, wu.E, out=dwu32)),
+            2 * wu.flops()),
     }
     out = {}
     for name, (fl, fm, flops) in cases.items():

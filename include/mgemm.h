@@ -169,7 +169,10 @@ typedef struct mg_gemm_desc {
  * array of G descriptors, 8-byte aligned, 1 <= G <= 1024; read by the kernel's
  * own scheduler, never on the host (checked on the host only under
  * MGEMM_VALIDATE=1, with mg_check_list_host).  The D regions must not overlap
- * each other or any input.  Allocates nothing. */
+ * each other or any input.  Allocates nothing.  M- and K-grouped problems mix
+ * in one list: a K-grouped weight gradient dW_e = dY_e^T X_e is the entry
+ * a = dY^T + offsets[e], b = X^T + offsets[e] (token-axis-last copies [N, M]
+ * and [K, M], lda = ldb = M), m = N, n = K, k = the expert's token count. */
 mg_status mgemm_list(const mg_gemm_desc* desc, int32_t G, void* stream);
 
 /* Host-side check of a descriptor list held in HOST memory (no device use):

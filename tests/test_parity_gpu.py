@@ -345,6 +345,47 @@ def _list_check(groups_bits, outs):
         assert rep.passed, f"group {g}: {rep}"
 
 
+def test_grouped_list_mixes_m_and_k_grouped():
+    """One launch holding an expert layer's M-grouped forward (Y_e = X_e W_e^T,
+    one group per expert) and its K-grouped weight gradient (dW_e = dY_e^T X_e,
+    one group per expert on token-axis-last operands: A and B are expert e's
+    column ranges of dY^T [N, M] and X^T [K, M], row stride M), against the
+    oracle's grouped forward and grouped weight gradient (bf16 results here).
+    Expert sizes are multiples of 8 so that the column views stay 16-byte
+    aligned; the empty expert gives an empty forward group and a k = 0
+    weight-gradient group (zeros)."""
+    from oracle import bf16_bits_to_f64, check_bf16, grouped_fwd, grouped_wgrad
+    sizes = [264, 0, 136, 520, 8]
+    off = offsets_from_sizes(sizes)
+    M, E, N, K = int(off[-1]), len(sizes), 200, 264
+    xb = normal_bf16_bits((M, K), 1.0, 610, 1)
+    wb = normal_bf16_bits((E, N, K), K ** -0.5, 610, 2)
+    dyb = normal_bf16_bits((M, N), 1.0, 610, 3)
+    x, w, dy = dev_bf16(xb), dev_bf16(wb), dev_bf16(dyb)
+    xt, dyt = x.t().contiguous(), dy.t().contiguous()
+    y = sentinel_bf16((M, N))
+    dws = [sentinel_bf16((N, K)) for _ in range(E)]
+    groups, outs = [], []
+    for e in range(E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        groups.append((x[lo:hi], w[e]))
+        outs.append(y[lo:hi])
+        groups.append((dyt[:, lo:hi], xt[:, lo:hi]))
+        outs.append(dws[e])
+    _say("grouped_list fwd + wgrad", sizes, N, K)
+    mg.grouped_list(groups, outs)
+    torch.cuda.synchronize()
+    x64, w64, dy64 = bf16_bits_to_f64(xb), bf16_bits_to_f64(wb), bf16_bits_to_f64(dyb)
+    rep = check_bf16(host_bits(y), grouped_fwd(x64, w64, off),
+                     grouped_fwd(np.abs(x64), np.abs(w64), off), K)
+    assert rep.passed, f"forward groups: {rep}"
+    dw = grouped_wgrad(dy64, x64, off, E)
+    dw_mag = grouped_wgrad(np.abs(dy64), np.abs(x64), off, E)
+    for e in range(E):
+        rep = check_bf16(host_bits(dws[e]), dw[e], dw_mag[e], max(sizes[e], 1))
+        assert rep.passed, f"weight-gradient group {e}: {rep}"
+
+
 def test_grouped_list_mixed_shapes():
     """Groups of different m, n, k in one launch: ragged tiles, row strides
     wider than the rows (views into bigger buffers), an empty group, a group
