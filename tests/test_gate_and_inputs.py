@@ -157,3 +157,20 @@ def test_zipf_and_random_offsets():
     o = random_offsets(9, 500, seed=3, special=[0, 1, 127, 128, 129])
     assert o[0] == 0 and o[-1] <= 500 and (np.diff(o) >= 0).all() and len(o) == 10
     assert sorted(np.diff(o).tolist())[:2] == [0, 1] or 0 in np.diff(o)
+
+
+def test_lattice_operand_host_and_device_builders_agree():
+    """The row-addressable operand for sizes past 4 GiB: the torch builder (run
+    here on the CPU, in several row chunks) and the host view give the same
+    values, rows and column slices alike, and every value is exact in bf16."""
+    import torch
+    from workloads.synth import LatticeMatrix, lattice_bf16, lattice_values
+    M, K = 300, 40
+    t = lattice_bf16(M, K, "cpu", chunk=64).float().numpy().astype(np.float64)
+    h = LatticeMatrix(M, K)
+    assert np.array_equal(t, h[np.arange(M)])
+    assert np.array_equal(t[17:250, 9], h[17:250, 9])
+    assert np.array_equal(t, lattice_values(np.arange(M)[:, None], np.arange(K)[None, :]))
+    assert set(np.unique(t * 8).astype(int)) <= set(range(-8, 9))
+    # neighbouring rows and columns differ (a misplaced read changes values)
+    assert not np.array_equal(t[:-1], t[1:]) and not np.array_equal(t[:, :-1], t[:, 1:])

@@ -136,6 +136,55 @@ def test_wgrad_fuzz(case, accumulate):
     assert r.passed, str(r)
 
 
+def test_operands_beyond_4gib_sampled():
+    """fwd, dgrad and wgrad where X [1052672, 2176] bf16 (4.58 GB) and the dgrad
+    output dX of the same shape extend past 4 GiB, the last expert's rows lying
+    beyond the 4 GiB byte offset: every tile base and store address must be
+    64-bit.  X is the row-addressable lattice operand (built on the device in
+    row chunks, recomputed on the host for the sampled rows); samples are
+    concentrated in the rows past the boundary."""
+    from oracle import check_bf16, sample_dgrad, sample_fwd
+    from workloads.synth import LatticeMatrix, lattice_bf16
+    M, K, N = (1 << 20) + 4096, 2176, 256
+    sizes = [400000, 0, 350000, M - 750000]
+    off = offsets_from_sizes(sizes)
+    E = len(sizes)
+    boundary = (1 << 32) // (2 * K)                  # first X row past 4 GiB
+    assert off[-2] < boundary < M
+    _say("beyond 4 GiB", M, K, N, sizes)
+    x = lattice_bf16(M, K, "cuda")
+    xh = LatticeMatrix(M, K)
+    wb = normal_bf16_bits((E, N, K), K ** -0.5, 900, 1)
+    dyb = normal_bf16_bits((M, N), 1.0, 900, 2)
+    w, dy, o = dev_bf16(wb), dev_bf16(dyb), dev_i32(off)
+    hint = int(max(sizes))
+    rng = np.random.default_rng(900)
+    rows = np.concatenate([rng.integers(0, M, 512), rng.integers(boundary, M, 1024),
+                           np.arange(M - 64, M), np.arange(boundary - 32, boundary + 32)])
+    rows_t = torch.from_numpy(rows).cuda()
+
+    y = mg.fwd(x, w, o, hint)
+    cols = rng.integers(0, N, rows.size)
+    got = host_bits(y[rows_t, torch.from_numpy(cols).cuda()])
+    exact, mag = sample_fwd(xh, wb, off, rows, cols)
+    rep = check_bf16(got, exact, mag, K)
+    assert rep.passed, f"fwd: {rep}"
+    del y
+
+    dx = mg.dgrad(dy, w, o, hint)
+    cols = rng.integers(0, K, rows.size)
+    got = host_bits(dx[rows_t, torch.from_numpy(cols).cuda()])
+    exact, mag = sample_dgrad(dyb, wb, off, rows, cols)
+    rep = check_bf16(got, exact, mag, N)
+    assert rep.passed, f"dgrad: {rep}"
+    del dx
+
+    dw = mg.wgrad(dy, x, o, E)
+    torch.cuda.synchronize()
+    rep = gate_wgrad_sampled(dyb, xh, off, dw.cpu().numpy(), S=96, seed=900)
+    assert rep.passed, f"wgrad: {rep}"
+
+
 def test_single_expert_is_plain_gemm():
     off, M, E, xb, wb, dyb = _inputs([777], 392, 328, 300)
     _say("E=1", M)

@@ -250,3 +250,45 @@ def mx_e8m0_codes(shape: Sequence[int], center: int, spread: int, *key: int) -> 
     rng = _stream(*key)
     c = rng.integers(center - spread, center + spread + 1, int(np.prod(shape, dtype=np.int64)))
     return np.clip(c, 0, 254).astype(np.uint8).reshape(tuple(shape))
+
+
+# -- a row-addressable operand for sizes past 4 GiB ---------------------------
+# Element (i, k) = ((37 i + 11 k + 5) mod 17 - 8) / 8: a multiple of 1/8 in
+# [-1, 1], exact in bf16, so that a tensor of billions of elements can be built
+# on the device in row chunks and any of its rows (or a column range) recomputed
+# on the host without materialising it.  Neighbouring rows and columns differ,
+# so a row or column read from the wrong place changes the result.
+
+def lattice_values(i, k) -> np.ndarray:
+    """Values (float64) at broadcast int64 indices i, k."""
+    i = np.asarray(i, np.int64); k = np.asarray(k, np.int64)
+    return ((37 * i + 11 * k + 5) % 17 - 8) / 8.0
+
+
+class LatticeMatrix:
+    """Host view of the [M, K] lattice operand: m[rows] gives those rows,
+    m[row_slice, col] one column over a row range (float64)."""
+
+    def __init__(self, M: int, K: int):
+        self.shape = (M, K)
+
+    def __getitem__(self, idx):
+        M, K = self.shape
+        if isinstance(idx, tuple):
+            rows, col = idx
+            return lattice_values(np.arange(M)[rows], int(col))
+        return lattice_values(np.asarray(idx, np.int64)[:, None], np.arange(K)[None, :])
+
+
+def lattice_bf16(M: int, K: int, device, chunk: int = 1 << 16):
+    """The [M, K] lattice operand as a torch bf16 tensor on `device`, built in
+    row chunks (exact: every value is a multiple of 1/8 in [-1, 1])."""
+    import torch
+    out = torch.empty((M, K), dtype=torch.bfloat16, device=device)
+    k = torch.arange(K, dtype=torch.int64, device=device)[None, :]
+    for r0 in range(0, M, chunk):
+        r1 = min(M, r0 + chunk)
+        i = torch.arange(r0, r1, dtype=torch.int64, device=device)[:, None]
+        v = (37 * i + 11 * k + 5) % 17 - 8
+        out[r0:r1] = (v.to(torch.float32) / 8.0).to(torch.bfloat16)
+    return out
