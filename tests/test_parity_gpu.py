@@ -185,6 +185,45 @@ def test_operands_beyond_4gib_sampled():
     assert rep.passed, f"wgrad: {rep}"
 
 
+def test_longest_reductions_sampled():
+    """The longest reductions the API takes (2^22 steps, 65536 stages in one
+    tile): the forward with K = 2^22, the dgrad with N = 2^22, and the weight
+    gradient over 2^22 tokens, on two ragged experts each, sampled against the
+    oracle."""
+    from oracle import check_bf16, sample_dgrad, sample_fwd
+    R = 1 << 22
+    rng = np.random.default_rng(901)
+    sizes = [24, 16]
+    off = offsets_from_sizes(sizes)
+    M, E = int(off[-1]), 2
+    rows = np.arange(M)
+    _say("longest reductions: fwd K", R)
+    xb = normal_bf16_bits((M, R), 1.0, 901, 1)
+    wb = normal_bf16_bits((E, 16, R), R ** -0.5, 901, 2)
+    y = mg.fwd(dev_bf16(xb), dev_bf16(wb), dev_i32(off))
+    cols = rng.integers(0, 16, M)
+    exact, mag = sample_fwd(xb, wb, off, rows, cols)
+    rep = check_bf16(host_bits(y)[rows, cols], exact, mag, R)
+    assert rep.passed, f"fwd: {rep}"
+    del xb, wb, y
+    _say("longest reductions: dgrad N", R)
+    dyb = normal_bf16_bits((M, R), 1.0, 901, 3)
+    wb = normal_bf16_bits((E, R, 16), R ** -0.5, 901, 4)
+    dx = mg.dgrad(dev_bf16(dyb), dev_bf16(wb), dev_i32(off))
+    exact, mag = sample_dgrad(dyb, wb, off, rows, cols)
+    rep = check_bf16(host_bits(dx)[rows, cols], exact, mag, R)
+    assert rep.passed, f"dgrad: {rep}"
+    del dyb, wb, dx
+    _say("longest reductions: wgrad tokens", R)
+    off2 = offsets_from_sizes([R - 1000, 1000])
+    dyb = normal_bf16_bits((R, 16), 1.0, 901, 5)
+    xb = normal_bf16_bits((R, 24), 1.0, 901, 6)
+    dw = mg.wgrad(dev_bf16(dyb), dev_bf16(xb), dev_i32(off2), 2)
+    torch.cuda.synchronize()
+    rep = gate_wgrad_sampled(dyb, xb, off2, dw.cpu().numpy(), S=64, seed=901)
+    assert rep.passed, f"wgrad: {rep}"
+
+
 def test_single_expert_is_plain_gemm():
     off, M, E, xb, wb, dyb = _inputs([777], 392, 328, 300)
     _say("E=1", M)
