@@ -26,6 +26,7 @@ import os
 import re
 import statistics
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -34,6 +35,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0        # MI355X published dense bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 PEAK_FP8_TFLOPS = 5000.0         # MI355X published dense fp8 matrix-core peak
+BF16_FLOP_PER_CLK = 256 * 4096   # 256 CUs x 4096 dense bf16 flop per clock and CU
 KERNEL_SRC = os.path.join(ROOT, "moe_grouped_gemm_bf16_amd", "csrc", "mgemm_kernels.hip")
 KERNEL_NAMES = {"fwd": "grouped_gemm_kernel<0>", "dgrad": "grouped_gemm_kernel<1>",
                 "wgrad": "grouped_gemm_kernel<2>", "fwd_swiglu": "grouped_gemm_kernel<3>",
@@ -559,6 +561,62 @@ def load_traffic(workload: str, kernel: str):
     return rec.get("bytes_per_launch", {}).get(kernel)
 
 
+class ClockSampler:
+    """Graphics clock while the step runs: amdsmi's per-XCD current gfx
+    clocks (MHz) read every 2 ms on a thread of its own (ctypes calls, which
+    release the interpreter lock).  The firmware's table lags the clock by a
+    good part of a second, so the step is repeated for `seconds` after the
+    timed region and only the samples of the last 70% of that window count.
+    Best effort: without amdsmi, or if every read fails, it reports nothing."""
+
+    def __init__(self):
+        self.samples, self._stop, self._th, self._h, self._smi = [], threading.Event(), None, None, None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._smi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+        except Exception:
+            self._smi = None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
+                c = [v for v in m.get("current_gfxclks", []) if isinstance(v, (int, float)) and v > 0]
+                if c:
+                    self.samples.append((time.perf_counter(), statistics.fmean(c)))
+            except Exception:
+                pass
+            self._stop.wait(0.002)
+
+    def measure(self, step, torch, seconds=1.0):
+        if self._smi is None:
+            return None
+        self._th = threading.Thread(target=self._run, daemon=True)
+        t0 = time.perf_counter()
+        self._th.start()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(10):
+                step()
+            torch.cuda.synchronize()
+        self._stop.set()
+        self._th.join()
+        try:
+            self._smi.amdsmi_shut_down()
+        except Exception:
+            pass
+        t1 = time.perf_counter()
+        late = [v for t, v in self.samples if t >= t0 + 0.3 * (t1 - t0)]
+        if not late:
+            return None
+        return {"gfx_mhz_median": round(statistics.median(late), 1),
+                "gfx_mhz_min": round(min(late), 1), "gfx_mhz_max": round(max(late), 1),
+                "samples": len(late),
+                "source": "amdsmi current_gfxclks (mean over the XCDs) every 2 ms while the "
+                          "step repeats for 1 s after the timed steps; last 70% of the window"}
+
+
 def main():
     args = parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -601,6 +659,11 @@ def main():
             ev[s][i][1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+
+    def one_step():
+        for op in ops:
+            op.launch()
+    clock = ClockSampler().measure(one_step, torch)
     for s in range(args.steps):
         for i, op in enumerate(ops):
             op.times_ms.append(ev[s][i][0].elapsed_time(ev[s][i][1]))
@@ -616,6 +679,8 @@ def main():
             "avg_us": round(avg * 1e3, 2),
             "median_us": round(statistics.median(op.times_ms) * 1e3, 2),
             "min_us": round(min(op.times_ms) * 1e3, 2),
+            "top10_mean_us": round(statistics.fmean(
+                sorted(op.times_ms)[:max(1, len(op.times_ms) // 10)]) * 1e3, 2),
             "tflops": round(op.flops / (avg * 1e-3) / 1e12, 1),
             "pct_peak": round(100 * op.flops / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 1),
             "algo_GBps": round(op.bytes / (avg * 1e-3) / 1e9, 1),
@@ -695,6 +760,10 @@ def main():
         "config": config,
         "per_op": per_op,
         "roofline": roofline,
+        "clock": clock,
+        "pct_of_clock_adjusted_peak": (
+            round(100 * value / (BF16_FLOP_PER_CLK * clock["gfx_mhz_median"] * 1e6 / 1e12), 2)
+            if clock else None),
         "cpu_baseline": cpu,
         "kernel_src_sha256_16": kernel_hash(),
     }
