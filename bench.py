@@ -504,19 +504,31 @@ def mx(torch, mg, reps=20):
 # ------------------------------------------------------------- CPU baseline --
 
 def cpu_baseline(workload: str):
-    """The oracle as it stands, timed on this host's cores over one whole step
-    of the default workload (all three ops, all experts); for the a3b
-    workload, over the gate-up fwd + dgrad of 4 of the 32 experts and the
-    gw13 weight gradient of those experts (a bounded sample)."""
+    """The oracle as it stands, timed on this host's cores over whole steps
+    of the default workload (all three ops, all experts), repeated until at
+    least 10 s of CPU work have run; for the a3b workload, over the gate-up
+    fwd + dgrad + wgrad of 4 of the 32 experts (a bounded sample).  The record
+    names the CPU model and the BLAS library the oracle's products ran on."""
     import numpy as np
     from oracle import (bf16_bits_to_f64, f64_to_bf16_bits, grouped_dgrad, grouped_fwd,
                         grouped_wgrad)
     from workloads import make_workload
+    blas = None
     try:
         from threadpoolctl import threadpool_info
-        cores = max(i.get("num_threads", 1) for i in threadpool_info()) if threadpool_info() else 1
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"] or threadpool_info()
+        cores = max(i.get("num_threads", 1) for i in info) if info else 1
+        if info:
+            blas = f"{info[0].get('internal_api', '?')} {info[0].get('version', '')}".strip()
     except Exception:  # pragma: no cover
         cores = len(os.sched_getaffinity(0))
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")),
+                             None)
+    except OSError:  # pragma: no cover
+        pass
     flops, secs = 0, 0.0
     if workload == "a3b":
         wl = make_workload(4, "a3b_gate_up")[0]
@@ -533,14 +545,18 @@ def cpu_baseline(workload: str):
         rows = int(off[-1])
         sample = f"one whole step (fwd+dgrad+wgrad, all {wl.E} experts) of {wl.name}"
     E = len(off) - 1
+    reps = 0
     t = time.perf_counter()
-    f64_to_bf16_bits(grouped_fwd(X, W, off))
-    f64_to_bf16_bits(grouped_dgrad(DY, W, off))
-    grouped_wgrad(DY, X, off, E).astype(np.float32)
+    while reps == 0 or time.perf_counter() - t < 10.0:
+        f64_to_bf16_bits(grouped_fwd(X, W, off))
+        f64_to_bf16_bits(grouped_dgrad(DY, W, off))
+        grouped_wgrad(DY, X, off, E).astype(np.float32)
+        reps += 1
     secs = time.perf_counter() - t
-    flops = 3 * 2 * rows * wl.N * wl.K
+    flops = reps * 3 * 2 * rows * wl.N * wl.K
     return {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
-            "kind": "oracle", "sample": sample, "seconds": round(secs, 3)}
+            "kind": "oracle", "sample": f"{sample}, {reps} times", "seconds": round(secs, 3),
+            "cpu_model": cpu_model, "blas": blas}
 
 
 # -------------------------------------------------------------------- traffic --
