@@ -580,10 +580,12 @@ def load_traffic(workload: str, kernel: str):
 class ClockSampler:
     """Graphics clock while the step runs: amdsmi's per-XCD current gfx
     clocks (MHz) read every 2 ms on a thread of its own (ctypes calls, which
-    release the interpreter lock).  The firmware's table lags the clock by a
-    good part of a second, so the step is repeated for `seconds` after the
-    timed region and only the samples of the last 70% of that window count.
-    Best effort: without amdsmi, or if every read fails, it reports nothing."""
+    release the interpreter lock).  The firmware refreshes that table only
+    about once a second, so the step is repeated for `seconds` after the
+    timed region and only samples taken after the table first changed inside
+    that window count, at or above the 500 MHz minimum clock (an idle reading
+    otherwise).  Best effort: without amdsmi, without a refresh in the window,
+    or if every read fails, it reports nothing."""
 
     def __init__(self):
         self.samples, self._stop, self._th, self._h, self._smi = [], threading.Event(), None, None, None
@@ -606,7 +608,7 @@ class ClockSampler:
                 pass
             self._stop.wait(0.002)
 
-    def measure(self, step, torch, seconds=1.0):
+    def measure(self, step, torch, seconds=2.5):
         if self._smi is None:
             return None
         self._th = threading.Thread(target=self._run, daemon=True)
@@ -622,15 +624,17 @@ class ClockSampler:
             self._smi.amdsmi_shut_down()
         except Exception:
             pass
-        t1 = time.perf_counter()
-        late = [v for t, v in self.samples if t >= t0 + 0.3 * (t1 - t0)]
+        vals = [v for _, v in self.samples]
+        first_new = next((i for i, v in enumerate(vals) if v != vals[0]), None)
+        late = [v for v in vals[first_new:] if v >= 500.0] if first_new is not None else []
         if not late:
             return None
         return {"gfx_mhz_median": round(statistics.median(late), 1),
                 "gfx_mhz_min": round(min(late), 1), "gfx_mhz_max": round(max(late), 1),
                 "samples": len(late),
                 "source": "amdsmi current_gfxclks (mean over the XCDs) every 2 ms while the "
-                          "step repeats for 1 s after the timed steps; last 70% of the window"}
+                          "step repeats for 2.5 s after the timed steps; samples after the "
+                          "table's first refresh in that window"}
 
 
 def main():
