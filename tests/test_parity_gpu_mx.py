@@ -326,3 +326,43 @@ def test_mx_dgrad_is_forward_on_requantized_transposed_weights():
     mag = grouped_dgrad(np.abs(dyv), np.abs(w), off)
     rep = check_bf16_mx(got, exact, mag)
     assert rep.passed, str(rep)
+
+
+def test_mx_longest_reductions_sampled():
+    """The MXFP8 forward with K = 2^22 (32768 stages of 128 fp8 steps in one
+    tile) and the MXFP8 weight gradient over 2^22 tokens, two experts each,
+    sampled against the oracle under the MX gates."""
+    R = 1 << 22
+    rng = np.random.default_rng(8800)
+    off = offsets_from_sizes([24, 16])
+    M, N = int(off[-1]), 16
+    _say("mx longest reductions: fwd K", R)
+    x8 = mx_e4m3_codes((M, R), 8800, 1)
+    w8 = mx_e4m3_codes((2, N, R), 8800, 2)
+    xs = mx_e8m0_codes((M, R // 32), 121, 1, 8800, 3)
+    ws = mx_e8m0_codes((2, N, R // 32), 121, 1, 8800, 4)
+    got = _run(off, M, N, x8, w8, xs, ws)
+    rows = np.arange(M)
+    cols = rng.integers(0, N, M)
+    val, mag = sample_fwd_mx(x8, xs, w8, ws, off, rows, cols)
+    rep = check_bf16_mx(got[rows, cols], val, mag)
+    assert rep.passed, f"fwd: {rep}"
+    del x8, w8, xs, ws
+    _say("mx longest reductions: wgrad tokens", R)
+    off2 = offsets_from_sizes([R - 1024, 1024])
+    K = 24
+    dyt8 = mx_e4m3_codes((N, R), 8800, 5)
+    xt8 = mx_e4m3_codes((K, R), 8800, 6)
+    dyts = mx_e8m0_codes((N, R // 32), 121, 1, 8800, 7)
+    xts = mx_e8m0_codes((K, R // 32), 121, 1, 8800, 8)
+    dw = mg.wgrad_mx(_u8(dyt8), _u8(mx_scales_blocked(dyts)), _u8(xt8),
+                     _u8(mx_scales_blocked(xts)), dev_i32(off2), 2)
+    torch.cuda.synchronize()
+    got = dw.cpu().numpy()
+    es = np.repeat(np.arange(2), 24)
+    ns = rng.integers(0, N, es.size)
+    ks = rng.integers(0, K, es.size)
+    val, mag = sample_wgrad_mx(dyt8, dyts, xt8, xts, off2, es, ns, ks)
+    k_red = np.maximum(np.diff(np.asarray(off2, np.int64))[es], 1)
+    rep = check_fp32_mx(got[es, ns, ks], val, mag, k_red)
+    assert rep.passed, f"wgrad: {rep}"
