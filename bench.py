@@ -54,6 +54,8 @@ def parse_args():
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="uniform_g8", choices=["uniform_g8", "uniform_g16", "a3b"])
+    p.add_argument("--no-clock", action="store_true",
+                   help="skip the clock sampling phase after the timed steps (profiler runs)")
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip the oracle timing (used for profiler passes)")
     p.add_argument("--cold", type=int, default=0,
@@ -683,7 +685,7 @@ def main():
     def one_step():
         for op in ops:
             op.launch()
-    clock = ClockSampler().measure(one_step, torch)
+    clock = None if args.no_clock else ClockSampler().measure(one_step, torch)
     for s in range(args.steps):
         for i, op in enumerate(ops):
             op.times_ms.append(ev[s][i][0].elapsed_time(ev[s][i][1]))

@@ -280,6 +280,7 @@ struct Sched {
   int bw;       // K-grouped: P-tiles per band
   int per;      // K-grouped: tiles per expert
   bool split;   // K-grouped: heavy tiles may be split in two token halves
+  bool whole;   // K-grouped: each XCD takes whole experts (see kchunk_start)
   const ListDesc* list;   // descriptor list (E groups), else null
 };
 
@@ -427,9 +428,15 @@ __device__ __forceinline__ void decode_list(int L, const Sched& S, const ListDes
 
 // K-grouped: chunk k (0..7) of an expert's tile grid is the band-order index
 // range [k per / 8, (k+1) per / 8).
-__device__ __forceinline__ int kchunk_start(int k, int per) { return (k * per) >> 3; }
-__device__ __forceinline__ int kchunk_size(int k, int per) {
-  return kchunk_start(k + 1, per) - kchunk_start(k, per);
+// With `whole` (equal experts, E a multiple of 8), chunk 0 is the expert's
+// whole grid and the others are empty: XCD x then takes the experts of rank
+// x, x + 8, ..., so that all tiles of an expert share its X and dY panels in
+// one L2 (with 8 chunks each expert's panels are read by every XCD).
+__device__ __forceinline__ int kchunk_start(int k, int per, bool whole) {
+  return whole ? (k == 0 ? 0 : per) : (k * per) >> 3;
+}
+__device__ __forceinline__ int kchunk_size(int k, int per, bool whole) {
+  return kchunk_start(k + 1, per, whole) - kchunk_start(k, per, whole);
 }
 
 // K-grouped set-up: every expert has tilesQ x tilesP tiles whose cost grows
@@ -441,6 +448,13 @@ template <int NT>
 __device__ void setup_kgrouped(const int32_t* __restrict__ offsets, int E, int M, Sched& S) {
   for (int e = threadIdx.x; e <= E; e += NT) S.offs[e] = clamp_off(offsets, e, M);
   __syncthreads();
+  // whole experts per XCD when every expert has the same, nonzero row count
+  // and E is a multiple of 8 (the XCDs then get equal shares)
+  int same = 1;
+  for (int e = threadIdx.x; e < E; e += NT)
+    same &= S.offs[e + 1] - S.offs[e] == S.offs[1] - S.offs[0] ? 1 : 0;
+  same = __syncthreads_and(same);
+  S.whole = S.whole && same != 0 && (E & 7) == 0 && S.offs[1] > S.offs[0];
   int* sizes = S.mine;
   for (int e = threadIdx.x; e < E + 4; e += NT)
     sizes[e] = e < E ? max(S.offs[e + 1] - S.offs[e], 0) : -1;
@@ -495,7 +509,7 @@ __device__ void balance_kgrouped(int x, int me, int nx, Sched& S) {
     for (int r = lane; r < S.E; r += 64) {
       const int e = S.inv[r];
       const int m = max(S.offs[e + 1] - S.offs[e], 0);
-      tot0 += (uint64_t)kchunk_size((x - r) & 7, S.per) * (uint64_t)((m + kBK - 1) / kBK + 3);
+      tot0 += (uint64_t)kchunk_size((x - r) & 7, S.per, S.whole) * (uint64_t)((m + kBK - 1) / kBK + 3);
     }
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) tot0 += __shfl_xor(tot0, d, 64);
@@ -510,7 +524,7 @@ __device__ void balance_kgrouped(int x, int me, int nx, Sched& S) {
     int nheavy = 0;
     for (int r = lane; r < S.E; r += 64) {
       const int e = S.inv[r];
-      if (heavy(max(S.offs[e + 1] - S.offs[e], 0))) nheavy += kchunk_size((x - r) & 7, S.per);
+      if (heavy(max(S.offs[e + 1] - S.offs[e], 0))) nheavy += kchunk_size((x - r) & 7, S.per, S.whole);
     }
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) nheavy += __shfl_xor(nheavy, d, 64);
@@ -533,7 +547,7 @@ __device__ void balance_kgrouped(int x, int me, int nx, Sched& S) {
       int c;
       uint32_t w;
       bool sp;
-      piece(m, kchunk_size((x - r) & 7, S.per), c, w, sp);
+      piece(m, kchunk_size((x - r) & 7, S.per, S.whole), c, w, sp);
       tot += (uint64_t)c * w;
       ntiles += c;
       if (c > 0) { wlo = min(wlo, w); whi = max(whi, w); }
@@ -570,7 +584,7 @@ __device__ void balance_kgrouped(int x, int me, int nx, Sched& S) {
         const int m = max(S.offs[e + 1] - S.offs[e], 0);
         uint32_t w;
         bool sp;
-        ctl = kchunk_size((x - rl) & 7, S.per);
+        ctl = kchunk_size((x - rl) & 7, S.per, S.whole);
         piece(m, ctl, cl, w, sp);
         spl = sp ? 1 : 0;
         wl = (w >> sh) + 1u;
@@ -680,9 +694,9 @@ __device__ __forceinline__ void decode_mgrouped(int L, const Sched& S, Tile& t) 
 // be narrower); within a band, Q-tile slow and P-tile fast.
 template <int BP, int BQ>
 __device__ __forceinline__ void decode_kgrouped(int r, int k, int u_in_chunk, const Sched& S,
-                                                Tile& t) {
+                                                bool whole, Tile& t) {
   const int e = S.inv[r];
-  const int u = kchunk_start(k, S.per) + u_in_chunk;
+  const int u = kchunk_start(k, S.per, whole) + u_in_chunk;
   const int nbw = S.bw * S.tilesQ;
   const int b = min(u / nbw, (S.tilesP - 1) / S.bw);
   const int local = u - b * nbw;
@@ -736,7 +750,7 @@ struct TileSeq {
       const bool sp = (rr >> 27) & 1;
       const int v = rho + j * nx;                 // piece of the chunk
       const int u = sp ? v >> 1 : v;
-      decode_kgrouped<BP, BQ>(r, (x - r) & 7, u, S, t);
+      decode_kgrouped<BP, BQ>(r, (x - r) & 7, u, S, MODE == kWgrad && S.whole, t);
       if (MODE == kWgradMx) {
         // whole 128-token stages (a no-op for offsets that are multiples of
         // 128, as documented; others give wrong sums but only aligned,
@@ -1728,6 +1742,7 @@ void grouped_gemm_kernel(KernelArgs a) {
   S.bw = bw;
   // (the MXFP8 weight gradient does not split: its registers are all taken)
   S.split = MODE == kWgrad && a.ws != nullptr && a.tickets != nullptr;
+  S.whole = MODE == kWgrad;                  // (the set-up keeps it only for equal experts)
   if (KG) {
     setup_kgrouped<C::NT>(a.offsets, E, (int)a.M, S);
     balance_kgrouped<C::NT>(blockIdx.x & 7, blockIdx.x >> 3, nx, S);

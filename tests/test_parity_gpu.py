@@ -114,6 +114,9 @@ WG_CASES = [
     # (ragged N, K and token counts)
     ([3000, 2900, 3100, 2990, 3050, 2950, 3011, 2987], 760, 2000),
     ([2000 + 7 * i for i in range(17)], 256, 2048),
+    # equal experts, E a multiple of 8: every XCD takes whole experts
+    ([300] * 8, 264, 136),
+    ([130] * 16, 520, 200),
 ]
 
 
