@@ -621,7 +621,9 @@ class ClockSampler:
                 step()
             torch.cuda.synchronize()
         self._stop.set()
-        self._th.join()
+        self._th.join(timeout=5.0)            # (a read that never returns is left behind)
+        if self._th.is_alive():
+            return None
         try:
             self._smi.amdsmi_shut_down()
         except Exception:
