@@ -117,6 +117,8 @@ WG_CASES = [
     # equal experts, E a multiple of 8: every XCD takes whole experts
     ([300] * 8, 264, 136),
     ([130] * 16, 520, 200),
+    # ... and with one long tile per expert: each XCD's tile is split in two halves
+    ([2000] * 8, 256, 256),
 ]
 
 
