@@ -532,6 +532,7 @@ def cpu_baseline(workload: str):
     except OSError:  # pragma: no cover
         pass
     flops, secs = 0, 0.0
+    td = time.perf_counter()      # generating the inputs and decoding them to fp64: reported apart
     if workload == "a3b":
         wl = make_workload(4, "a3b_gate_up")[0]
         sel = 4
@@ -547,6 +548,7 @@ def cpu_baseline(workload: str):
         rows = int(off[-1])
         sample = f"one whole step (fwd+dgrad+wgrad, all {wl.E} experts) of {wl.name}"
     E = len(off) - 1
+    decode_secs = time.perf_counter() - td
     reps = 0
     t = time.perf_counter()
     while reps == 0 or time.perf_counter() - t < 10.0:
@@ -558,7 +560,7 @@ def cpu_baseline(workload: str):
     flops = reps * 3 * 2 * rows * wl.N * wl.K
     return {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
             "kind": "oracle", "sample": f"{sample}, {reps} times", "seconds": round(secs, 3),
-            "cpu_model": cpu_model, "blas": blas}
+            "cpu_model": cpu_model, "blas": blas, "input_seconds": round(decode_secs, 3)}
 
 
 # -------------------------------------------------------------------- traffic --
