@@ -16,7 +16,7 @@ from workloads import normal_bf16_bits, offsets_from_sizes
 from workloads.synth import mx_e4m3_codes, mx_e8m0_codes
 
 pytestmark = pytest.mark.gpu
-SEEDS = range(6)
+SEEDS = range(12)
 
 
 def _u8(a):
