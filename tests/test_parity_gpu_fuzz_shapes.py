@@ -122,3 +122,42 @@ def test_fuzz_moe_combine(seed):
     mag = moe_combine(np.abs(R), tr, None if wf is None else np.abs(wf))
     rep = check_bf16(got, exact, mag, k)
     assert rep.passed, str(rep)
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_fuzz_core_ops(seed):
+    """The three core calls on random shapes: the M-grouped forward and dgrad
+    (rows past offsets[E] untouched) and the K-grouped weight gradient (with or
+    without accumulation into a prior), every element against the oracle."""
+    from parity import gate_dgrad_full, gate_fwd_full, gate_wgrad_full
+    rng = np.random.default_rng(5000 + seed)
+    E = int(rng.integers(1, 10))
+    sizes = _sizes(rng, E, 600)
+    if sum(sizes) == 0:
+        sizes[0] = 40                     # (all experts empty has a test of its own)
+    N = 8 * int(rng.integers(1, 80)); K = 8 * int(rng.integers(1, 80))
+    acc = bool(seed % 2)
+    print("[case] fuzz core", seed, sizes, N, K, "accumulate" if acc else "", flush=True)
+    off = offsets_from_sizes(sizes)
+    M = int(off[-1]) + 3
+    xb = normal_bf16_bits((M, K), K ** -0.5, 5100, seed, 1)
+    wb = normal_bf16_bits((E, N, K), K ** -0.5, 5100, seed, 2)
+    dyb = normal_bf16_bits((M, N), 1.0, 5100, seed, 3)
+    o = dev_i32(off)
+    y = mg.fwd(dev_bf16(xb), dev_bf16(wb), o, out=sentinel_bf16((M, N)))
+    dx = mg.dgrad(dev_bf16(dyb), dev_bf16(wb), o, out=sentinel_bf16((M, K)))
+    prior = rng.standard_normal((E, N, K)).astype(np.float32) if acc else None
+    dw = mg.wgrad(dev_bf16(dyb), dev_bf16(xb), o, E,
+                  out=None if prior is None else torch.from_numpy(prior.copy()).cuda(),
+                  accumulate=acc)
+    torch.cuda.synchronize()
+    yb, dxb = host_bits(y), host_bits(dx)
+    o_end = int(off[-1])
+    assert (yb[o_end:] == SENTINEL).all() and (dxb[o_end:] == SENTINEL).all()
+    rep = gate_fwd_full(xb, wb, off, yb)
+    assert rep.passed, f"fwd: {rep}"
+    rep = gate_dgrad_full(dyb, wb, off, dxb)
+    assert rep.passed, f"dgrad: {rep}"
+    rep = gate_wgrad_full(dyb, xb, off, dw.cpu().numpy(),
+                          prior=None if prior is None else prior.astype(np.float64))
+    assert rep.passed, f"wgrad: {rep}"
