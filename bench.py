@@ -5,16 +5,21 @@
 One step is one pass of the whole path over one batch of seeded synthetic
 input: the M-grouped forward Y = X W_e^T, the M-grouped input gradient
 dX = dY W_e and the K-grouped fp32 weight gradient dW_e = dY_e^T X_e, each one
-launch of libmgemm.so.  The default workload is the grouped-GEMM shape of the
-TransformerEngine PR #2045 perf table, (g, m, n, k) = (8, 4096, 768, 2048);
-`--workload a3b` runs one GPU's expert share of the 30B-A3B layout instead
-(router-assigned rows for fwd/dgrad of the gate-up and down GEMMs, the Zipf
-split for both weight gradients).
+launch of libmgemm.so.  The default workload is one GPU's expert share of the
+30B-A3B layout (RapidGEMM README, *Model layout* / *Settings*: 32 local experts,
+d_model 3072, expert FFN 1280): the forward and input gradient of the gate-up
+(K 3072 -> N 2560) and down (K 1280 -> N 3072) GEMMs on router-assigned rows,
+and both weight gradients (gw13, gw2) on the Zipf-skewed split -- six launches
+per step.  `--workload uniform_g8` / `uniform_g16` run the grouped-GEMM shapes
+of the TransformerEngine PR #2045 perf table instead, (g, m, n, k) =
+(8, 4096, 768, 2048) / (16, 2048, 768, 2048).
 
 Prints ONE JSON line: whole-step TFLOP/s (algorithmic flops 2*M*N*K per op,
 M = rows owned by experts), the fraction of the bf16 dense matrix-core peak,
-per-op HIP-event timings, the roofline entry of the dominant kernel and the
-oracle's CPU time on the host's cores.  Inputs are resident in HBM before
+per-op HIP-event timings (warm, and with the L2 and the Infinity Cache flushed
+before every launch: the flushed median is each op's headline), each op's
+fraction of the peak beside its target, the roofline entry of the dominant
+kernel and the oracle's CPU time on the host's cores.  Inputs are resident in HBM before
 the timed region; nothing is skipped inside it.
 """
 from __future__ import annotations
@@ -53,13 +58,13 @@ def parse_args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="uniform_g8", choices=["uniform_g8", "uniform_g16", "a3b"])
+    p.add_argument("--workload", default="a3b", choices=["a3b", "uniform_g8", "uniform_g16"])
     p.add_argument("--no-clock", action="store_true",
                    help="skip the clock sampling phase after the timed steps (profiler runs)")
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip the oracle timing (used for profiler passes)")
-    p.add_argument("--cold", type=int, default=0,
-                   help="also time each op N times after flushing the caches")
+    p.add_argument("--cold", type=int, default=50,
+                   help="time each op N times after flushing the caches (0: skip)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run one plain 1 GiB device copy (for HBM counter calibration)")
     p.add_argument("--comparators", action="store_true",
@@ -727,23 +732,49 @@ def main():
                 sorted(op.times_ms)[:max(1, len(op.times_ms) // 10)]) * 1e3, 2),
             "tflops": round(op.flops / (avg * 1e-3) / 1e12, 1),
             "pct_peak": round(100 * op.flops / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 1),
+            "median_pct_peak": round(
+                100 * op.flops / (statistics.median(op.times_ms) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 1),
             "algo_GBps": round(op.bytes / (avg * 1e-3) / 1e9, 1),
         }
 
     if args.cold > 0:
+        # Flushed launches: a 512 MiB fill (twice the 256 MB Infinity Cache,
+        # far beyond the L2s) runs before every launch, outside its events;
+        # one synchronisation at the end.
         flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
         for op in ops:
-            ts = []
-            for _ in range(args.cold):
+            cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.cold)]
+            for e0, e1 in cev:
                 flush.fill_(1)
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
                 op.launch()
                 e1.record(stream)
-                torch.cuda.synchronize()
-                ts.append(e0.elapsed_time(e1))
-            per_op[op.name]["cold_median_us"] = round(statistics.median(ts) * 1e3, 2)
+            torch.cuda.synchronize()
+            ts = sorted(e0.elapsed_time(e1) for e0, e1 in cev)
+            med = statistics.median(ts)
+            per_op[op.name].update({
+                "cold_median_us": round(med * 1e3, 2),
+                "cold_min_us": round(ts[0] * 1e3, 2),
+                "cold_top10_mean_us": round(statistics.fmean(ts[:max(1, len(ts) // 10)]) * 1e3, 2),
+                "cold_tflops": round(op.flops / (med * 1e-3) / 1e12, 1),
+                "cold_pct_peak": round(100 * op.flops / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 1),
+            })
         del flush
+
+    # each op against its target fraction of the peak (M-grouped forward and
+    # input gradient 60%, K-grouped weight gradient 50%), on the flushed
+    # median when measured, else the warm median
+    targets = {}
+    for op in ops:
+        r = per_op[op.name]
+        t_us = r.get("cold_median_us", r["median_us"])
+        pct = 100 * op.flops / (t_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS
+        goal = 50.0 if op.kind == "wgrad" else 60.0
+        targets[op.name] = {"pct_peak": round(pct, 1), "target_pct": goal,
+                            "target_us": round(op.flops / (goal / 100 * PEAK_BF16_TFLOPS * 1e12) * 1e6, 1),
+                            "us": t_us, "timing": "flushed median" if "cold_median_us" in r else "warm median",
+                            "met": pct >= goal}
 
     dom = ops[dom_i]
     dom_avg_s = statistics.fmean(dom_times_ms) * 1e-3      # in the timed region
@@ -804,6 +835,7 @@ def main():
         "data": "synthetic (seeded N(0,1)-scaled bf16 inputs, see workloads/synth.py)",
         "config": config,
         "per_op": per_op,
+        "targets": targets,
         "roofline": roofline,
         "clock": clock,
         "pct_of_clock_adjusted_peak": (

@@ -29,18 +29,23 @@
  *     enqueues work on that stream and returns; it never synchronises or
  *     keeps a caller pointer after returning.  The caller owns every buffer
  *     and must keep it alive until the stream has run the work.  The one
- *     allocation: the first kgemm_wgrad call on a (device, stream) pair
- *     allocates a 64 MiB device workspace for that pair (hipMalloc, zeroing
- *     its counters on the stream) and keeps it until the process ends; calls
- *     on one stream share it in stream order, calls on different streams
- *     never share one.  If that allocation fails the call still runs, without
- *     the token split.  MGEMM_SPLIT=0 turns the split (and the workspace) off.
+ *     allocation: the first kgemm_wgrad call on a (device, stream) pair that
+ *     is not being captured into a graph allocates a 64 MiB device workspace
+ *     for that pair (hipMalloc, its counters cleared with a synchronous
+ *     hipMemset -- nothing is enqueued on the caller's stream for it) and
+ *     keeps it until the process ends; calls on one stream share it in stream
+ *     order, calls on different streams never share one.  A kgemm_wgrad call
+ *     made while its stream is being captured allocates nothing and runs
+ *     without the token split (so it enqueues exactly one kernel and no
+ *     memory operation).  If the allocation fails the call still runs,
+ *     without the split.  MGEMM_SPLIT=0 turns the split (and the workspace)
+ *     off.
  *   - Host-detectable errors are returned before anything is enqueued.
  *     Launch failures return MG_ERR_LAUNCH.  Faults during execution surface
  *     at the caller's next synchronisation, like any stream work.  Nothing
  *     throws across this ABI.
  *   - Thread safety: calls may be made concurrently from several threads; the
- *     shared state is a per-device architecture check done once and the
+ *     shared state is a per-device architecture check done once, the
  *     mutex-protected table of per-stream workspaces.
  */
 #ifndef MGEMM_H
@@ -248,8 +253,12 @@ mg_status mg_mx_scales_blocked(const void* scales, void* blocked, int64_t rows, 
  * Rows i >= offsets[E] do not contribute.  N == 0 or K == 0 is a no-op.
  * An expert much heavier than the rest may have its token range split in two
  * halves whose fp32 partial sums are added as (half + half), then + dw when
- * accumulating: results are bitwise reproducible from call to call.  This is
- * the call that uses the per-stream workspace described above. */
+ * accumulating: results are bitwise reproducible from call to call (a call
+ * captured into a graph computes such tiles whole, which may differ from an
+ * uncaptured call in the last bits).  This is the call that uses the
+ * per-stream workspace described above.  The halves meet through one ticket
+ * word per split tile, tagged with a per-launch mark, so a word left behind
+ * by a launch that did not complete cannot mislead a later one. */
 mg_status kgemm_wgrad(const void* dy, const void* x, const int32_t* offsets, float* dw,
                       int64_t M, int64_t N, int64_t K, int32_t E, int32_t accumulate,
                       void* stream);

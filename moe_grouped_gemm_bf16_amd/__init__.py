@@ -107,6 +107,10 @@ def wgrad(dy: torch.Tensor, x: torch.Tensor, offsets: torch.Tensor, E: int | Non
 
     dy bf16 [M, N], x bf16 [M, K]; returns fp32 [E, N, K].  E defaults to
     offsets.numel() - 1.  With accumulate=True the sum is added into `out`."""
+    return _wgrad("kgemm_wgrad", dy, x, offsets, E, out, accumulate)
+
+
+def _wgrad(fn: str, dy, x, offsets, E, out, accumulate):
     _need(dy, "dy", torch.bfloat16, 2)
     _need(x, "x", torch.bfloat16, 2)
     M, N = dy.shape
@@ -125,9 +129,9 @@ def wgrad(dy: torch.Tensor, x: torch.Tensor, offsets: torch.Tensor, E: int | Non
         if tuple(out.shape) != (E, N, K):
             raise ValueError(f"out must be [{E}, {N}, {K}]")
     with torch.cuda.device(dy.device):
-        st = LIB.kgemm_wgrad(dy.data_ptr(), x.data_ptr(), offsets.data_ptr(), out.data_ptr(),
-                             M, N, K, E, 1 if accumulate else 0, _stream(dy))
-    check(st, "kgemm_wgrad")
+        st = getattr(LIB, fn)(dy.data_ptr(), x.data_ptr(), offsets.data_ptr(), out.data_ptr(),
+                              M, N, K, E, 1 if accumulate else 0, _stream(dy))
+    check(st, fn)
     return out
 
 

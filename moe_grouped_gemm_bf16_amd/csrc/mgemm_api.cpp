@@ -6,7 +6,8 @@
 // lifetime race discussed in the TransformerEngine PR #2045 review; this
 // design has no such buffer).  The only allocation is the device workspace of
 // the weight gradient's token split, made once per (device, stream) by the
-// launch layer and kept for the life of the process.
+// launch layer and kept for the life of the process (never while the stream
+// is being captured).
 #include <hip/hip_runtime.h>
 
 #include <atomic>

@@ -1525,14 +1525,19 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
   // ---- end of a half of a split K-grouped tile.  Each half writes its fp32
   // accumulators to its own workspace slot (in register order: entry
   // (i MQ + j) 4 + g of thread tid at ((i MQ + j) 4 + g) NT + tid), waits for
-  // the writes and takes the tile's ticket; the half that draws the second
-  // ticket stores (own + other) -- a commutative sum, so the result does not
-  // depend on which half ends last -- plus the prior value when accumulating,
-  // and resets the ticket for the next launch.  Nothing waits for another
-  // workgroup.  The slots are written and read with device-coherent accesses
-  // (cache policy sc1, what device-scope atomic loads and stores compile to),
-  // so no cache is written back or invalidated; the ticket is a device-scope
-  // atomic add.
+  // the writes and swaps the launch's odd mark into the tile's ticket word:
+  // the half that finds the mark already there ends second and stores (own +
+  // other) -- a commutative sum, so the result does not depend on which half
+  // ends last -- plus the prior value when accumulating, then clears the
+  // word.  The mark is 2 g + 1 for the launch count g of the workspace, so a
+  // word left behind by an earlier launch (one cleared, or one that never
+  // completed) never equals it; clearing keeps repeated launches with one
+  // mark (a replayed graph) correct.  Nothing waits for another workgroup.
+  // The slots are written and read with device-scope accesses (cache policy
+  // sc1: the store is acknowledged once it is visible device-wide, the load
+  // misses every cache that is not coherent device-wide), the stores are
+  // waited for (vmcnt) before the exchange, and the exchange is a
+  // device-scope atomic, so no cache is written back or invalidated.
   constexpr int kSlotFloats = C::BP * C::BQ;
   constexpr int kCoherent = 16;                 // cache policy bit sc1
   auto finish_half = [&](const Tile& t) {
@@ -1564,8 +1569,8 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
     __syncthreads();
     uint32_t* ticket = a.tickets + sid;
     if (tid == 0)
-      S.scan[8] = (int)__hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
+      S.scan[8] = __hip_atomic_exchange(ticket, a.ticket_mark, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT) == a.ticket_mark ? 1 : 0;
     __syncthreads();
     if (S.scan[8] == 0) return;                 // the other half finishes the tile
     const OutView ov = out_view(t);
@@ -1783,40 +1788,50 @@ static int device_cus() {
   return n;
 }
 
-// Token-split workspace of one (device, stream): the ticket counters (zeroed
-// once here; every launch leaves them zeroed) followed by two fp32 slots of
-// one tile per split tile.  Launches on one stream run in order and share it;
-// launches on different streams get different workspaces.  Allocated on the
-// first K-grouped launch of the pair and kept until the process ends.
+// Token-split workspace: the ticket words (one per split tile) followed by two
+// fp32 slots of one tile per split tile.
 constexpr int kSplitTiles = 8 * kSplitPerXcd;
 constexpr size_t kTicketBytes = 4096;
+constexpr size_t kWorkspaceBytes =
+    kTicketBytes + (size_t)2 * kSplitTiles * Cfg::BP * Cfg::BQ * sizeof(float);
 static_assert(kSplitTiles * sizeof(uint32_t) <= kTicketBytes, "ticket area");
+// Per (device, stream): allocated on the first weight-gradient launch of the
+// pair that is not being captured into a graph, its tickets cleared there
+// (synchronously, not on the caller's stream), and kept until the process
+// ends.  Launches on one stream run in order and share it; launches on
+// different streams never do.  `launches` numbers the pair's launches for
+// the ticket marks.
 struct Workspace {
   int dev;
   hipStream_t stream;
   char* base;
+  uint32_t launches;
 };
 static std::mutex g_ws_mutex;
 static std::vector<Workspace> g_ws;
 
-static char* stream_workspace(hipStream_t s) {
+// The pair's workspace and this launch's ticket mark, or nullptr (no split).
+static char* stream_workspace(hipStream_t s, uint32_t* mark) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return nullptr;
   std::lock_guard<std::mutex> lock(g_ws_mutex);
-  for (const Workspace& w : g_ws)
-    if (w.dev == dev && w.stream == s) return w.base;
-  const size_t bytes = kTicketBytes + (size_t)2 * kSplitTiles * Cfg::BP * Cfg::BQ * sizeof(float);
+  for (Workspace& w : g_ws)
+    if (w.dev == dev && w.stream == s) {
+      *mark = 2u * (++w.launches & 0x7FFFFFFFu) + 1u;
+      return w.base;
+    }
   void* p = nullptr;
-  if (hipMalloc(&p, bytes) != hipSuccess) {
+  if (hipMalloc(&p, kWorkspaceBytes) != hipSuccess) {
     (void)hipGetLastError();
     return nullptr;                       // no workspace: launches do not split
   }
-  if (hipMemsetAsync(p, 0, kTicketBytes, s) != hipSuccess) {
+  if (hipMemset(p, 0, kTicketBytes) != hipSuccess) {
     (void)hipGetLastError();
     (void)hipFree(p);
     return nullptr;
   }
-  g_ws.push_back({dev, s, static_cast<char*>(p)});
+  g_ws.push_back({dev, s, static_cast<char*>(p), 1u});
+  *mark = 3u;
   return static_cast<char*>(p);
 }
 
@@ -1829,16 +1844,33 @@ static bool split_enabled() {
   return on;
 }
 
+// Whether work enqueued on `s` now would be captured into a graph.
+static bool capturing(hipStream_t s) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &st) != hipSuccess) {
+    (void)hipGetLastError();
+    return true;                          // unknown: take the path that allocates nothing
+  }
+  return st != hipStreamCaptureStatusNone;
+}
+
 int launch_grouped(int mode, const KernelArgs& a_in, int64_t max_m_per_e, hipStream_t s) {
   KernelArgs a = a_in;
   a.ws = nullptr;
   a.tickets = nullptr;
+  a.ticket_mark = 0;
   const bool kg = mode == kWgrad || mode == kWgradMx;
-  if (kg && a.M > 0 && split_enabled()) {
-    char* w = stream_workspace(s);
+  // (only the bf16 weight gradient splits; a stream being captured never
+  // gets a per-stream workspace: the graph could be replayed on another
+  // stream next to direct launches on this one)
+  if (mode == kWgrad && a.M > 0 && split_enabled()) {
+    char* w = nullptr;
+    uint32_t mark = 0;
+    if (!capturing(s)) w = stream_workspace(s, &mark);
     if (w != nullptr) {
       a.tickets = reinterpret_cast<uint32_t*>(w);
       a.ws = reinterpret_cast<float*>(w + kTicketBytes);
+      a.ticket_mark = mark;
     }
   }
   int64_t tiles;

@@ -38,7 +38,8 @@ struct KernelArgs {
   const int32_t* gather;    // FWD_SWIGLU: row i of the problem is row gather[i] of x (or NULL)
   int64_t T;                // FWD_SWIGLU with gather: rows of x
   float* ws;                // WGRAD token split: 2 slots of 256 x 256 fp32 per split tile
-  uint32_t* tickets;        // one zeroed counter per split tile (every launch leaves them zeroed)
+  uint32_t* tickets;        // one word per split tile (see ticket_mark)
+  uint32_t ticket_mark;     // this launch's odd ticket value, 2 g + 1 for a launch count g
   const uint8_t* p_scale;   // FWD_MX: W's E8M0 scales, blocked [E][ceil(K/128)][N][4];
                             // WGRAD_MX: X^T's, blocked [M/128][K][4]
   const uint8_t* q_scale;   // FWD_MX: X's E8M0 scales, blocked [ceil(K/128)][M][4];

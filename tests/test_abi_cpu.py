@@ -84,8 +84,9 @@ def test_mgrouped_argument_errors(fn):
     assert f(None, None, None, None, 0, 128, 256, 4, 0, None) == OK
 
 
-def test_wgrad_argument_errors():
-    f = L.kgemm_wgrad
+@pytest.mark.parametrize("fn", ["kgemm_wgrad"])
+def test_wgrad_argument_errors(fn):
+    f = getattr(L, fn)
     # (dy, x, offsets, dw, M, N, K, E, accumulate, stream)
     assert f(A, A, A, A, 512, 128, 256, 0, 0, None) == SHAPE
     assert f(A, A, A, A, 512, 120, 252, 4, 0, None) == SHAPE

@@ -174,3 +174,44 @@ def test_lattice_operand_host_and_device_builders_agree():
     assert set(np.unique(t * 8).astype(int)) <= set(range(-8, 9))
     # neighbouring rows and columns differ (a misplaced read changes values)
     assert not np.array_equal(t[:-1], t[1:]) and not np.array_equal(t[:, :-1], t[:, 1:])
+
+
+# ------------------------------------- whole-tensor gates, expert by expert --
+
+def test_expert_gates_pass_fp32_emulation_and_catch_planted_mistakes():
+    """The expert-by-expert whole-tensor gates (tests/parity.py) pass an fp32
+    emulation with no strict failure on non-cancelling elements, and fail an
+    element left at the output sentinel, one element 3 ulps off, and, for the
+    fp32 weight gradient, a nonzero empty expert and one expert's block taken
+    from another expert."""
+    import sys, os
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from parity import SENTINEL, gate_fwd_experts, gate_wgrad_experts
+    from oracle.bf16 import bf16_ulp
+    K = 512
+    off, x, w = _problem(K, 77, sizes=(300, 0, 70, 257), N=136)
+    xb = f64_to_bf16_bits(x)
+    wb = f64_to_bf16_bits(w)
+    got = f64_to_bf16_bits(_emulated_fwd(x, w, off))
+    rep = gate_fwd_experts(xb, wb, off, got)
+    assert rep.passed and rep.nc_strict_fails == 0, str(rep)
+    bad = got.copy()
+    bad[301, 5] = SENTINEL
+    assert not gate_fwd_experts(xb, wb, off, bad).passed
+    bad = got.copy()
+    v = bf16_bits_to_f64(bad[[400]][:, [9]])
+    bad[400, 9] = f64_to_bf16_bits(v + 3 * bf16_ulp(v))[0, 0]
+    r = gate_fwd_experts(xb, wb, off, bad)
+    assert not r.passed and r.nc_strict_fails == 1
+    # fp32 weight gradient
+    dy = bf16_bits_to_f64(normal_bf16_bits((int(off[-1]), 136), 1.0, 951, 1))
+    dyb = f64_to_bf16_bits(dy)
+    E = len(off) - 1
+    dw = grouped_wgrad(dy, x, off, E).astype(np.float32)
+    assert gate_wgrad_experts(dyb, xb, off, dw).passed
+    b2 = dw.copy()
+    b2[1, 3, 3] = 1e-30
+    assert not gate_wgrad_experts(dyb, xb, off, b2).passed
+    b3 = dw.copy()
+    b3[2] = dw[3]
+    assert not gate_wgrad_experts(dyb, xb, off, b3).passed

@@ -8,18 +8,18 @@ compares with the oracle on the same bits:
   * fp32 outputs (wgrad): relative Frobenius <= 1e-4 per expert and overall,
     element-wise accumulation bound, empty experts exactly zero (or exactly
     the prior contents when accumulating).
-Sizes span several 256-wide tiles with ragged tails; the full-size workloads
-are checked on sampled elements plus properties (determinism, untouched
-rows).
+Sizes span several 256-wide tiles with ragged tails; the benchmark
+workloads are checked on every output element (expert by expert), the
+operands past 4 GiB and the longest reductions on sampled elements.
 """
 import numpy as np
 import pytest
 import torch
 
 import moe_grouped_gemm_bf16_amd as mg
-from parity import (SENTINEL, dev_bf16, dev_i32, gate_dgrad_full, gate_dgrad_sampled,
-                    gate_fwd_full, gate_fwd_sampled, gate_wgrad_full, gate_wgrad_sampled,
-                    host_bits, sentinel_bf16)
+from parity import (SENTINEL, dev_bf16, dev_i32, gate_dgrad_experts, gate_dgrad_full,
+                    gate_fwd_experts, gate_fwd_full, gate_wgrad_experts, gate_wgrad_full,
+                    gate_wgrad_sampled, host_bits, sentinel_bf16)
 from workloads import make_workload, normal_bf16_bits, offsets_from_sizes
 
 pytestmark = pytest.mark.gpu
@@ -139,6 +139,35 @@ def test_wgrad_fuzz(case, accumulate):
     r = gate_wgrad_full(dyb, xb, off, dw.cpu().numpy(),
                         prior=None if prior is None else prior.astype(np.float64))
     assert r.passed, str(r)
+
+
+def test_wgrad_first_call_captured_on_fresh_stream():
+    """kgemm_wgrad's first call on a new stream, made while that stream is
+    being captured into a graph: the call allocates nothing and enqueues no
+    memory operation (it runs without the token split, which would otherwise
+    take this heavy expert's tiles), and every replay -- three, with eager
+    work between them -- matches the oracle."""
+    sizes, N, K = [2017, 33, 65, 129, 0, 0, 0, 700], 1544, 776
+    off, M, E, xb, wb, dyb = _inputs(sizes, N, K, 1800, extra_rows=3, x_scale=1.0, w_scale=1.0)
+    dy, x, o = dev_bf16(dyb), dev_bf16(xb), dev_i32(off)
+    out = torch.full((E, N, K), float("nan"), device="cuda")
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    _say("wgrad captured on a fresh stream", sizes, N, K)
+    with torch.cuda.graph(g, stream=s):
+        mg.wgrad(dy, x, o, out=out)
+    torch.cuda.synchronize()
+    other = torch.empty((E, N, K), device="cuda")
+    for rep in range(3):
+        out.fill_(float("nan"))
+        mg.wgrad(dy, x, o, out=other)               # eager, on the current stream
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        r = gate_wgrad_full(dyb, xb, off, out.cpu().numpy())
+        _say("replay", rep, str(r))
+        assert r.passed, f"replay {rep}: {r}"
 
 
 def test_operands_beyond_4gib_sampled():
@@ -288,50 +317,85 @@ def test_side_stream_and_aliases():
 
 
 # ------------------------------------------------------ full-size workloads --
+#
+# Every output element of the benchmark workloads against the oracle (expert
+# by expert, tests/parity.py): outputs pre-filled with a sentinel (bf16) or NaN
+# (fp32), so that an element the kernel never wrote fails; each op launched
+# twice into two live buffers and compared bitwise (run-to-run
+# reproducibility); and no strict one-ulp failure among elements that do not
+# cancel.
+
+def _nan_f32(shape):
+    return torch.full(shape, float("nan"), dtype=torch.float32, device="cuda")
+
+
+def _twice_mgrouped(fn, a, w, o, hint, shape):
+    r1 = fn(a, w, o, hint, out=sentinel_bf16(shape))
+    r2 = fn(a, w, o, hint, out=sentinel_bf16(shape))
+    torch.cuda.synchronize()
+    assert torch.equal(r1.view(torch.int16), r2.view(torch.int16)), "not bitwise reproducible"
+    return host_bits(r1)
+
+
+def _twice_wgrad(dy, x, o, shape):
+    d1 = mg.wgrad(dy, x, o, out=_nan_f32(shape))
+    d2 = mg.wgrad(dy, x, o, out=_nan_f32(shape))
+    torch.cuda.synchronize()
+    assert torch.equal(d1.view(torch.int32), d2.view(torch.int32)), "wgrad not bitwise reproducible"
+    return d1.cpu().numpy()
+
+
+def _assert_bf16_gate(what, rep):
+    _say(what, str(rep), f"nc_strict_fails={rep.nc_strict_fails}")
+    assert rep.passed, what + " " + str(rep)
+    assert rep.nc_strict_fails == 0, f"{what}: strict failures on non-cancelling elements"
+
 
 @pytest.mark.parametrize("cfg", [2, 3])
-def test_uniform_workloads_sampled(cfg):
+def test_uniform_workloads_whole(cfg):
     (wl,) = make_workload(cfg)
     _say(wl.name)
     xb, wb, dyb = wl.x_bits(), wl.w_bits(), wl.dy_bits()
     x, w, dy, o = dev_bf16(xb), dev_bf16(wb), dev_bf16(dyb), dev_i32(wl.offsets)
-    y1 = host_bits(mg.fwd(x, w, o, 4096))
-    y2 = host_bits(mg.fwd(x, w, o, 4096))
-    dx = host_bits(mg.dgrad(dy, w, o, 4096))
-    dw = mg.wgrad(dy, x, o).cpu().numpy()
-    assert np.array_equal(y1, y2), "fwd is not bitwise reproducible"
-    r = gate_fwd_sampled(xb, wb, wl.offsets, y1); assert r.passed, "fwd " + str(r)
-    r = gate_dgrad_sampled(dyb, wb, wl.offsets, dx); assert r.passed, "dgrad " + str(r)
-    r = gate_wgrad_sampled(dyb, xb, wl.offsets, dw); assert r.passed, "wgrad " + str(r)
+    hint = int(wl.sizes().max())
+    yb = _twice_mgrouped(mg.fwd, x, w, o, hint, (wl.M, wl.N))
+    dxb = _twice_mgrouped(mg.dgrad, dy, w, o, hint, (wl.M, wl.K))
+    dw = _twice_wgrad(dy, x, o, (wl.E, wl.N, wl.K))
+    del x, w, dy
+    _assert_bf16_gate("fwd", gate_fwd_experts(xb, wb, wl.offsets, yb))
+    _assert_bf16_gate("dgrad", gate_dgrad_experts(dyb, wb, wl.offsets, dxb))
+    r = gate_wgrad_experts(dyb, xb, wl.offsets, dw)
+    _say("wgrad", str(r))
+    assert r.passed, "wgrad " + str(r)
 
 
 @pytest.mark.parametrize("name", ["a3b_gate_up", "a3b_down"])
-def test_a3b_router_workload_sampled(name):
+def test_a3b_router_workload_whole(name):
     (wl,) = make_workload(4, name)
     _say(wl.name, wl.rows)
     xb, wb, dyb = wl.x_bits(), wl.w_bits(), wl.dy_bits()
     x, w, dy, o = dev_bf16(xb), dev_bf16(wb), dev_bf16(dyb), dev_i32(wl.offsets)
-    y = host_bits(mg.fwd(x, w, o))
-    dx1 = mg.dgrad(dy, w, o)
-    dx2 = mg.dgrad(dy, w, o)
-    assert torch.equal(dx1.view(torch.int16), dx2.view(torch.int16))
-    r = gate_fwd_sampled(xb, wb, wl.offsets, y); assert r.passed, "fwd " + str(r)
-    r = gate_dgrad_sampled(dyb, wb, wl.offsets, host_bits(dx1)); assert r.passed, "dgrad " + str(r)
+    hint = int(wl.sizes().max())
+    yb = _twice_mgrouped(mg.fwd, x, w, o, hint, (wl.M, wl.N))
+    dxb = _twice_mgrouped(mg.dgrad, dy, w, o, hint, (wl.M, wl.K))
+    del x, w, dy
+    _assert_bf16_gate("fwd", gate_fwd_experts(xb, wb, wl.offsets, yb))
+    _assert_bf16_gate("dgrad", gate_dgrad_experts(dyb, wb, wl.offsets, dxb))
 
 
 @pytest.mark.parametrize("name", ["a3b_zipf_gw13", "a3b_zipf_gw2"])
-def test_a3b_zipf_wgrad_sampled(name):
+def test_a3b_zipf_wgrad_whole(name):
     (wl,) = make_workload(5, name)
     _say(wl.name, wl.sizes().tolist())
     xb, dyb = wl.x_bits(), wl.dy_bits()
     x, dy, o = dev_bf16(xb), dev_bf16(dyb), dev_i32(wl.offsets)
-    dw = mg.wgrad(dy, x, o)
-    dw2 = mg.wgrad(dy, x, o)
-    assert torch.equal(dw, dw2), "wgrad is not bitwise reproducible"
-    got = dw.cpu().numpy()
-    r = gate_wgrad_sampled(dyb, xb, wl.offsets, got); assert r.passed, str(r)
+    got = _twice_wgrad(dy, x, o, (wl.E, wl.N, wl.K))
+    del x, dy
     empty = np.flatnonzero(wl.sizes() == 0)
     assert len(empty) == 4 and (got[empty] == 0).all()
+    r = gate_wgrad_experts(dyb, xb, wl.offsets, got)
+    _say("wgrad", str(r))
+    assert r.passed, str(r)
 
 
 # ------------------------------------- gate-up forward with SwiGLU, gathered --
