@@ -39,14 +39,15 @@
  *     without the token split (so it enqueues exactly one kernel and no
  *     memory operation).  If the allocation fails the call still runs,
  *     without the split.  MGEMM_SPLIT=0 turns the split (and the workspace)
- *     off.
+ *     off.  kgemm_wgrad_noalloc never allocates (a static device array).
  *   - Host-detectable errors are returned before anything is enqueued.
  *     Launch failures return MG_ERR_LAUNCH.  Faults during execution surface
  *     at the caller's next synchronisation, like any stream work.  Nothing
  *     throws across this ABI.
  *   - Thread safety: calls may be made concurrently from several threads; the
  *     shared state is a per-device architecture check done once, the
- *     mutex-protected table of per-stream workspaces.
+ *     mutex-protected table of per-stream workspaces and the per-device
+ *     address of kgemm_wgrad_noalloc's static array.
  */
 #ifndef MGEMM_H
 #define MGEMM_H
@@ -262,6 +263,28 @@ mg_status mg_mx_scales_blocked(const void* scales, void* blocked, int64_t rows, 
 mg_status kgemm_wgrad(const void* dy, const void* x, const int32_t* offsets, float* dw,
                       int64_t M, int64_t N, int64_t K, int32_t E, int32_t accumulate,
                       void* stream);
+
+/* Bytes of kgemm_wgrad_noalloc's static device array: 4 KiB of ticket words
+ * and two 256 x 256 fp32 slots for each of at most 128 split tiles. */
+#define MG_NOALLOC_SCRATCH_BYTES (4096 + 2 * 128 * 256 * 256 * 4)
+
+/* kgemm_wgrad for callers that cannot allocate device memory: code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, results and errors as kgemm_wgrad (bitwise the
+ * same results as an uncaptured kgemm_wgrad call), but the token split's
+ * workspace is a static device array of MG_NOALLOC_SCRATCH_BYTES that each
+ * GPU the library runs on holds from load until the process ends; the call
+ * allocates nothing, enqueues only the kernel (no memset) and also splits
+ * while its stream is being captured.  The array's need is bounded by
+ * construction (at most 128 split tiles per launch, whatever the sizes), so
+ * no size is rejected for it.  Every call on one GPU shares that GPU's array:
+ * calls that may run at the same time on one GPU (other streams, other
+ * threads, replays of graphs holding this call) race on it and can give
+ * wrong results; order them on one stream.  Returns MG_ERR_LAUNCH if the
+ * array's device address cannot be obtained. */
+mg_status kgemm_wgrad_noalloc(const void* dy, const void* x, const int32_t* offsets, float* dw,
+                              int64_t M, int64_t N, int64_t K, int32_t E, int32_t accumulate,
+                              void* stream);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* mg_status_str(int32_t status);

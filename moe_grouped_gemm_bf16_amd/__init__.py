@@ -110,6 +110,17 @@ def wgrad(dy: torch.Tensor, x: torch.Tensor, offsets: torch.Tensor, E: int | Non
     return _wgrad("kgemm_wgrad", dy, x, offsets, E, out, accumulate)
 
 
+def wgrad_noalloc(dy: torch.Tensor, x: torch.Tensor, offsets: torch.Tensor, out: torch.Tensor,
+                  E: int | None = None, accumulate: bool = False) -> torch.Tensor:
+    """wgrad through kgemm_wgrad_noalloc: the library allocates nothing (its
+    token-split workspace is a static device array shared by every call on
+    the GPU, so calls that can overlap race).  `out` (fp32 [E, N, K]) is
+    required: the binding allocates nothing either."""
+    if out is None:
+        raise ValueError("wgrad_noalloc needs `out`")
+    return _wgrad("kgemm_wgrad_noalloc", dy, x, offsets, E, out, accumulate)
+
+
 def _wgrad(fn: str, dy, x, offsets, E, out, accumulate):
     _need(dy, "dy", torch.bfloat16, 2)
     _need(x, "x", torch.bfloat16, 2)

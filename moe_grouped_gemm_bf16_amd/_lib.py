@@ -19,6 +19,7 @@ SIGNATURES = {
     "mgemm_fwd": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i64, _vp]),
     "mgemm_dgrad": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i64, _vp]),
     "kgemm_wgrad": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp]),
+    "kgemm_wgrad_noalloc": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp]),
     "mgemm_fwd_swiglu": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32, _i64, _vp]),
     "mgemm_fwd_swiglu_gu": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32, _i64,
                                    _vp]),

@@ -7,7 +7,8 @@
 // design has no such buffer).  The only allocation is the device workspace of
 // the weight gradient's token split, made once per (device, stream) by the
 // launch layer and kept for the life of the process (never while the stream
-// is being captured).
+// is being captured); kgemm_wgrad_noalloc takes it from a static device array
+// instead.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -75,8 +76,9 @@ static_assert(sizeof(mg_gemm_desc) == sizeof(mg::ListDesc) &&
                   offsetof(mg_gemm_desc, ldd) == offsetof(mg::ListDesc, ldd),
               "mg_gemm_desc and the kernel's descriptor must have one layout");
 
-mg_status launch(int mode, const mg::KernelArgs& a, int64_t max_m_per_e, hipStream_t s) {
-  int err = mg::launch_grouped(mode, a, max_m_per_e, s);
+mg_status launch(int mode, const mg::KernelArgs& a, int64_t max_m_per_e, hipStream_t s,
+                 mg::WsKind ws = mg::kWsStream) {
+  int err = mg::launch_grouped(mode, a, max_m_per_e, s, ws);
   return err == hipSuccess ? MG_OK : MG_ERR_LAUNCH;
 }
 
@@ -317,9 +319,11 @@ mg_status mg_mx_scales_blocked(const void* scales, void* blocked, int64_t rows, 
   return err == hipSuccess ? MG_OK : MG_ERR_LAUNCH;
 }
 
-mg_status kgemm_wgrad(const void* dy, const void* x, const int32_t* offsets, float* dw,
-                      int64_t M, int64_t N, int64_t K, int32_t E, int32_t accumulate,
-                      void* stream) {
+namespace {
+
+mg_status wgrad_common(const void* dy, const void* x, const int32_t* offsets, float* dw,
+                       int64_t M, int64_t N, int64_t K, int32_t E, int32_t accumulate,
+                       void* stream, mg::WsKind ws) {
   mg_status st = check_sizes(M, N, K, E);
   if (st != MG_OK) return st;
   if ((int64_t)E * ((N + 255) / 256) * ((K + 255) / 256) > kMaxRows) return MG_ERR_SHAPE;
@@ -338,8 +342,24 @@ mg_status kgemm_wgrad(const void* dy, const void* x, const int32_t* offsets, flo
   a.out = dw;
   a.M = M; a.N = N; a.K = K; a.E = E;
   a.accumulate = accumulate ? 1 : 0;
-  return launch(mg::kWgrad, a, 0, s);
+  return launch(mg::kWgrad, a, 0, s, ws);
 }
+
+}  // namespace
+
+mg_status kgemm_wgrad(const void* dy, const void* x, const int32_t* offsets, float* dw,
+                      int64_t M, int64_t N, int64_t K, int32_t E, int32_t accumulate,
+                      void* stream) {
+  return wgrad_common(dy, x, offsets, dw, M, N, K, E, accumulate, stream, mg::kWsStream);
+}
+
+mg_status kgemm_wgrad_noalloc(const void* dy, const void* x, const int32_t* offsets, float* dw,
+                              int64_t M, int64_t N, int64_t K, int32_t E, int32_t accumulate,
+                              void* stream) {
+  return wgrad_common(dy, x, offsets, dw, M, N, K, E, accumulate, stream, mg::kWsStatic);
+}
+
+static_assert(MG_NOALLOC_SCRATCH_BYTES > 0, "scratch size");
 
 const char* mg_status_str(int32_t status) {
   switch (status) {

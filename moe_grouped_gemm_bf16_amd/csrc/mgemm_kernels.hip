@@ -67,6 +67,7 @@
 #include <type_traits>
 #include <vector>
 
+#include "mgemm.h"
 #include "mgemm_launch.h"
 
 namespace mg {
@@ -1795,6 +1796,8 @@ constexpr size_t kTicketBytes = 4096;
 constexpr size_t kWorkspaceBytes =
     kTicketBytes + (size_t)2 * kSplitTiles * Cfg::BP * Cfg::BQ * sizeof(float);
 static_assert(kSplitTiles * sizeof(uint32_t) <= kTicketBytes, "ticket area");
+constexpr int kMaxDevices = 64;
+
 // Per (device, stream): allocated on the first weight-gradient launch of the
 // pair that is not being captured into a graph, its tickets cleared there
 // (synchronously, not on the caller's stream), and kept until the process
@@ -1835,6 +1838,33 @@ static char* stream_workspace(hipStream_t s, uint32_t* mark) {
   return static_cast<char*>(p);
 }
 
+// The static workspace: one array per device, zero at load, which the
+// no-allocation entry point uses in place of the per-stream one.  Its device
+// address is looked up once per device (hipGetSymbolAddress, with that device
+// current); in host code the array's own name is not a device address.
+static_assert(kWorkspaceBytes == MG_NOALLOC_SCRATCH_BYTES, "the size kgemm_wgrad_noalloc states");
+static __device__ __align__(256) char scratch[kWorkspaceBytes];
+static std::mutex g_scratch_mutex;
+static char* g_scratch_ptr[kMaxDevices];
+static uint32_t g_scratch_launches[kMaxDevices];
+
+static int static_workspace(char** base, uint32_t* mark) {
+  int dev = 0;
+  int err = (int)hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    err = (int)hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess || p == nullptr) return err != hipSuccess ? err : (int)hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = static_cast<char*>(p);
+  }
+  *base = g_scratch_ptr[dev];
+  *mark = 2u * (++g_scratch_launches[dev] & 0x7FFFFFFFu) + 1u;
+  return hipSuccess;
+}
+
 // MGEMM_SPLIT=0 turns the token split off (every tile is then computed whole).
 static bool split_enabled() {
   static const bool on = [] {
@@ -1854,7 +1884,8 @@ static bool capturing(hipStream_t s) {
   return st != hipStreamCaptureStatusNone;
 }
 
-int launch_grouped(int mode, const KernelArgs& a_in, int64_t max_m_per_e, hipStream_t s) {
+int launch_grouped(int mode, const KernelArgs& a_in, int64_t max_m_per_e, hipStream_t s,
+                   WsKind ws_kind) {
   KernelArgs a = a_in;
   a.ws = nullptr;
   a.tickets = nullptr;
@@ -1866,7 +1897,12 @@ int launch_grouped(int mode, const KernelArgs& a_in, int64_t max_m_per_e, hipStr
   if (mode == kWgrad && a.M > 0 && split_enabled()) {
     char* w = nullptr;
     uint32_t mark = 0;
-    if (!capturing(s)) w = stream_workspace(s, &mark);
+    if (ws_kind == kWsStatic) {
+      const int err = static_workspace(&w, &mark);
+      if (err != hipSuccess) return err;
+    } else if (!capturing(s)) {
+      w = stream_workspace(s, &mark);
+    }
     if (w != nullptr) {
       a.tickets = reinterpret_cast<uint32_t*>(w);
       a.ws = reinterpret_cast<float*>(w + kTicketBytes);

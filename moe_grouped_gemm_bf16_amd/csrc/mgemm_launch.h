@@ -59,7 +59,14 @@ int launch_moe_combine(const uint16_t* rows, const int32_t* token_rows, const fl
 int launch_mx_scales_blocked(const uint8_t* src, uint8_t* dst, int64_t rows, int64_t K,
                              int64_t batch, hipStream_t s);
 
+// Where the weight gradient's token split takes its workspace from.
+enum WsKind {
+  kWsStream = 0,   // a device allocation per (device, stream), made on first use
+  kWsStatic = 1,   // the library's static device array (one per device); never allocates
+};
+
 // Enqueue one grouped GEMM on stream `s`.  Returns a hipError_t value.
-int launch_grouped(int mode, const KernelArgs& a, int64_t max_m_per_e, hipStream_t s);
+int launch_grouped(int mode, const KernelArgs& a, int64_t max_m_per_e, hipStream_t s,
+                   WsKind ws = kWsStream);
 
 }  // namespace mg

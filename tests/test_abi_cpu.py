@@ -84,7 +84,7 @@ def test_mgrouped_argument_errors(fn):
     assert f(None, None, None, None, 0, 128, 256, 4, 0, None) == OK
 
 
-@pytest.mark.parametrize("fn", ["kgemm_wgrad"])
+@pytest.mark.parametrize("fn", ["kgemm_wgrad", "kgemm_wgrad_noalloc"])
 def test_wgrad_argument_errors(fn):
     f = getattr(L, fn)
     # (dy, x, offsets, dw, M, N, K, E, accumulate, stream)
