@@ -234,6 +234,25 @@ mg_status kgemm_wgrad_mx(const void* dyt, const void* dyt_scale, const void* xt,
                          const void* xt_scale, const int32_t* offsets, float* dw, int64_t M,
                          int64_t N, int64_t K, int32_t E, int32_t accumulate, void* stream);
 
+/* kgemm_wgrad_mx on operands as the layer holds them, token-major: the same
+ * weight gradient, with
+ *   dw[e, n, k] (= or +=) sum_{offsets[e] <= i < offsets[e+1]} DY[i, n] X[i, k]
+ * where DY, X are the dequantized E4M3 codes dy8 [M, N] and x8 [M, K] (rows of
+ * tokens, quantized along the tokens: one E8M0 scale per 32 consecutive tokens
+ * of a column) -- no transposed copies: the kernel stages 128-token blocks of
+ * the rows and transposes them in its LDS reads (the weight gradient needs
+ * transposed operands, DeepGEMM issue #10).  dy_scale: blocked [M/128][N][4]
+ * (entry [t][n][j] scales dy8[128 t + 32 j .. + 31, n], i.e.
+ * mg_mx_scales_blocked of the per-column scales [N][M/32]); x_scale: blocked
+ * [M/128][K][4].  M a multiple of 128 and every offsets[e] a multiple of 128
+ * (as for kgemm_wgrad_mx); N and K multiples of 16; M/128 N and M/128 K below
+ * 2^29.  Pointers: dy8, x8, dw 16-byte aligned, scales 4-byte aligned.
+ * Results bitwise equal to kgemm_wgrad_mx on the transposed codes with the
+ * same scales.  N == 0 or K == 0 is a no-op.  Allocates nothing. */
+mg_status kgemm_wgrad_mx_tm(const void* dy8, const void* dy_scale, const void* x8,
+                            const void* x_scale, const int32_t* offsets, float* dw, int64_t M,
+                            int64_t N, int64_t K, int32_t E, int32_t accumulate, void* stream);
+
 /* Blocked layout of MXFP8 scales (the torchao PR #3416 "scale blocked format"
  * step, for the layout above): scales: uint8 [batch][rows][K/32] (DEVICE);
  * blocked: uint8 [batch][ceil(K/128)][rows][4] (DEVICE, 4-byte aligned,

@@ -383,6 +383,46 @@ def wgrad_mx(dyt8: torch.Tensor, dyt_scale: torch.Tensor, xt8: torch.Tensor,
     return out
 
 
+def wgrad_mx_tm(dy8: torch.Tensor, dy_scale: torch.Tensor, x8: torch.Tensor,
+                x_scale: torch.Tensor, offsets: torch.Tensor, E: int | None = None,
+                out: torch.Tensor | None = None, accumulate: bool = False) -> torch.Tensor:
+    """MXFP8 K-grouped weight gradient on token-major operands:
+    out[e] (=/+=) DY[rows_e].T @ X[rows_e].
+
+    dy8 [M, N], x8 [M, K]: uint8 E4M3 codes quantized along the tokens (token
+    axis first, as the layer holds them); dy_scale [M/128, N, 4], x_scale
+    [M/128, K, 4]: blocked E8M0 scales (mx_scales_blocked of [N, M/32] and
+    [K, M/32]).  offsets int32 [E+1] with every entry a multiple of 128.
+    out fp32 [E, N, K]."""
+    _need(dy8, "dy8", torch.uint8, 2)
+    _need(x8, "x8", torch.uint8, 2)
+    M, N = dy8.shape
+    M2, K = x8.shape
+    if M2 != M:
+        raise ValueError(f"dy8 is [{M}, N] but x8 is [{M2}, K]")
+    if E is None:
+        E = offsets.numel() - 1
+    _need(dy_scale, "dy_scale", torch.uint8, 3)
+    _need(x_scale, "x_scale", torch.uint8, 3)
+    if tuple(dy_scale.shape) != (M // 128, N, 4) or tuple(x_scale.shape) != (M // 128, K, 4):
+        raise ValueError(f"blocked scales must be [{M // 128}, {N}, 4] and [{M // 128}, {K}, 4]")
+    _offsets(offsets, E, dy8.device)
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs an `out` to add into")
+        out = torch.empty((E, N, K), dtype=torch.float32, device=dy8.device)
+    else:
+        _need(out, "out", torch.float32, 3)
+        if tuple(out.shape) != (E, N, K):
+            raise ValueError(f"out must be [{E}, {N}, {K}]")
+    with torch.cuda.device(dy8.device):
+        st = LIB.kgemm_wgrad_mx_tm(dy8.data_ptr(), dy_scale.data_ptr(), x8.data_ptr(),
+                                   x_scale.data_ptr(), offsets.data_ptr(), out.data_ptr(),
+                                   M, N, K, E, 1 if accumulate else 0, _stream(dy8))
+    check(st, "kgemm_wgrad_mx_tm")
+    return out
+
+
 def moe_combine(rows: torch.Tensor, token_rows: torch.Tensor,
                 weights: torch.Tensor | None = None, out: torch.Tensor | None = None
                 ) -> torch.Tensor:

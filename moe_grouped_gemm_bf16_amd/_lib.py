@@ -29,6 +29,7 @@ SIGNATURES = {
     "mgemm_fwd_mx": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i64, _vp]),
     "mg_mx_scales_blocked": (_i32, [_vp, _vp, _i64, _i64, _i64, _vp]),
     "kgemm_wgrad_mx": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp]),
+    "kgemm_wgrad_mx_tm": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp]),
     "mg_check_list_host": (_i32, [_vp, _i32]),
     "mg_status_str": (ctypes.c_char_p, [_i32]),
     "mg_abi_version": (_i32, []),

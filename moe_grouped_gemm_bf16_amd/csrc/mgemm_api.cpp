@@ -248,6 +248,39 @@ mg_status mgemm_fwd_mx(const void* x, const void* x_scale, const void* w, const 
   return launch(mg::kFwdMx, a, max_m_per_e, s);
 }
 
+mg_status kgemm_wgrad_mx_tm(const void* dy8, const void* dy_scale, const void* x8,
+                            const void* x_scale, const int32_t* offsets, float* dw, int64_t M,
+                            int64_t N, int64_t K, int32_t E, int32_t accumulate, void* stream) {
+  mg_status st = check_sizes(M, N, K, E);
+  if (st != MG_OK) return st;
+  // tokens in 128-step stages; rows of N and K code bytes start 16-byte
+  // aligned; 32-bit buffer offsets over 128 token rows and the blocked scales
+  constexpr int64_t k2G = int64_t(1) << 31;
+  const int64_t ks = M / 128;
+  if ((M & 127) || (N & 15) || (K & 15) || ks * N * 4 >= k2G || ks * K * 4 >= k2G)
+    return MG_ERR_SHAPE;
+  if (N == 0 || K == 0) return MG_OK;
+  if (!offsets || !dw || (M > 0 && (!dy8 || !x8 || !dy_scale || !x_scale))) return MG_ERR_NULL;
+  if ((M > 0 && (!aligned16(dy8) || !aligned16(x8) ||
+                 (reinterpret_cast<uintptr_t>(dy_scale) & 3u) ||
+                 (reinterpret_cast<uintptr_t>(x_scale) & 3u))) ||
+      !aligned16(dw) || (reinterpret_cast<uintptr_t>(offsets) & 3u))
+    return MG_ERR_ALIGN;
+  if ((st = check_device()) != MG_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = maybe_validate(offsets, E, M, s, 128)) != MG_OK) return st;
+  mg::KernelArgs a{};
+  a.p_src = x8;
+  a.q_src = dy8;
+  a.p_scale = static_cast<const uint8_t*>(x_scale);
+  a.q_scale = static_cast<const uint8_t*>(dy_scale);
+  a.offsets = offsets;
+  a.out = dw;
+  a.M = M; a.N = N; a.K = K; a.E = E;
+  a.accumulate = accumulate ? 1 : 0;
+  return launch(mg::kWgradMxT, a, 0, s);
+}
+
 mg_status kgemm_wgrad_mx(const void* dyt, const void* dyt_scale, const void* xt,
                          const void* xt_scale, const int32_t* offsets, float* dw, int64_t M,
                          int64_t N, int64_t K, int32_t E, int32_t accumulate, void* stream) {

@@ -719,8 +719,9 @@ __device__ __forceinline__ void decode_kgrouped(int r, int k, int u_in_chunk, co
 template <int MODE, int BP, int BQ>
 struct TileSeq {
   int x, c, nx, count, lo, j, ie;
-  static constexpr bool KG = MODE == kWgrad || MODE == kWgradMx;   // K-grouped
-  static constexpr int SBK = MODE == kWgradMx ? 128 : kBK;         // reduction steps per stage
+  static constexpr bool MXW = MODE == kWgradMx || MODE == kWgradMxT;   // MXFP8 weight gradient
+  static constexpr bool KG = MODE == kWgrad || MXW;                      // K-grouped
+  static constexpr int SBK = MXW ? 128 : kBK;                            // reduction steps per stage
 
   __device__ __forceinline__ void init(const Sched& S) {
     x = blockIdx.x & 7;
@@ -752,7 +753,7 @@ struct TileSeq {
       const int v = rho + j * nx;                 // piece of the chunk
       const int u = sp ? v >> 1 : v;
       decode_kgrouped<BP, BQ>(r, (x - r) & 7, u, S, MODE == kWgrad && S.whole, t);
-      if (MODE == kWgradMx) {
+      if (MXW) {
         // whole 128-token stages (a no-op for offsets that are multiples of
         // 128, as documented; others give wrong sums but only aligned,
         // in-bounds loads: M is a multiple of 128)
@@ -854,11 +855,12 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
                                           int Pdim, int Qdim) {
   constexpr bool SWI = MODE == kFwdSwiglu;
   constexpr bool LIST = MODE == kList;
-  constexpr bool MX = MODE == kFwdMx || MODE == kWgradMx;
-  constexpr bool KG = MODE == kWgrad || MODE == kWgradMx;   // K-grouped, fp32 out
+  constexpr bool MXT = MODE == kWgradMxT;      // MXFP8 weight gradient on token-major operands
+  constexpr bool MX = MODE == kFwdMx || MODE == kWgradMx || MXT;
+  constexpr bool KG = MODE == kWgrad || MODE == kWgradMx || MXT;   // K-grouped, fp32 out
   constexpr bool DG = MODE == kDgrad || MODE == kDgradSwiglu;
-  constexpr bool P_RS = DG || MODE == kWgrad;   // P is R-strided for dgrad and wgrad
-  constexpr bool Q_RS = MODE == kWgrad;    // Q is R-strided for wgrad
+  constexpr bool P_RS = DG || MODE == kWgrad || MXT;   // P is R-strided for dgrad and wgrad
+  constexpr bool Q_RS = MODE == kWgrad || MXT;        // Q is R-strided for wgrad
   constexpr int SPW = C::SEGS_PER_WAVE;
   // element bytes, and reduction steps per stage (a staged row is kRowB bytes)
   constexpr int ES = MX ? 1 : 2;
@@ -868,6 +870,7 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
 
   int ldP, ldQ;
   if (MODE == kWgradMx) { ldP = (int)a.M; ldQ = (int)a.M; }   // X^T, dY^T rows of M tokens
+  else if (MXT) { ldP = (int)a.K; ldQ = (int)a.N; }           // X8, dY8 rows of K, N codes
   else if (MODE == kFwd || SWI || LIST || MX) { ldP = (int)a.K; ldQ = (int)a.K; }   // LIST: per tile
   else if (DG) { ldP = (int)a.K; ldQ = (int)a.N; }
   else { ldP = (int)a.K; ldQ = (int)a.N; }
@@ -893,7 +896,16 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
 #pragma unroll
   for (int j = 0; j < SPW; ++j) {
     const int p = (seg0 + j) * 1024 + lane * 16;             // byte within the tile
-    if (rs) {                                                // [kBK][outer]
+    if (MXT) {                                               // [128 tokens][outer] fp8
+      // rows of outer bytes in 16-byte chunks; chunk c of token row r sits at
+      // chunk c ^ (2 (r % 8)), so that the transpose reads of 8 consecutive
+      // rows at two neighbouring chunks hit 16 distinct chunks
+      const int r = p / outer, pc = (p >> 4) % (outer / 16);
+      const int c = pc ^ (2 * (r & 7));
+      voff[j] = (uint32_t)(r * ld + 16 * c);
+      col[j] = 16 * c;
+      orow[j] = 0;
+    } else if (rs) {                                         // [kBK][outer]
       const int r = p / (outer * 2), pc = (p >> 4) % (outer / 8);
       const int c = pc ^ rs_swz(r & 3);
       voff[j] = (uint32_t)(r * ld + 8 * c) * 2u;
@@ -926,9 +938,17 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
   // MXFP8 data loads, without per-load tables: load d of a wave covers rows
   // 8 (seg0 + d) + lane / 8 of its operand tile, and with seg0 a multiple of
   // 8 the swizzled chunk of that row is (lane % 8) ^ (lane / 8) ^ (d % 4).
-  static_assert(!MX || (SPW % 8 == 0 && kRowChunks == 8), "MXFP8 load plan");
+  static_assert(!MX || MXT || (SPW % 8 == 0 && kRowChunks == 8), "MXFP8 load plan");
   const int mx_c0 = (lane & 7) ^ (lane >> 3);
   const uint32_t mx_rowoff = (uint32_t)(seg0 * 8 + (lane >> 3)) * (uint32_t)ld;
+  // Token-major fp8 loads, without per-load tables: load d of a wave covers
+  // token rows 4 (seg0 + d) + lane / 16 of its operand tile, logical chunk
+  // lane % 16, which with seg0 a multiple of 2 sits at chunk
+  // (lane % 16) ^ (2 ((4 (d % 2) + lane / 16) % 8)).
+  static_assert(!MXT || (SPW % 2 == 0 && C::BP == 256), "token-major fp8 load plan");
+  const uint32_t mxt_row = (uint32_t)(4 * seg0 + (lane >> 4)) * (uint32_t)ld;
+  const uint32_t mxt_c0 = 16u * (uint32_t)((lane & 15) ^ (2 * ((lane >> 4) & 7)));
+  const uint32_t mxt_c1 = 16u * (uint32_t)((lane & 15) ^ (2 * ((4 + (lane >> 4)) & 7)));
   const uint32_t sc_base = lds_u32(lds) + (uint32_t)C::LDS +
                            (wP ? 0u : (uint32_t)C::BP * 4u) + (uint32_t)(4 * kScRows) * w4;
 
@@ -939,6 +959,9 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
     if (MODE == kWgradMx) {        // P = X^T rows k (R = i), Q = dY^T rows n (R = i)
       P += (int64_t)t.p0 * a.M + t.r_begin;
       Q += (int64_t)t.q0 * a.M + t.r_begin;
+    } else if (MXT) {              // P = X8 [i][k] R-strided, Q = dY8 [i][n] R-strided
+      P += (int64_t)t.r_begin * a.K + t.p0;
+      Q += (int64_t)t.r_begin * a.N + t.q0;
     } else if (MODE == kFwd || MX) {   // P = W[e] rows n (R = k), Q = X rows m (R = k)
       P += ((int64_t)t.e * a.N + t.p0) * a.K * ES;
       Q += (int64_t)t.q0 * a.K * ES;
@@ -1002,8 +1025,8 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
         // per expert.  A row past the tile's valid rows reads zero.
         const int row = kScRows * w4 + lane;
         const int base = wP ? t.p0 : t.q0;
-        if (MODE == kWgradMx) {
-          // X^T's and dY^T's scales over all M tokens: the tile's stages start
+        if (MODE == kWgradMx || MXT) {
+          // the operands' scales over all M tokens: the tile's stages start
           // at token stage r_begin / 128 (expert boundaries are multiples of 128)
           const int rows_total = wP ? Pdim : Qdim, ks = (int)((a.M + 127) / 128);
           const int end = rows_total;
@@ -1069,16 +1092,16 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
 
   auto stage_rsrc = [&](int r0) {
     if (!rs) return p_rc;
-    const int rr = min(p_red - r0, kBK), oc = min(p_nouter, outer);
-    const uint32_t bytes = rr > 0 && oc > 0 ? ((uint32_t)(rr - 1) * ld + oc) * 2u : 0u;
-    return make_rsrc(p_src + (int64_t)r0 * ld * 2, bytes);
+    const int rr = min(p_red - r0, BKE), oc = min(p_nouter, outer);
+    const uint32_t bytes = rr > 0 && oc > 0 ? ((uint32_t)(rr - 1) * ld + oc) * (uint32_t)ES : 0u;
+    return make_rsrc(p_src + (int64_t)r0 * ld * ES, bytes);
   };
   // Load d of the stage whose data go to `dst` (and, MXFP8, whose scales go
   // to `sdst`, loaded with the first loads); returns the vector-memory
   // operations issued.
   auto dma_one = [&](const i32x4& rsrc, uint32_t dst, uint32_t sdst, int d, int r0) {
     uint32_t off;
-    if (MX) {
+    if (MX && !MXT) {
       const int cj = 16 * (mx_c0 ^ (d & 3));
       uint32_t ro = mx_rowoff;
       // The weight gradient runs at the register limit: left alone, the
@@ -1088,6 +1111,11 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
       if constexpr (MODE == kWgradMx) asm volatile("" : "+v"(ro));
       off = (ro + (uint32_t)d * 8u * (uint32_t)ld + (uint32_t)(cj + r0)) |
             (r0 + cj < p_red ? 0u : kOOB);
+    } else if (MXT) {
+      uint32_t ro = mxt_row;
+      asm volatile("" : "+v"(ro));
+      const uint32_t cj = (d & 1) ? mxt_c1 : mxt_c0;
+      off = (ro + (uint32_t)d * 4u * (uint32_t)ld + cj) | ((int)cj < p_nouter ? 0u : kOOB);
     } else if (SWI || LIST)
       off = (tvoff[d] + (uint32_t)r0 * 2u) |
             (r0 + col[d] < p_red && ((tmask >> d) & 1u) ? 0u : kOOB);
@@ -1155,6 +1183,23 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
 #pragma unroll
     for (int kk = 0; kk < KR; ++kk) offQ[kk] = rc_off(wq * C::WTQ, kk);
   }
+  // Token-major fp8 tiles [128 tokens][256 outer bytes] (MXFP8 weight gradient
+  // on token-major operands), read with the 8-bit LDS transpose load: within
+  // each 16-lane group, lane i receives byte i % 8 of the 8-byte words that
+  // lanes 2 j + i / 8 address, j = 0..7.  So lane L of the group addresses
+  // token row 16 h + L / 2 (+ 8 q for its q-th read) at outer bytes
+  // o0 + 8 (L % 2), and lane i receives outer o0 + i of 8 consecutive tokens.
+  // The fragment of outer block i sits 2 i chunks further, which with the
+  // row swizzle is an XOR of 32 i on the lane's base.
+  auto mxt_off = [&](int obase) {
+    const int L = lane & 15, g16 = (lane >> 4) & 1;
+    const int row = 16 * h + (L >> 1);
+    const int chunk = ((obase >> 4) + g16) ^ (2 * (L >> 1));
+    return (uint32_t)(row * 256 + 16 * chunk + 8 * (L & 1));
+  };
+  const uint32_t mxt_offP = MXT ? mxt_off(wp * C::WTP) : 0u;
+  const uint32_t mxt_offQ = MXT ? mxt_off(wq * C::WTQ) : 0u;
+  static_assert(!MXT || (C::BP == 256 && C::BQ == 256), "token-major fp8 rows of 256 bytes");
 
   f32x16 acc[C::MP][C::MQ];
 #pragma unroll
@@ -1204,6 +1249,30 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
       f.sq = pk(4);
       const char* tp = lds + (g % kStages) * C::STAGE;
       const char* tq = tp + C::P_BYTES;
+      if constexpr (MXT) {
+        // four transpose reads of 8 tokens each: tokens 16 h + 0..15 and
+        // 32 + 16 h + 0..15 of the slice, the operand layout of the scaled product
+        auto frag8t = [&](const char* tile, uint32_t off) {
+          typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
+          typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+          auto tr = [&](uint32_t o) {
+            return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (lds_i32x2*)((__attribute__((address_space(3))) char*)(
+                                 (__attribute__((address_space(3))) void*)tile) + o));
+          };
+          const uint32_t base = off + (uint32_t)(kk * 64 * 256);
+          const i32x2 a0 = tr(base), a1 = tr(base + 8 * 256), a2 = tr(base + 32 * 256),
+                      a3 = tr(base + 40 * 256);
+          const i32x4 lo = __builtin_shufflevector(a0, a1, 0, 1, 2, 3);
+          const i32x4 hi = __builtin_shufflevector(a2, a3, 0, 1, 2, 3);
+          return (i32x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        };
+#pragma unroll
+        for (int i = 0; i < C::MP; ++i) f.p[i] = frag8t(tp, mxt_offP ^ (uint32_t)(32 * i));
+#pragma unroll
+        for (int j = 0; j < C::MQ; ++j) f.q[j] = frag8t(tq, mxt_offQ ^ (uint32_t)(32 * j));
+        return;
+      }
       // chunk 2 kk' + h of a 128-byte row: offP[kk'] = offP[0] ^ (kk' << 5) (the
       // row base has no low bits and (2 kk' + h) ^ swz = (h ^ swz) ^ 2 kk'), which
       // keeps one address register per operand instead of four
@@ -1700,8 +1769,8 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
 template <int MODE, class C>
 __global__ __launch_bounds__(C::NT)
 void grouped_gemm_kernel(KernelArgs a) {
-  constexpr bool KG = MODE == kWgrad || MODE == kWgradMx;
-  constexpr bool MXM = MODE == kFwdMx || MODE == kWgradMx;
+  constexpr bool KG = MODE == kWgrad || MODE == kWgradMx || MODE == kWgradMxT;
+  constexpr bool MXM = MODE == kFwdMx || MODE == kWgradMx || MODE == kWgradMxT;
   __shared__ __attribute__((aligned(16))) char lds[C::LDS + (MXM ? kStages * (C::BP + C::BQ) * 4 : 0)];
   // keys [64] | scan [16] | mine [2 kMaxExperts + 8] | pref [E+1] | offs [E+1] | inv [E]
   // (keys and mine 16-byte aligned: they are read four entries at a time)
@@ -1890,7 +1959,7 @@ int launch_grouped(int mode, const KernelArgs& a_in, int64_t max_m_per_e, hipStr
   a.ws = nullptr;
   a.tickets = nullptr;
   a.ticket_mark = 0;
-  const bool kg = mode == kWgrad || mode == kWgradMx;
+  const bool kg = mode == kWgrad || mode == kWgradMx || mode == kWgradMxT;
   // (only the bf16 weight gradient splits; a stream being captured never
   // gets a per-stream workspace: the graph could be replayed on another
   // stream next to direct launches on this one)
@@ -1948,6 +2017,9 @@ int launch_grouped(int mode, const KernelArgs& a_in, int64_t max_m_per_e, hipStr
       break;
     case kWgradMx:
       hipLaunchKernelGGL((grouped_gemm_kernel<kWgradMx, CfgMx>), g, dim3(CfgMx::NT), 0, s, a);
+      break;
+    case kWgradMxT:
+      hipLaunchKernelGGL((grouped_gemm_kernel<kWgradMxT, CfgMx>), g, dim3(CfgMx::NT), 0, s, a);
       break;
     case kDgradSwiglu:
       hipLaunchKernelGGL((grouped_gemm_kernel<kDgradSwiglu, Cfg>), g, b, 0, s, a);

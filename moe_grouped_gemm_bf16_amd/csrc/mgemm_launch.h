@@ -6,7 +6,7 @@
 namespace mg {
 
 enum { kFwd = 0, kDgrad = 1, kWgrad = 2, kFwdSwiglu = 3, kList = 4, kFwdMx = 5, kWgradMx = 6,
-       kDgradSwiglu = 7 };
+       kDgradSwiglu = 7, kWgradMxT = 8 };
 
 // Largest expert count a launch accepts: the device-side scheduler keeps the
 // per-expert tile prefix in LDS, two entries per thread of a 512-thread block.
@@ -24,13 +24,15 @@ struct ListDesc {
 
 struct KernelArgs {
   const void* p_src;        // FWD/DGRAD: W [E,N,K]; FWD_SWIGLU: W13 [E,N=2I,K]; WGRAD: X [M,K];
-                            // FWD_MX: W8 [E,N,K] E4M3 codes; WGRAD_MX: X^T [K,M] E4M3 codes
+                            // FWD_MX: W8 [E,N,K] E4M3 codes; WGRAD_MX: X^T [K,M] E4M3 codes;
+                            // WGRAD_MX_T: X8 [M,K] E4M3 codes (token-major)
   const void* q_src;        // FWD: X [M,K]; FWD_SWIGLU: X [M or T,K]; DGRAD/WGRAD: dY [M,N];
-                            // FWD_MX: X8 [M,K] E4M3 codes; WGRAD_MX: dY^T [N,M] E4M3 codes
+                            // FWD_MX: X8 [M,K] E4M3 codes; WGRAD_MX: dY^T [N,M] E4M3 codes;
+                            // WGRAD_MX_T: dY8 [M,N] E4M3 codes (token-major)
   const int32_t* offsets;   // [E+1], device
   void* out;                // FWD: Y [M,N] bf16; FWD_SWIGLU: H [M,N/2] bf16; DGRAD: dX [M,K] bf16;
                             // DGRAD_SWIGLU: dGU [M,2K] bf16 (dg | du);
-                            // WGRAD, WGRAD_MX: dW [E,N,K] fp32
+                            // WGRAD, WGRAD_MX, WGRAD_MX_T: dW [E,N,K] fp32
   int64_t M, N, K;
   int32_t E;
   int32_t accumulate;       // WGRAD only: add into `out`
@@ -41,9 +43,9 @@ struct KernelArgs {
   uint32_t* tickets;        // one word per split tile (see ticket_mark)
   uint32_t ticket_mark;     // this launch's odd ticket value, 2 g + 1 for a launch count g
   const uint8_t* p_scale;   // FWD_MX: W's E8M0 scales, blocked [E][ceil(K/128)][N][4];
-                            // WGRAD_MX: X^T's, blocked [M/128][K][4]
+                            // WGRAD_MX, WGRAD_MX_T: X's, blocked [M/128][K][4]
   const uint8_t* q_scale;   // FWD_MX: X's E8M0 scales, blocked [ceil(K/128)][M][4];
-                            // WGRAD_MX: dY^T's, blocked [M/128][N][4]
+                            // WGRAD_MX, WGRAD_MX_T: dY's, blocked [M/128][N][4]
   void* aux;                // FWD_SWIGLU: optional gu [M, N] bf16 out (pre-activation g | u);
                             // DGRAD_SWIGLU: gu [M, 2K] bf16 in
 };

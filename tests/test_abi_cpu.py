@@ -141,6 +141,25 @@ def test_wgrad_mx_argument_errors():
     assert f(None, None, None, None, None, None, 512, 0, 256, 4, 0, None) == OK   # empty dw
 
 
+def test_wgrad_mx_tm_argument_errors():
+    f = L.kgemm_wgrad_mx_tm
+    # (dy8, dy_scale, x8, x_scale, offsets, dw, M, N, K, E, accumulate, stream)
+    assert f(A, A, A, A, A, A, 512, 128, 256, 0, 0, None) == SHAPE        # E < 1
+    assert f(A, A, A, A, A, A, 500, 128, 256, 4, 0, None) == SHAPE        # M % 128
+    assert f(A, A, A, A, A, A, 512, 136, 256, 4, 0, None) == SHAPE        # N % 16
+    assert f(A, A, A, A, A, A, 512, 128, 264, 4, 0, None) == SHAPE        # K % 16
+    assert f(A, A, A, A, A, A, 1 << 31, 128, 256, 4, 0, None) == SHAPE    # M too large
+    assert f(None, A, A, A, A, A, 512, 128, 256, 4, 0, None) == NUL
+    assert f(A, A, A, None, A, A, 512, 128, 256, 4, 0, None) == NUL
+    assert f(A, A, A, A, None, A, 512, 128, 256, 4, 0, None) == NUL
+    assert f(A, A, A, A, A, None, 512, 128, 256, 4, 0, None) == NUL
+    assert f(A + 8, A, A, A, A, A, 512, 128, 256, 4, 0, None) == ALIGN
+    assert f(A, A, A + 8, A, A, A, 512, 128, 256, 4, 0, None) == ALIGN
+    assert f(A, A + 2, A, A, A, A, 512, 128, 256, 4, 0, None) == ALIGN
+    assert f(A, A, A, A, A, A + 8, 512, 128, 256, 4, 0, None) == ALIGN
+    assert f(None, None, None, None, None, None, 512, 0, 256, 4, 0, None) == OK   # empty dw
+
+
 def test_swiglu_backward_and_saving_forward_argument_errors():
     f = L.mgemm_dgrad_swiglu
     # (dy, w2, gu, offsets, dgu, M, N, I, E, max_m_per_e, stream)

@@ -273,6 +273,79 @@ def test_wgrad_mx_rejects_bad_shapes():
                     dev_i32(offsets_from_sizes([96])), 1)
 
 
+# ------------------------------------ MXFP8 wgrad on token-major operands --
+
+# (expert sizes in multiples of 128, N, K, scale spread); N and K multiples of 16
+WG_MX_TM_CASES = [
+    ([128, 0, 384, 256], 272, 144, 2),
+    ([1024], 528, 272, 1),
+    ([0, 128], 16, 16, 0),
+    ([128, 128, 128, 128, 128, 0, 640], 256, 256, 1),
+    ([2048, 128, 0, 256], 144, 528, 3),
+    ([384, 256], 1040, 48, 1),
+]
+
+
+@pytest.mark.parametrize("case", range(len(WG_MX_TM_CASES)))
+@pytest.mark.parametrize("accumulate", [False, True])
+def test_wgrad_mx_token_major(case, accumulate):
+    """kgemm_wgrad_mx_tm on dY [M, N] and X [M, K] codes as the layer holds
+    them: within the oracle's MXFP8 gate, and bitwise equal to kgemm_wgrad_mx
+    on the transposed codes with the same scales (empty experts, a stage of
+    rows owned by no expert, ragged N and K)."""
+    sizes, N, K, spread = WG_MX_TM_CASES[case]
+    _say("wgrad_mx_tm", sizes, N, K, spread, "accumulate" if accumulate else "")
+    off, M, dyt8, dyts, xt8, xts = _wg_inputs(sizes, N, K, spread, 50 + case)
+    E = len(sizes)
+    prior = None
+    outs = []
+    for _ in range(2):
+        if accumulate:
+            prior = np.random.default_rng(case).standard_normal((E, N, K)).astype(np.float32)
+            outs.append(torch.from_numpy(prior.copy()).cuda())
+        else:
+            outs.append(torch.full((E, N, K), float("nan"), dtype=torch.float32, device="cuda"))
+    bd, bx = _u8(mx_scales_blocked(dyts)), _u8(mx_scales_blocked(xts))
+    o = dev_i32(off)
+    mg.wgrad_mx_tm(_u8(np.ascontiguousarray(dyt8.T)), bd, _u8(np.ascontiguousarray(xt8.T)), bx,
+                   o, E, out=outs[0], accumulate=accumulate)
+    mg.wgrad_mx(_u8(dyt8), bd, _u8(xt8), bx, o, E, out=outs[1], accumulate=accumulate)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0].view(torch.int32), outs[1].view(torch.int32)), \
+        "token-major result differs from the transposed-operand one"
+    rep = _wg_gate(off, dyt8, dyts, xt8, xts, outs[0].cpu().numpy(),
+                   prior=None if prior is None else prior.astype(np.float64))
+    assert rep.passed, str(rep)
+
+
+def test_wgrad_mx_token_major_rejects_bad_shapes():
+    z = lambda *sh: torch.zeros(sh, dtype=torch.uint8, device="cuda")
+    with pytest.raises(mg.MgemmError):        # N = 24 is not a multiple of 16
+        mg.wgrad_mx_tm(z(128, 24), z(1, 24, 4), z(128, 16), z(1, 16, 4),
+                       dev_i32(offsets_from_sizes([128])), 1)
+
+
+@pytest.mark.parametrize("name", ["a3b_zipf_gw13", "a3b_zipf_gw2"])
+def test_a3b_zipf_wgrad_mx_token_major(name):
+    """The skewed 30B-A3B weight gradients on token-major MXFP8 operands:
+    bitwise equal to the transposed-operand call on every element."""
+    (wl,) = make_workload(5, name)
+    sizes = [((int(s) + 127) // 128) * 128 for s in wl.sizes()]
+    off = offsets_from_sizes(sizes)
+    M, N, K, E = int(off[-1]), wl.N, wl.K, wl.E
+    _say("a3b wgrad mx token-major", name, M, N, K, E)
+    dyt8 = mx_e4m3_codes((N, M), 8600, wl.tag, 1)
+    xt8 = mx_e4m3_codes((K, M), 8600, wl.tag, 2)
+    bd = _u8(mx_scales_blocked(mx_e8m0_codes((N, M // 32), 121, 1, 8600, wl.tag, 3)))
+    bx = _u8(mx_scales_blocked(mx_e8m0_codes((K, M // 32), 121, 1, 8600, wl.tag, 4)))
+    o = dev_i32(off)
+    a = mg.wgrad_mx_tm(_u8(np.ascontiguousarray(dyt8.T)), bd, _u8(np.ascontiguousarray(xt8.T)),
+                       bx, o, E, out=torch.full((E, N, K), float("nan"), device="cuda"))
+    b = mg.wgrad_mx(_u8(dyt8), bd, _u8(xt8), bx, o, E)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
 @pytest.mark.parametrize("name", ["a3b_zipf_gw13", "a3b_zipf_gw2"])
 def test_a3b_zipf_wgrad_mx_sampled(name):
     """The skewed 30B-A3B weight gradients with MXFP8 operands, experts padded
