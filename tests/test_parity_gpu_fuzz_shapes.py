@@ -1,4 +1,5 @@
-"""Seeded random-shape fuzz of the MXFP8 forward and weight gradient, the
+"""Seeded random-shape fuzz of the MXFP8 forward and weight gradients (on
+transposed and on token-major operands), the
 SwiGLU backward and the token-order combine against the oracle (needs an
 MI355X).  Ragged and empty experts, reductions of one block to several
 stages, widths that are not multiples of the tile."""
@@ -67,6 +68,37 @@ def test_fuzz_wgrad_mx(seed):
     xts = mx_e8m0_codes((K, M // 32), 121, 2, 2100, seed, 4)
     out = mg.wgrad_mx(_u8(dyt8), _u8(mx_scales_blocked(dyts)), _u8(xt8),
                       _u8(mx_scales_blocked(xts)), dev_i32(off), E)
+    got = out.cpu().numpy()
+    exact = grouped_wgrad_mx(dyt8, dyts, xt8, xts, off, E)
+    mag = grouped_wgrad(np.abs(mx_dequant(dyt8, dyts)).T, np.abs(mx_dequant(xt8, xts)).T, off, E)
+    sz = np.diff(np.asarray(off, np.int64))
+    k_red = np.broadcast_to(np.maximum(sz, 1)[:, None, None], exact.shape)
+    empty = np.broadcast_to((sz == 0)[:, None, None], exact.shape)
+    rep = check_fp32_mx(got, exact, mag, k_red, empty_mask=empty)
+    assert rep.passed, str(rep)
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_fuzz_wgrad_mx_token_major(seed):
+    """The token-major MXFP8 weight gradient on random shapes (N, K multiples
+    of 16): within the oracle's gate and bitwise equal to the call on the
+    transposed codes."""
+    rng = np.random.default_rng(2500 + seed)
+    E = int(rng.integers(1, 6))
+    sizes = _sizes(rng, E, 5, multiple=128)
+    N = 16 * int(rng.integers(1, 40)); K = 16 * int(rng.integers(1, 40))
+    print("[case] fuzz wgrad_mx_tm", seed, sizes, N, K, flush=True)
+    off = offsets_from_sizes(sizes)
+    M = int(off[-1]) + 128
+    dyt8 = mx_e4m3_codes((N, M), 2600, seed, 1); xt8 = mx_e4m3_codes((K, M), 2600, seed, 2)
+    dyts = mx_e8m0_codes((N, M // 32), 121, 2, 2600, seed, 3)
+    xts = mx_e8m0_codes((K, M // 32), 121, 2, 2600, seed, 4)
+    bd, bx, o = _u8(mx_scales_blocked(dyts)), _u8(mx_scales_blocked(xts)), dev_i32(off)
+    out = mg.wgrad_mx_tm(_u8(dyt8.T), bd, _u8(xt8.T), bx, o, E,
+                         out=torch.full((E, N, K), float("nan"), device="cuda"))
+    ref = mg.wgrad_mx(_u8(dyt8), bd, _u8(xt8), bx, o, E)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int32), ref.view(torch.int32))
     got = out.cpu().numpy()
     exact = grouped_wgrad_mx(dyt8, dyts, xt8, xts, off, E)
     mag = grouped_wgrad(np.abs(mx_dequant(dyt8, dyts)).T, np.abs(mx_dequant(xt8, xts)).T, off, E)
