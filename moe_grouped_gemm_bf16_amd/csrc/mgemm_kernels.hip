@@ -1312,8 +1312,9 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
   auto wait_stage = [&](int g) {
     int n = issued - after[g % kStages];
     n = n < 0 ? 0 : n;
-    // (the counts that occur are exact steps: the loads of the first half of
-    // a stage, 4 (bf16) or 10 (MXFP8: 8 data + 2 scale loads), or a whole one)
+    // (the counts that occur are exact steps: the next stage's loads issued
+    // before the publish, 6 (bf16), 4 (bf16, other configurations) or 10
+    // (MXFP8: 8 data + 2 scale loads), or a whole stage's)
     if (n >= 24) wait_vmcnt<24>();
     else if (n >= 16) { if (n >= 20) wait_vmcnt<20>(); else if (n >= 18) wait_vmcnt<18>(); else wait_vmcnt<16>(); }
     else if (n >= 8) { if (n >= 12) wait_vmcnt<12>(); else if (n >= 10) wait_vmcnt<10>(); else wait_vmcnt<8>(); }
@@ -1665,20 +1666,37 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
   };
 
   // ---- pipeline.  Stage g is consumed in KK k-slices; while slice kk's
-  // products run, slice kk+1 is read.  The last slice of a stage has two
-  // barriers.  The first comes as soon as every wave holds that slice (each
-  // waits for its own LDS reads before arriving): stage g's buffer is then
-  // free, and the producer's next stage g + kStages is issued into it during
-  // the first half of the slice's products -- it does not wait for stage g+1
-  // to land.  The second, in the middle of the products, publishes stage g+1
-  // once this wave's loads of it have landed, and its first slice is read
-  // while the second half of the products runs.
+  // products run, the next slice is read.  Two barriers per stage:
+  //  - release: once every wave holds the stage's remaining slices in
+  //    registers (each waits for its own LDS reads before arriving), stage g's
+  //    buffer is free and the producer's stage g + kStages is issued into it,
+  //    its loads spread between the remaining products -- it does not wait
+  //    for stage g+1 to land;
+  //  - publish: in the last slice, once this wave's loads of stage g+1 have
+  //    landed; stage g+1's first slice is read while the rest of the last
+  //    slice's products run.
+  // bf16 (four slices, eight loads per wave and stage): slices 2 and 3 are
+  // both read during slice 1, and the release comes after slice 1's second
+  // product, so the refill gets about two slices more lead than with a
+  // release in the last slice, and its loads are spread at about one per 2.5
+  // products (denser bursts slow the products and the fragment reads that
+  // share the CU's memory path).  Slices 0 and 2 go to fr[0], slice 1 to
+  // fr[1], slice 3 to fr3.  MXFP8 (one wave per SIMD, 32-byte fragments) has
+  // no register room for a third fragment set: it reads one slice ahead and
+  // releases in the last slice, as do the other compile-time configurations.
 #pragma unroll
   for (int s = 0; s < kStages; ++s) produce();   // every buffer is free at the start
   TileSeq<MODE, C::BP, C::BQ> cseq;
   cseq.init(S);
   Frags fr[2];
+  Frags fr3;                                   // bf16: slice 3 of the stage
   const StageDma sd_none = {0, 0u, 0u, p_rc, false};
+  StageDma refill = sd_none;                   // bf16: the refill being issued
+  // bf16 schedule: products of slice 1 before the release; loads issued by
+  // the ends of slice 1, slice 2 and slice 3's first part; products of slice
+  // 3 before the publish
+  constexpr bool kEarly = !MX && KK == 4 && SPW == 8;
+  constexpr int kRel = 2, kL1 = 2, kL2 = 5, kL3 = 6, kPub = 3;
   int g = 0;
   if (gp > 0) {
     wait_stage(0);
@@ -1729,6 +1747,42 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
             if (more) mx_pack_read_fr(g + 1, 0, raw, nxt);
             __builtin_amdgcn_sched_barrier(0);
             mma_part(cur, kMM / 2 + X2, kMM, sd, SPW / 2 + X2, SPW);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          continue;
+        }
+        if constexpr (kEarly) {
+          if (kk == 0) {
+            read(g, 1, fr[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            mma_part(fr[0], 0, kMM, sd_none, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+          } else if (kk == 1) {
+            read(g, 2, fr[0]);
+            read(g, 3, fr3);
+            __builtin_amdgcn_sched_barrier(0);
+            mma_part(fr[1], 0, kRel, sd_none, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __syncthreads();                    // release stage g's buffer
+            refill = dma_begin();
+            __builtin_amdgcn_sched_barrier(0);
+            mma_part(fr[1], kRel, kMM, refill, 0, kL1);
+            __builtin_amdgcn_sched_barrier(0);
+          } else if (kk == 2) {
+            mma_part(fr[0], 0, kMM, refill, kL1, kL2);
+            __builtin_amdgcn_sched_barrier(0);
+          } else {
+            const bool more = g + 1 < gp;
+            mma_part(fr3, 0, kPub, refill, kL2, kL3);
+            __builtin_amdgcn_sched_barrier(0);
+            if (more) {
+              wait_stage(g + 1);
+              __syncthreads();                  // publish stage g+1
+              read(g + 1, 0, fr[0]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            mma_part(fr3, kPub, kMM, refill, kL3, SPW);
             __builtin_amdgcn_sched_barrier(0);
           }
           continue;
