@@ -1308,13 +1308,28 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
                     : frag_rc(tq, offQ[kk] + j * 32 * kRowB);
     }
   };
+  // bf16 stage schedule (see the pipeline below): products of slice 1 before
+  // the release; loads issued by the ends of slice 1, slice 2 and slice 3's
+  // first part; products of slice 3 before the publish
+  constexpr bool kEarly = !MX && KK == 4 && SPW == 8;
+  constexpr int kRel = 2, kL1 = 2, kL2 = 5, kL3 = 6, kPub = 3;
+  // Operations of the following stage's refill issued before the publish
+  // wait in steady state: kL3 (bf16), half a stage's loads (other bf16
+  // configurations), or MXFP8's first half: 8 data + 2 scale loads.
+  constexpr int kSteady = kEarly ? kL3 : MX ? SPW / 2 + (kScLoads < SPW / 2 ? kScLoads : SPW / 2)
+                                           : SPW / 2;
   // wait until this wave's loads of stage g have landed
   auto wait_stage = [&](int g) {
     int n = issued - after[g % kStages];
     n = n < 0 ? 0 : n;
-    // (the counts that occur are exact steps: the next stage's loads issued
-    // before the publish, 6 (bf16), 4 (bf16, other configurations) or 10
-    // (MXFP8: 8 data + 2 scale loads), or a whole stage's)
+    // The steady-state count is tested first, on the fall-through path: the
+    // chain below costs several taken branches per stage, which measurably
+    // slows the stage loop.  (The counts that occur otherwise are exact
+    // steps: fewer loads at a tile or list end, or a whole stage's.)
+    if (__builtin_expect(n == kSteady, 1)) {
+      wait_vmcnt<kSteady>();
+      return;
+    }
     if (n >= 24) wait_vmcnt<24>();
     else if (n >= 16) { if (n >= 20) wait_vmcnt<20>(); else if (n >= 18) wait_vmcnt<18>(); else wait_vmcnt<16>(); }
     else if (n >= 8) { if (n >= 12) wait_vmcnt<12>(); else if (n >= 10) wait_vmcnt<10>(); else wait_vmcnt<8>(); }
@@ -1692,11 +1707,6 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
   Frags fr3;                                   // bf16: slice 3 of the stage
   const StageDma sd_none = {0, 0u, 0u, p_rc, false};
   StageDma refill = sd_none;                   // bf16: the refill being issued
-  // bf16 schedule: products of slice 1 before the release; loads issued by
-  // the ends of slice 1, slice 2 and slice 3's first part; products of slice
-  // 3 before the publish
-  constexpr bool kEarly = !MX && KK == 4 && SPW == 8;
-  constexpr int kRel = 2, kL1 = 2, kL2 = 5, kL3 = 6, kPub = 3;
   int g = 0;
   if (gp > 0) {
     wait_stage(0);
