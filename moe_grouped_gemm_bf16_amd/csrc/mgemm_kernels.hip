@@ -1367,9 +1367,17 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
 #pragma unroll
     for (int x = x0; x < x1; ++x) {
       const int i = x / C::MQ, j = x % C::MQ;
-      if constexpr (MX)
+      if constexpr (MX) {
         acc[i][j] = mfma_mx(i, j, f.p[i], f.q[j], acc[i][j], f.sp, f.sq);
-      else
+        // An empty use of the result (in its accumulator register) keeps the
+        // product where it is written: the scaled product's builtin has no
+        // side effects, and without the use the compiler moves a slice's
+        // products past the loads, waits and barriers that follow, towards
+        // their next use, and the one wave of the SIMD then waits at each
+        // barrier with no product queued.  (The bf16 products stay in place.)
+        const float pin = acc[i][j][0];
+        asm volatile("" ::"a"(pin));
+      } else
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.p[i], f.q[j], acc[i][j], 0, 0, 0);
       // after product x, (x - x0 + 1) (d1 - d0) / (x1 - x0) loads are due
       while (d < d1 && (d - d0) * (x1 - x0) < (x - x0 + 1) * (d1 - d0)) {
