@@ -1313,10 +1313,15 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
   // first part; products of slice 3 before the publish
   constexpr bool kEarly = !MX && KK == 4 && SPW == 8;
   constexpr int kRel = 2, kL1 = 2, kL2 = 5, kL3 = 6, kPub = 3;
+  // MXFP8 stage schedule (16 products per slice, 16 data loads per stage):
+  // products of slice 0 before the release; loads issued by the end of slice
+  // 0 and before the publish; products of slice 1 before the publish
+  constexpr int kMxRel = 4, kMxL0 = 6, kMxL1 = 10, kMxPub = 8;
   // Operations of the following stage's refill issued before the publish
   // wait in steady state: kL3 (bf16), half a stage's loads (other bf16
-  // configurations), or MXFP8's first half: 8 data + 2 scale loads.
-  constexpr int kSteady = kEarly ? kL3 : MX ? SPW / 2 + (kScLoads < SPW / 2 ? kScLoads : SPW / 2)
+  // configurations), or MXFP8's kMxL1 data loads and the scale loads (issued
+  // with the first data loads).
+  constexpr int kSteady = kEarly ? kL3 : MX ? kMxL1 + (kScLoads < kMxL1 ? kScLoads : kMxL1)
                                            : SPW / 2;
   // wait until this wave's loads of stage g have landed
   auto wait_stage = [&](int g) {
@@ -1730,41 +1735,48 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
         Frags& cur = fr[kk & 1];
         Frags& nxt = fr[(kk + 1) & 1];
         if constexpr (MX) {
-          // The next slice's scale reads go first; they are packed after two
-          // products, when they have landed, and only then are the fragment
-          // reads issued (a pack right behind all the reads would wait for
-          // most of them: the LDS counter tracks at most 15 in order, and one
-          // wave per SIMD leaves the matrix core idle meanwhile).
+          // Two slices of 64 steps per stage.  Slice 0: the next slice's scale
+          // reads go first; they are packed after two products, when they have
+          // landed, and only then are the fragment reads issued (a pack right
+          // behind all the reads would wait for most of them: the LDS counter
+          // tracks at most 15 in order, and one wave per SIMD leaves the
+          // matrix core idle meanwhile).  Once slice 1 is in registers (after
+          // kMxRel products) the stage's buffer is released and the refill
+          // issued, spread over the rest of slice 0 and slice 1; the publish
+          // of the next stage follows slice 1's kMxPub-th product.
+          static_assert(KK == 2, "MXFP8 stages of two 64-step slices");
           constexpr int X2 = 2;
           uint32_t raw[8];
-          if (kk + 1 < KK) {
+          if (kk == 0) {
             mx_read_sc(g, raw);
             __builtin_amdgcn_sched_barrier(0);
             mma_part(cur, 0, X2, sd_none, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
-            mx_pack_read_fr(g, kk + 1, raw, nxt);
+            mx_pack_read_fr(g, 1, raw, nxt);
             __builtin_amdgcn_sched_barrier(0);
-            mma_part(cur, X2, kMM, sd_none, 0, 0);
+            mma_part(cur, X2, kMxRel, sd_none, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __syncthreads();                    // release stage g's buffer
+            refill = dma_begin();
+            __builtin_amdgcn_sched_barrier(0);
+            mma_part(cur, kMxRel, kMM, refill, 0, kMxL0);
             __builtin_amdgcn_sched_barrier(0);
           } else {
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            __syncthreads();
             const bool more = g + 1 < gp;
-            const StageDma sd = dma_begin();
-            __builtin_amdgcn_sched_barrier(0);
-            mma_part(cur, 0, kMM / 2, sd, 0, SPW / 2);
+            mma_part(cur, 0, kMxPub, refill, kMxL0, kMxL1);
             __builtin_amdgcn_sched_barrier(0);
             if (more) {
               wait_stage(g + 1);
-              __syncthreads();
+              __syncthreads();                  // publish stage g+1
               mx_read_sc(g + 1, raw);
             }
             __builtin_amdgcn_sched_barrier(0);
-            mma_part(cur, kMM / 2, kMM / 2 + X2, sd, SPW / 2, SPW / 2 + X2);
+            mma_part(cur, kMxPub, kMxPub + X2, refill, kMxL1, kMxL1 + 2);
             __builtin_amdgcn_sched_barrier(0);
             if (more) mx_pack_read_fr(g + 1, 0, raw, nxt);
             __builtin_amdgcn_sched_barrier(0);
-            mma_part(cur, kMM / 2 + X2, kMM, sd, SPW / 2 + X2, SPW);
+            mma_part(cur, kMxPub + X2, kMM, refill, kMxL1 + 2, SPW);
             __builtin_amdgcn_sched_barrier(0);
           }
           continue;
