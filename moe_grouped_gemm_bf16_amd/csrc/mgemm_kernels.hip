@@ -1709,9 +1709,10 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
   // release in the last slice, and its loads are spread at about one per 2.5
   // products (denser bursts slow the products and the fragment reads that
   // share the CU's memory path).  Slices 0 and 2 go to fr[0], slice 1 to
-  // fr[1], slice 3 to fr3.  MXFP8 (one wave per SIMD, 32-byte fragments) has
-  // no register room for a third fragment set: it reads one slice ahead and
-  // releases in the last slice, as do the other compile-time configurations.
+  // fr[1], slice 3 to fr3.  MXFP8 (two slices of 64 steps): the release
+  // follows slice 0's fourth product, once slice 1 is in registers.  The other
+  // compile-time configurations read one slice ahead and release in the last
+  // slice.
 #pragma unroll
   for (int s = 0; s < kStages; ++s) produce();   // every buffer is free at the start
   TileSeq<MODE, C::BP, C::BQ> cseq;
@@ -1719,7 +1720,7 @@ __device__ __forceinline__ void run_tiles(const KernelArgs& a, const Sched& S, c
   Frags fr[2];
   Frags fr3;                                   // bf16: slice 3 of the stage
   const StageDma sd_none = {0, 0u, 0u, p_rc, false};
-  StageDma refill = sd_none;                   // bf16: the refill being issued
+  StageDma refill = sd_none;                   // the refill being issued
   int g = 0;
   if (gp > 0) {
     wait_stage(0);
