@@ -3,6 +3,8 @@ transposed and on token-major operands), the
 SwiGLU backward and the token-order combine against the oracle (needs an
 MI355X).  Ragged and empty experts, reductions of one block to several
 stages, widths that are not multiples of the tile."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -17,7 +19,8 @@ from workloads import normal_bf16_bits, offsets_from_sizes
 from workloads.synth import mx_e4m3_codes, mx_e8m0_codes
 
 pytestmark = pytest.mark.gpu
-SEEDS = range(12)
+# more seeds for a longer sweep: MG_FUZZ_SEEDS=<n>
+SEEDS = range(int(os.environ.get("MG_FUZZ_SEEDS", "12")))
 
 
 def _u8(a):
