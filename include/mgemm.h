@@ -61,8 +61,10 @@ extern "C" {
 typedef enum mg_status {
   MG_OK = 0,
   MG_ERR_NULL = 1,     /* a required pointer is NULL                          */
-  MG_ERR_SHAPE = 2,    /* E < 1 or > 1024, negative or too large sizes, N or K
-                          not a multiple of 8                                 */
+  MG_ERR_SHAPE = 2,    /* sizes outside the entry point's rules: E < 1 or > 1024,
+                          negative or too large sizes, N or K not a multiple of
+                          8 (16 for kgemm_wgrad_mx_tm), MXFP8 token counts or
+                          offsets not multiples of 128 where required         */
   MG_ERR_ALIGN = 3,    /* a data pointer is not 16-byte aligned               */
   MG_ERR_DEVICE = 4,   /* current device is not gfx950, or HIP query failed   */
   MG_ERR_LAUNCH = 5,   /* the kernel launch was rejected                      */

@@ -398,7 +398,10 @@ const char* mg_status_str(int32_t status) {
   switch (status) {
     case MG_OK: return "MG_OK";
     case MG_ERR_NULL: return "MG_ERR_NULL: a required pointer is NULL";
-    case MG_ERR_SHAPE: return "MG_ERR_SHAPE: unsupported sizes (E in [1,1024], N,K multiples of 8)";
+    case MG_ERR_SHAPE:
+      return "MG_ERR_SHAPE: sizes outside the entry point's rules (E in [1,1024]; N, K multiples "
+             "of 8, of 16 for the token-major MXFP8 weight gradient; MXFP8 token counts and "
+             "offsets multiples of 128 where the call reduces over tokens)";
     case MG_ERR_ALIGN: return "MG_ERR_ALIGN: data pointers must be 16-byte aligned";
     case MG_ERR_DEVICE: return "MG_ERR_DEVICE: current device is not gfx950 (or HIP failed)";
     case MG_ERR_LAUNCH: return "MG_ERR_LAUNCH: kernel launch failed";

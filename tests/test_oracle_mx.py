@@ -296,3 +296,31 @@ def test_sample_wgrad_mx_and_gate():
     assert oracle.check_fp32_mx(bad, dw, mag, k_red, empty_mask=empty).fails > 0.8 * dw[2].size
     swapped = dw[[2, 1, 0]]
     assert not oracle.check_fp32_mx(swapped, dw, mag, k_red, empty_mask=empty).passed
+
+
+def test_small_integer_inputs_decode_to_integers_and_sum_exactly():
+    """The exact-result GPU cases rest on two facts checked here: the small
+    integer codes decode (torch's float8 cast) to every integer in [-3, 3] and
+    nothing else, and with scales constant along the reduction the oracle's
+    forward equals integer brute force times the two scales."""
+    c = synth.mx_small_int_codes((4096,), 3, 1)
+    v = _torch_e4m3(c)
+    assert sorted(set(v.tolist())) == [-3.0, -2.0, -1.0, 0.0, 1.0, 2.0, 3.0]
+    s = synth.mx_e8m0_row_codes(9, 5, 127, 6, 3, 2)
+    assert (s == s[:, :1]).all() and s.min() >= 121 and s.max() <= 133
+    off = synth.offsets_from_sizes([3, 0, 2])
+    M, N, K = 5, 3, 64
+    x8 = synth.mx_small_int_codes((M, K), 3, 3)
+    w8 = synth.mx_small_int_codes((3, N, K), 3, 4)
+    xs = synth.mx_e8m0_row_codes(M, K // 32, 127, 6, 3, 5)
+    ws = synth.mx_e8m0_row_codes(3 * N, K // 32, 127, 6, 3, 6).reshape(3, N, K // 32)
+    got = oracle.grouped_fwd_mx(x8, xs, w8, ws, off)
+    xi = _torch_e4m3(x8).astype(np.int64).tolist()
+    wi = _torch_e4m3(w8).astype(np.int64).tolist()
+    for i in range(M):
+        e = int(np.searchsorted(off, i, side="right")) - 1
+        for n in range(N):
+            dot = sum(xi[i][k] * wi[e][n][k] for k in range(K))
+            want = Fraction(dot) * Fraction(2) ** (int(xs[i, 0]) - 127) \
+                * Fraction(2) ** (int(ws[e, n, 0]) - 127)
+            assert Fraction(got[i, n]) == want

@@ -439,3 +439,90 @@ def test_mx_longest_reductions_sampled():
     k_red = np.maximum(np.diff(np.asarray(off2, np.int64))[es], 1)
     rep = check_fp32_mx(got[es, ns, ks], val, mag, k_red)
     assert rep.passed, f"wgrad: {rep}"
+
+
+# ------------------------------------------------ exact small-integer cases --
+# Codes of integers in [-3, 3], each row of X and of W (each row of dY^T and
+# X^T in the weight gradient) scaled by one power of two along its whole
+# reduction axis.  The products that make one output element are then integers
+# times one common power of two, and every partial sum is at most 9 x (the
+# reduction length) of those units: fewer than 24 significant bits, and fewer
+# than 10 within one matrix-core instruction.  Any summation order is exact, so
+# the kernels owe the exact value itself: fp32 outputs bit for bit, bf16 outputs
+# its round to nearest even, with no tolerance.  A scale taken from the wrong
+# row or column, or a code from the wrong place, changes the bits.
+
+from oracle import f64_to_bf16_bits  # noqa: E402
+from workloads.synth import mx_e8m0_row_codes, mx_small_int_codes  # noqa: E402
+
+MX_EXACT_FWD = [([300, 0, 17, 513], 264, 2048), ([1, 255, 257], 136, 96), ([700], 520, 416)]
+
+
+def _fwd_exact_inputs(sizes, N, K, seed):
+    off = offsets_from_sizes(sizes)
+    M, E = int(off[-1]), len(sizes)
+    x8 = mx_small_int_codes((M, K), 8900, seed, 1)
+    w8 = mx_small_int_codes((E, N, K), 8900, seed, 2)
+    xs = mx_e8m0_row_codes(M, K // 32, 127, 6, 8900, seed, 3)
+    ws = mx_e8m0_row_codes(E * N, K // 32, 127, 6, 8900, seed, 4).reshape(E, N, K // 32)
+    return off, M, x8, w8, xs, ws
+
+
+@pytest.mark.parametrize("case", range(len(MX_EXACT_FWD)))
+def test_fwd_mx_exact_on_small_integers(case):
+    sizes, N, K = MX_EXACT_FWD[case]
+    _say("fwd_mx exact", sizes, N, K)
+    off, M, x8, w8, xs, ws = _fwd_exact_inputs(sizes, N, K, case)
+    got = _run(off, M, N, x8, w8, xs, ws)
+    want = f64_to_bf16_bits(grouped_fwd_mx(x8, xs, w8, ws, off))
+    bad = int((got != want).sum())
+    assert bad == 0, f"{bad} of {got.size} elements differ from the rounded exact value"
+
+
+@pytest.mark.parametrize("name", ["a3b_gate_up", "a3b_down"])
+def test_a3b_mx_exact_whole_tensor(name):
+    """The 30B-A3B expert shapes in the launch the bench times, every element
+    of the output equal to the round to nearest even of the exact value."""
+    (wl,) = make_workload(4, name)
+    off = np.asarray(wl.offsets)
+    M, N, K, E = wl.M, wl.N, wl.K, wl.E
+    _say("a3b mx exact", name, M, N, K, E)
+    x8 = mx_small_int_codes((M, K), 8910, 1)
+    w8 = mx_small_int_codes((E, N, K), 8910, 2)
+    xs = mx_e8m0_row_codes(M, K // 32, 127, 6, 8910, 3)
+    ws = mx_e8m0_row_codes(E * N, K // 32, 127, 6, 8910, 4).reshape(E, N, K // 32)
+    got = _run(off, M, N, x8, w8, xs, ws)
+    last = int(off[-1])
+    assert (got[last:] == SENTINEL).all()
+    want = f64_to_bf16_bits(grouped_fwd_mx(x8, xs, w8, ws, off)[:last])
+    bad = int((got[:last] != want).sum())
+    assert bad == 0, f"{bad} of {want.size} elements differ from the rounded exact value"
+
+
+MX_EXACT_WG = [([128, 0, 384, 1024], 272, 144), ([2048, 128, 0, 256], 144, 528)]   # N, K: x16
+
+
+@pytest.mark.parametrize("case", range(len(MX_EXACT_WG)))
+def test_wgrad_mx_exact_on_small_integers(case):
+    """Both MXFP8 weight-gradient calls (transposed and token-major operands)
+    equal to the exact fp32 value on every element; empty experts exactly 0."""
+    sizes, N, K = MX_EXACT_WG[case]
+    off = offsets_from_sizes(sizes)
+    M, E = int(off[-1]) + 128, len(sizes)
+    _say("wgrad_mx exact", sizes, N, K)
+    dyt8 = mx_small_int_codes((N, M), 8920, case, 1)
+    xt8 = mx_small_int_codes((K, M), 8920, case, 2)
+    dyts = mx_e8m0_row_codes(N, M // 32, 127, 6, 8920, case, 3)
+    xts = mx_e8m0_row_codes(K, M // 32, 127, 6, 8920, case, 4)
+    exact = grouped_wgrad_mx(dyt8, dyts, xt8, xts, off, E)
+    assert (exact.astype(np.float32).astype(np.float64) == exact).all()
+    bd, bx = _u8(mx_scales_blocked(dyts)), _u8(mx_scales_blocked(xts))
+    o = dev_i32(off)
+    a = mg.wgrad_mx(_u8(dyt8), bd, _u8(xt8), bx, o, E,
+                    out=torch.full((E, N, K), float("nan"), device="cuda"))
+    b = mg.wgrad_mx_tm(_u8(np.ascontiguousarray(dyt8.T)), bd, _u8(np.ascontiguousarray(xt8.T)),
+                       bx, o, E, out=torch.full((E, N, K), float("nan"), device="cuda"))
+    torch.cuda.synchronize()
+    for got, what in ((a.cpu().numpy(), "transposed"), (b.cpu().numpy(), "token-major")):
+        bad = int((got.astype(np.float64) != exact).sum())
+        assert bad == 0, f"{what}: {bad} of {got.size} elements differ from the exact value"

@@ -252,6 +252,30 @@ def mx_e8m0_codes(shape: Sequence[int], center: int, spread: int, *key: int) -> 
     return np.clip(c, 0, 254).astype(np.uint8).reshape(tuple(shape))
 
 
+# E4M3 codes of the integers 0..3 from their fields (sign bit 7, exponent field
+# bits 6..3 with bias 7, mantissa bits 2..0): 0 is all zeros, 1 = 2^0 (E = 7),
+# 2 = 2^1 (E = 8), 3 = 2^1 * 1.5 (E = 8, m = 4).
+_E4M3_SMALL_INT = np.array([0x00, 0x38, 0x40, 0x44], dtype=np.uint8)
+
+
+def mx_small_int_codes(shape: Sequence[int], *key: int) -> np.ndarray:
+    """uint8 E4M3 codes of integers uniform in [-3, 3] (zero without a sign
+    bit).  Products of two such values are integers of magnitude <= 9."""
+    rng = _stream(*key)
+    n = int(np.prod(shape, dtype=np.int64))
+    mag = rng.integers(0, 4, n)
+    neg = (rng.integers(0, 2, n) == 1) & (mag > 0)
+    c = _E4M3_SMALL_INT[mag] | np.where(neg, np.uint8(0x80), np.uint8(0))
+    return c.astype(np.uint8).reshape(tuple(shape))
+
+
+def mx_e8m0_row_codes(rows: int, blocks: int, center: int, spread: int, *key: int) -> np.ndarray:
+    """uint8 E8M0 scale codes [rows, blocks], uniform in [center - spread,
+    center + spread] per row and the same for every block of a row."""
+    c = mx_e8m0_codes((rows, 1), center, spread, *key)
+    return np.ascontiguousarray(np.broadcast_to(c, (rows, blocks)))
+
+
 # -- a row-addressable operand for sizes past 4 GiB ---------------------------
 # Element (i, k) = ((37 i + 11 k + 5) mod 17 - 8) / 8: a multiple of 1/8 in
 # [-1, 1], exact in bf16, so that a tensor of billions of elements can be built
