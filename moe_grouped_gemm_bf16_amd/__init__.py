@@ -20,8 +20,10 @@ import torch
 
 from ._lib import LIB, GemmDesc, MgemmError, check, status_str  # noqa: F401
 
-__all__ = ["fwd", "dgrad", "wgrad", "fwd_swiglu", "grouped_list", "list_descriptors",
-           "grouped_list_desc", "Mgemm", "Kgemm", "MgemmError", "status_str", "LIB"]
+__all__ = ["fwd", "dgrad", "wgrad", "wgrad_noalloc", "fwd_swiglu", "dgrad_swiglu",
+           "moe_combine", "grouped_list", "list_descriptors", "grouped_list_desc",
+           "mx_scales_blocked", "fwd_mx", "wgrad_mx", "wgrad_mx_tm", "Mgemm", "Kgemm",
+           "MgemmError", "status_str", "LIB"]
 
 
 def _stream(t: torch.Tensor) -> int:
@@ -39,6 +41,12 @@ def _need(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int) -> None:
         raise ValueError(f"{name} must be on a GPU device")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _same_device(dev, **tensors) -> None:
+    for name, t in tensors.items():
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the data on {dev}")
 
 
 def _offsets(offsets: torch.Tensor, E: int, dev) -> torch.Tensor:
@@ -69,6 +77,7 @@ def fwd(x: torch.Tensor, w: torch.Tensor, offsets: torch.Tensor, max_m_per_e: in
         _need(out, "out", torch.bfloat16, 2)
         if tuple(out.shape) != (M, N):
             raise ValueError(f"out must be [{M}, {N}]")
+    _same_device(x.device, w=w, out=out)
     with torch.cuda.device(x.device):
         st = LIB.mgemm_fwd(x.data_ptr(), w.data_ptr(), offsets.data_ptr(), out.data_ptr(),
                            M, N, K, E, int(max_m_per_e), _stream(x))
@@ -94,6 +103,7 @@ def dgrad(dy: torch.Tensor, w: torch.Tensor, offsets: torch.Tensor, max_m_per_e:
         _need(out, "out", torch.bfloat16, 2)
         if tuple(out.shape) != (M, K):
             raise ValueError(f"out must be [{M}, {K}]")
+    _same_device(dy.device, w=w, out=out)
     with torch.cuda.device(dy.device):
         st = LIB.mgemm_dgrad(dy.data_ptr(), w.data_ptr(), offsets.data_ptr(), out.data_ptr(),
                              M, N, K, E, int(max_m_per_e), _stream(dy))
@@ -139,6 +149,7 @@ def _wgrad(fn: str, dy, x, offsets, E, out, accumulate):
         _need(out, "out", torch.float32, 3)
         if tuple(out.shape) != (E, N, K):
             raise ValueError(f"out must be [{E}, {N}, {K}]")
+    _same_device(dy.device, x=x, out=out)
     with torch.cuda.device(dy.device):
         st = getattr(LIB, fn)(dy.data_ptr(), x.data_ptr(), offsets.data_ptr(), out.data_ptr(),
                               M, N, K, E, 1 if accumulate else 0, _stream(dy))
@@ -190,6 +201,7 @@ def fwd_swiglu(x: torch.Tensor, w13: torch.Tensor, offsets: torch.Tensor,
         if tuple(gu_out.shape) != (M, 2 * I):
             raise ValueError(f"gu_out must be [{M}, {2 * I}]")
         guptr = gu_out.data_ptr()
+    _same_device(x.device, w13=w13, out=out, gu_out=gu_out)
     with torch.cuda.device(x.device):
         st = LIB.mgemm_fwd_swiglu_gu(x.data_ptr(), gptr, w13.data_ptr(), offsets.data_ptr(),
                                      out.data_ptr(), guptr, M, T, I, K, E, int(max_m_per_e),
@@ -221,6 +233,7 @@ def dgrad_swiglu(dy: torch.Tensor, w2: torch.Tensor, gu: torch.Tensor, offsets: 
         _need(out, "out", torch.bfloat16, 2)
         if tuple(out.shape) != (M, 2 * I):
             raise ValueError(f"out must be [{M}, {2 * I}]")
+    _same_device(dy.device, w2=w2, gu=gu, out=out)
     with torch.cuda.device(dy.device):
         st = LIB.mgemm_dgrad_swiglu(dy.data_ptr(), w2.data_ptr(), gu.data_ptr(),
                                     offsets.data_ptr(), out.data_ptr(), M, N, I, E,
@@ -303,6 +316,7 @@ def mx_scales_blocked(scales: torch.Tensor, out: torch.Tensor | None = None) -> 
         _need(out, "out", torch.uint8, len(shape))
         if tuple(out.shape) != shape:
             raise ValueError(f"out must be {shape}")
+    _same_device(scales.device, out=out)
     with torch.cuda.device(scales.device):
         st = LIB.mg_mx_scales_blocked(scales.data_ptr(), out.data_ptr(), rows, 32 * nb, batch,
                                       _stream(scales))
@@ -337,6 +351,7 @@ def fwd_mx(x8: torch.Tensor, x_scale: torch.Tensor, w8: torch.Tensor, w_scale: t
         _need(out, "out", torch.bfloat16, 2)
         if tuple(out.shape) != (M, N):
             raise ValueError(f"out must be [{M}, {N}]")
+    _same_device(x8.device, x_scale=x_scale, w8=w8, w_scale=w_scale, out=out)
     with torch.cuda.device(x8.device):
         st = LIB.mgemm_fwd_mx(x8.data_ptr(), x_scale.data_ptr(), w8.data_ptr(), w_scale.data_ptr(),
                               offsets.data_ptr(), out.data_ptr(), M, N, K, E, int(max_m_per_e),
@@ -375,6 +390,7 @@ def wgrad_mx(dyt8: torch.Tensor, dyt_scale: torch.Tensor, xt8: torch.Tensor,
         _need(out, "out", torch.float32, 3)
         if tuple(out.shape) != (E, N, K):
             raise ValueError(f"out must be [{E}, {N}, {K}]")
+    _same_device(dyt8.device, dyt_scale=dyt_scale, xt8=xt8, xt_scale=xt_scale, out=out)
     with torch.cuda.device(dyt8.device):
         st = LIB.kgemm_wgrad_mx(dyt8.data_ptr(), dyt_scale.data_ptr(), xt8.data_ptr(),
                                 xt_scale.data_ptr(), offsets.data_ptr(), out.data_ptr(),
@@ -415,6 +431,7 @@ def wgrad_mx_tm(dy8: torch.Tensor, dy_scale: torch.Tensor, x8: torch.Tensor,
         _need(out, "out", torch.float32, 3)
         if tuple(out.shape) != (E, N, K):
             raise ValueError(f"out must be [{E}, {N}, {K}]")
+    _same_device(dy8.device, dy_scale=dy_scale, x8=x8, x_scale=x_scale, out=out)
     with torch.cuda.device(dy8.device):
         st = LIB.kgemm_wgrad_mx_tm(dy8.data_ptr(), dy_scale.data_ptr(), x8.data_ptr(),
                                    x_scale.data_ptr(), offsets.data_ptr(), out.data_ptr(),
@@ -447,6 +464,7 @@ def moe_combine(rows: torch.Tensor, token_rows: torch.Tensor,
         _need(out, "out", torch.bfloat16, 2)
         if tuple(out.shape) != (T, D):
             raise ValueError(f"out must be [{T}, {D}]")
+    _same_device(rows.device, token_rows=token_rows, weights=weights, out=out)
     with torch.cuda.device(rows.device):
         st = LIB.mg_moe_combine(rows.data_ptr(), token_rows.data_ptr(), wptr, out.data_ptr(),
                                 M, T, k, D, _stream(rows))
