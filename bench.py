@@ -414,12 +414,68 @@ def lists(torch, mg, reps=20):
 
 # ----------------------------------------------------------------------- mx --
 
+def per_expert_scaled_mm(torch, x8, xs, w8, ws, offsets, y_grouped):
+    """A loop of torch._scaled_mm calls, one per non-empty expert, on MXFP8
+    codes with E8M0 scales per 32 reduction steps (uint8 [rows, K/32]).
+    Returns {"fn": the loop} when the call works here, with the relative
+    Frobenius difference of its result from the grouped call's; else
+    {"error": ...}.  Where the library refuses an expert's row count, each
+    expert's rows are copied once (outside any timing) into a block padded
+    with zero codes to a multiple of 128 rows, and the loop runs on those."""
+    if not hasattr(torch, "_scaled_mm") or not hasattr(torch, "float8_e8m0fnu"):
+        return {"error": "torch._scaled_mm with E8M0 scales not in this build"}
+    ends = [int(v) for v in offsets]
+    live = [e for e in range(len(ends) - 1) if ends[e + 1] > ends[e]]
+    wf, we = w8.view(torch.float8_e4m3fn), ws.view(torch.float8_e8m0fnu)
+
+    def run(blocks):
+        return [torch._scaled_mm(xa, wf[e].t(), scale_a=sa, scale_b=we[e],
+                                 out_dtype=torch.bfloat16) for e, xa, sa in blocks]
+
+    blocks = [(e, x8[ends[e]:ends[e + 1]].view(torch.float8_e4m3fn),
+               xs[ends[e]:ends[e + 1]].view(torch.float8_e8m0fnu)) for e in live]
+    padded = False
+    try:
+        ys = run(blocks)
+        torch.cuda.synchronize()
+    except Exception as exc:                       # the library refuses some shapes
+        first = f"{type(exc).__name__}: {str(exc)[:400]}"
+        padded = True
+        pb = []
+        for e in live:
+            m = ends[e + 1] - ends[e]
+            mp = (m + 127) // 128 * 128
+            xa = torch.zeros((mp, x8.shape[1]), dtype=torch.uint8, device=x8.device)
+            sa = torch.full((mp, xs.shape[1]), 127, dtype=torch.uint8, device=xs.device)
+            xa[:m] = x8[ends[e]:ends[e + 1]]
+            sa[:m] = xs[ends[e]:ends[e + 1]]
+            pb.append((e, xa.view(torch.float8_e4m3fn), sa.view(torch.float8_e8m0fnu)))
+        blocks = pb
+        try:
+            ys = run(blocks)
+            torch.cuda.synchronize()
+        except Exception as exc2:
+            return {"error": first, "padded_error": f"{type(exc2).__name__}: {str(exc2)[:200]}"}
+    num = den = 0.0
+    for e, ye in zip(live, ys):
+        g = y_grouped[ends[e]:ends[e + 1]].float()
+        num += float((ye[:g.shape[0]].float() - g).pow(2).sum())
+        den += float(g.pow(2).sum())
+    rec = {"fn": lambda: run(blocks),
+           "rel_frobenius_vs_grouped": float(f"{(num / max(den, 1e-300)) ** 0.5:.3e}")}
+    if padded:
+        rec["rows_padded_to_128"] = sum(int(xa.shape[0]) for _, xa, _ in blocks)
+        rec["unpadded_error"] = first
+    return rec
+
+
 def mx(torch, mg, reps=20):
     """The MXFP8 grouped forward (E4M3 operands, E8M0 scales per 32 steps) on
     the uniform g8 shape and the 30B-A3B share's two expert GEMMs, timed
-    interleaved with the bf16 forward of the same shape; plus the blocked
-    scale layout kernel on the gate-up operands.  Reported beside the step
-    only (`value` is the bf16 path)."""
+    interleaved with the bf16 forward of the same shape and with a loop of
+    per-expert torch._scaled_mm calls on the same codes (the library
+    comparator); plus the blocked scale layout kernel on the gate-up operands.
+    Reported beside the step only (`value` is the bf16 path)."""
     import numpy as np
     from workloads import make_workload
     from workloads.synth import mx_e4m3_codes, mx_e8m0_codes
@@ -439,9 +495,16 @@ def mx(torch, mg, reps=20):
         x, w = up(wl.x_bits()), up(wl.w_bits())
         y8 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
         y = torch.empty_like(y8)
-        fns = (lambda: mg.fwd_mx(x8, bx, w8, bw, off, hint, out=y8),
+        fns = [lambda: mg.fwd_mx(x8, bx, w8, bw, off, hint, out=y8),
                lambda: mg.fwd(x, w, off, hint, out=y),
-               lambda: (mg.mx_scales_blocked(xs, out=bx), mg.mx_scales_blocked(ws, out=bw)))
+               lambda: (mg.mx_scales_blocked(xs, out=bx), mg.mx_scales_blocked(ws, out=bw))]
+        # library comparator: one torch._scaled_mm (hipBLASLt) per expert on the
+        # same codes with the plain [rows, K/32] E8M0 scales, where this build
+        # supports it; its agreement with the grouped call is reported
+        cmp_rec = per_expert_scaled_mm(torch, x8, xs, w8, ws, wl.offsets, mg.fwd_mx(
+            x8, bx, w8, bw, off, hint, out=y8))
+        if "fn" in cmp_rec:
+            fns.append(cmp_rec.pop("fn"))
         for _ in range(5):
             for fn in fns:
                 fn()
@@ -464,6 +527,10 @@ def mx(torch, mg, reps=20):
             "bf16_us": round(t[1], 1), "speedup_vs_bf16": round(t[1] / t[0], 3),
             "scale_layout_us": round(t[2], 1),
             "scale_layout_GBps": round(sc_bytes / t[2] / 1e3, 1)}
+        if len(t) > 3:
+            cmp_rec["us"] = round(t[3], 1)
+            cmp_rec["speedup_of_grouped"] = round(t[3] / t[0], 3)
+        out[f"fwd_mx:{wl.name}"]["per_expert_scaled_mm"] = cmp_rec
         del x8, w8, xs, ws, bx, bw, x, w, y8, y
         torch.cuda.empty_cache()
     # weight gradients: uniform g8 and the skewed 30B-A3B ones, experts padded to
