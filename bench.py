@@ -469,6 +469,44 @@ def per_expert_scaled_mm(torch, x8, xs, w8, ws, offsets, y_grouped):
     return rec
 
 
+def per_expert_scaled_mm_wgrad(torch, dyt8, dyts, xt8, xts, offsets, dw_grouped):
+    """The MXFP8 weight gradient as a loop of torch._scaled_mm calls, one per
+    non-empty expert: dW_e = DYT[:, rows_e] XT[:, rows_e]^T, on contiguous
+    per-expert copies of the codes and plain E8M0 scales (made once, outside
+    any timing).  The library's block-scaled path writes bf16 only, so its dW
+    is bf16 where the grouped call's is fp32.  Returns {"fn": ...} with the
+    relative Frobenius difference from the grouped call's result, or
+    {"error": ...}."""
+    if not hasattr(torch, "_scaled_mm") or not hasattr(torch, "float8_e8m0fnu"):
+        return {"error": "torch._scaled_mm with E8M0 scales not in this build"}
+    ends = [int(v) for v in offsets]
+    live = [e for e in range(len(ends) - 1) if ends[e + 1] > ends[e]]
+    blocks = []
+    for e in live:
+        lo, hi = ends[e], ends[e + 1]
+        blocks.append((e, dyt8[:, lo:hi].contiguous().view(torch.float8_e4m3fn),
+                       dyts[:, lo // 32:hi // 32].contiguous().view(torch.float8_e8m0fnu),
+                       xt8[:, lo:hi].contiguous().view(torch.float8_e4m3fn),
+                       xts[:, lo // 32:hi // 32].contiguous().view(torch.float8_e8m0fnu)))
+
+    def run():
+        return [torch._scaled_mm(a, b.t(), scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16)
+                for _, a, sa, b, sb in blocks]
+
+    try:
+        ys = run()
+        torch.cuda.synchronize()
+    except Exception as exc:
+        return {"error": f"{type(exc).__name__}: {str(exc)[:400]}"}
+    num = den = 0.0
+    for (e, *_), ye in zip(blocks, ys):
+        g = dw_grouped[e]
+        num += float((ye.float() - g).pow(2).sum())
+        den += float(g.pow(2).sum())
+    return {"fn": run, "out_dtype": "bf16",
+            "rel_frobenius_vs_grouped": float(f"{(num / max(den, 1e-300)) ** 0.5:.3e}")}
+
+
 def mx(torch, mg, reps=20):
     """The MXFP8 grouped forward (E4M3 operands, E8M0 scales per 32 steps) on
     the uniform g8 shape and the 30B-A3B share's two expert GEMMs, timed
@@ -544,17 +582,22 @@ def mx(torch, mg, reps=20):
         off = torch.from_numpy(offn).cuda()
         dyt8 = u8(mx_e4m3_codes((N, M), 8310, wl.cfg, wl.tag, 1))
         xt8 = u8(mx_e4m3_codes((K, M), 8310, wl.cfg, wl.tag, 2))
-        bd = mg.mx_scales_blocked(u8(mx_e8m0_codes((N, M // 32), 121, 1, 8310, wl.cfg, wl.tag, 3)))
-        bx = mg.mx_scales_blocked(u8(mx_e8m0_codes((K, M // 32), 121, 1, 8310, wl.cfg, wl.tag, 4)))
+        dyts = u8(mx_e8m0_codes((N, M // 32), 121, 1, 8310, wl.cfg, wl.tag, 3))
+        xts = u8(mx_e8m0_codes((K, M // 32), 121, 1, 8310, wl.cfg, wl.tag, 4))
+        bd, bx = mg.mx_scales_blocked(dyts), mg.mx_scales_blocked(xts)
         dy = torch.randn((M, N), device="cuda").to(torch.bfloat16)
         x = torch.randn((M, K), device="cuda").to(torch.bfloat16)
         dy8, x8 = dyt8.t().contiguous(), xt8.t().contiguous()      # token-major codes
         d8 = torch.empty((E, N, K), dtype=torch.float32, device="cuda")
         d16 = torch.empty_like(d8)
         dtm = torch.empty_like(d8)
-        fns = (lambda: mg.wgrad_mx(dyt8, bd, xt8, bx, off, E, out=d8),
+        fns = [lambda: mg.wgrad_mx(dyt8, bd, xt8, bx, off, E, out=d8),
                lambda: mg.wgrad(dy, x, off, E, out=d16),
-               lambda: mg.wgrad_mx_tm(dy8, bd, x8, bx, off, E, out=dtm))
+               lambda: mg.wgrad_mx_tm(dy8, bd, x8, bx, off, E, out=dtm)]
+        cmp_rec = per_expert_scaled_mm_wgrad(torch, dyt8, dyts, xt8, xts, offn,
+                                             mg.wgrad_mx(dyt8, bd, xt8, bx, off, E, out=d8))
+        if "fn" in cmp_rec:
+            fns.append(cmp_rec.pop("fn"))
         for _ in range(3):
             for fn in fns:
                 fn()
@@ -576,7 +619,11 @@ def mx(torch, mg, reps=20):
             "bf16_us": round(t[1], 1), "speedup_vs_bf16": round(t[1] / t[0], 3),
             "token_major_us": round(t[2], 1),
             "token_major_pct_fp8_peak": round(100 * flops / t[2] / 1e6 / PEAK_FP8_TFLOPS, 1)}
-        del dyt8, xt8, dy8, x8, bd, bx, dy, x, d8, d16, dtm
+        if len(t) > 3:
+            cmp_rec["us"] = round(t[3], 1)
+            cmp_rec["speedup_of_grouped"] = round(t[3] / t[0], 3)
+        out[f"wgrad_mx:{wl.name}"]["per_expert_scaled_mm"] = cmp_rec
+        del dyt8, xt8, dyts, xts, dy8, x8, bd, bx, dy, x, d8, d16, dtm
         torch.cuda.empty_cache()
     return out
 
