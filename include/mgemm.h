@@ -24,7 +24,9 @@
  *     the host and synchronises the stream).
  *   - All data pointers are DEVICE pointers, 16-byte aligned; N and K must be
  *     multiples of 8 (every row starts 16-byte aligned).  1 <= E <= 1024.
- *     M, N, K < 2^31.  Outputs must not alias inputs.
+ *     M < 2^31, N and K <= 2^22 (the longest reduction one tile runs), and
+ *     a call's count of 256 x 256 output tiles below 2^31.  Each call below
+ *     adds its own limits.  Outputs must not alias inputs.
  *   - stream: a hipStream_t (NULL = the null stream).  Each call only
  *     enqueues work on that stream and returns; it never synchronises or
  *     keeps a caller pointer after returning.  The caller owns every buffer
@@ -185,7 +187,9 @@ mg_status mgemm_list(const mg_gemm_desc* desc, int32_t G, void* stream);
 
 /* Host-side check of a descriptor list held in HOST memory (no device use):
  * MG_OK, or MG_ERR_SHAPE / MG_ERR_NULL / MG_ERR_ALIGN for the first group that
- * breaks the rules above. */
+ * breaks the rules above (within a group a size error is reported before a
+ * NULL pointer, and a NULL pointer before a misaligned one; pointers of a
+ * group with m == 0 or n == 0, and a and b when k == 0, are not checked). */
 mg_status mg_check_list_host(const mg_gemm_desc* desc_host, int32_t G);
 
 /* MXFP8 M-grouped forward (torchao PR #3416: MoE training with MXFP8
