@@ -39,7 +39,7 @@ def offsets_case(draw):
     return off, E, M
 
 
-@settings(max_examples=400, derandomize=True, deadline=None)
+@settings(max_examples=400, derandomize=True, deadline=None, database=None)
 @given(offsets_case())
 def test_offsets_check_follows_the_header(case):
     off, E, M = case
@@ -90,7 +90,7 @@ ld = st.sampled_from([0, 8, 12, 16, 24, 64, MAX_DIM, MAX_DIM + 8])
 group = st.tuples(ptr, ptr, ptr, dim, dim, dim, ld, ld, ld)
 
 
-@settings(max_examples=600, derandomize=True, deadline=None)
+@settings(max_examples=600, derandomize=True, deadline=None, database=None)
 @given(st.lists(group, min_size=1, max_size=5))
 def test_list_check_follows_the_header(descs):
     arr = (GemmDesc * len(descs))(*[GemmDesc(*d) for d in descs])
