@@ -453,7 +453,7 @@ def test_mx_longest_reductions_sampled():
 # row or column, or a code from the wrong place, changes the bits.
 
 from oracle import f64_to_bf16_bits  # noqa: E402
-from workloads.synth import mx_e8m0_row_codes, mx_small_int_codes  # noqa: E402
+from workloads.synth import mx_e8m0_pair_codes, mx_e8m0_row_codes, mx_small_int_codes  # noqa: E402
 
 MX_EXACT_FWD = [([300, 0, 17, 513], 264, 2048), ([1, 255, 257], 136, 96), ([700], 520, 416)]
 
@@ -514,6 +514,51 @@ def test_wgrad_mx_exact_on_small_integers(case):
     xt8 = mx_small_int_codes((K, M), 8920, case, 2)
     dyts = mx_e8m0_row_codes(N, M // 32, 127, 6, 8920, case, 3)
     xts = mx_e8m0_row_codes(K, M // 32, 127, 6, 8920, case, 4)
+    exact = grouped_wgrad_mx(dyt8, dyts, xt8, xts, off, E)
+    assert (exact.astype(np.float32).astype(np.float64) == exact).all()
+    bd, bx = _u8(mx_scales_blocked(dyts)), _u8(mx_scales_blocked(xts))
+    o = dev_i32(off)
+    a = mg.wgrad_mx(_u8(dyt8), bd, _u8(xt8), bx, o, E,
+                    out=torch.full((E, N, K), float("nan"), device="cuda"))
+    b = mg.wgrad_mx_tm(_u8(np.ascontiguousarray(dyt8.T)), bd, _u8(np.ascontiguousarray(xt8.T)),
+                       bx, o, E, out=torch.full((E, N, K), float("nan"), device="cuda"))
+    torch.cuda.synchronize()
+    for got, what in ((a.cpu().numpy(), "transposed"), (b.cpu().numpy(), "token-major")):
+        bad = int((got.astype(np.float64) != exact).sum())
+        assert bad == 0, f"{what}: {bad} of {got.size} elements differ from the exact value"
+
+
+def test_fwd_mx_exact_with_block_scales_along_the_reduction():
+    """Small-integer codes with every 32-block scaled by 2^0 or 2^1 at random
+    (X and W): each product is an integer, every partial sum at most 36 K,
+    inside one instruction at most 2304 -- still exact in any order.  The
+    rounded exact value is owed bit for bit, which pins the addressing of the
+    block scales along K (a block scale from the wrong block is off by 2x)."""
+    sizes, N, K = [300, 0, 17, 513], 264, 1024
+    off = offsets_from_sizes(sizes)
+    M, E = int(off[-1]), len(sizes)
+    _say("fwd_mx exact, block scales along K", sizes, N, K)
+    x8 = mx_small_int_codes((M, K), 8930, 1)
+    w8 = mx_small_int_codes((E, N, K), 8930, 2)
+    xs = mx_e8m0_pair_codes((M, K // 32), 127, 8930, 3)
+    ws = mx_e8m0_pair_codes((E, N, K // 32), 127, 8930, 4)
+    got = _run(off, M, N, x8, w8, xs, ws)
+    want = f64_to_bf16_bits(grouped_fwd_mx(x8, xs, w8, ws, off))
+    bad = int((got != want).sum())
+    assert bad == 0, f"{bad} of {got.size} elements differ from the rounded exact value"
+
+
+def test_wgrad_mx_exact_with_block_scales_along_the_tokens():
+    """The same for both MXFP8 weight-gradient calls: 32-token blocks scaled
+    by 2^0 or 2^1 at random, the exact fp32 value owed on every element."""
+    sizes, N, K = [128, 0, 384, 1024], 272, 144
+    off = offsets_from_sizes(sizes)
+    M, E = int(off[-1]) + 128, len(sizes)
+    _say("wgrad_mx exact, block scales along the tokens", sizes, N, K)
+    dyt8 = mx_small_int_codes((N, M), 8940, 1)
+    xt8 = mx_small_int_codes((K, M), 8940, 2)
+    dyts = mx_e8m0_pair_codes((N, M // 32), 127, 8940, 3)
+    xts = mx_e8m0_pair_codes((K, M // 32), 127, 8940, 4)
     exact = grouped_wgrad_mx(dyt8, dyts, xt8, xts, off, E)
     assert (exact.astype(np.float32).astype(np.float64) == exact).all()
     bd, bx = _u8(mx_scales_blocked(dyts)), _u8(mx_scales_blocked(xts))

@@ -269,6 +269,14 @@ def mx_small_int_codes(shape: Sequence[int], *key: int) -> np.ndarray:
     return c.astype(np.uint8).reshape(tuple(shape))
 
 
+def mx_e8m0_pair_codes(shape: Sequence[int], lo: int, *key: int) -> np.ndarray:
+    """uint8 E8M0 scale codes drawn uniformly from {lo, lo + 1}: neighbouring
+    32-blocks scaled by the same power of two or by twice it."""
+    rng = _stream(*key)
+    c = lo + rng.integers(0, 2, int(np.prod(shape, dtype=np.int64)))
+    return c.astype(np.uint8).reshape(tuple(shape))
+
+
 def mx_e8m0_row_codes(rows: int, blocks: int, center: int, spread: int, *key: int) -> np.ndarray:
     """uint8 E8M0 scale codes [rows, blocks], uniform in [center - spread,
     center + spread] per row and the same for every block of a row."""
