@@ -308,6 +308,9 @@ def test_small_integer_inputs_decode_to_integers_and_sum_exactly():
     assert sorted(set(v.tolist())) == [-3.0, -2.0, -1.0, 0.0, 1.0, 2.0, 3.0]
     s = synth.mx_e8m0_row_codes(9, 5, 127, 6, 3, 2)
     assert (s == s[:, :1]).all() and s.min() >= 121 and s.max() <= 133
+    pc = synth.mx_e8m0_pair_codes((64, 8), 127, 3, 7)
+    assert set(np.unique(pc).tolist()) == {127, 128}
+    assert sorted(set(_torch_e8m0(pc).ravel().tolist())) == [1.0, 2.0]
     off = synth.offsets_from_sizes([3, 0, 2])
     M, N, K = 5, 3, 64
     x8 = synth.mx_small_int_codes((M, K), 3, 3)
