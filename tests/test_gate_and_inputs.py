@@ -132,6 +132,29 @@ def test_generators_are_deterministic():
     assert abs(v.mean()) < 0.01 and abs(v.std() - 1) < 0.01
 
 
+def test_small_integer_operands_are_exact_and_their_sums_exact_in_fp32():
+    """The exact-result GPU cases rest on these facts: the generator's bf16
+    bits decode (torch's bf16 cast agrees) to every integer in [-3, 3], and a
+    sum of R products of such values, |sum| <= 9 R, is exact in fp32 for the
+    longest reduction those cases use (10804 tokens)."""
+    import torch
+    from workloads.synth import small_int_bf16_bits
+    b = small_int_bf16_bits((4096,), 5, 6)
+    v = bf16_bits_to_f64(b)
+    assert sorted(set(v.tolist())) == [-3.0, -2.0, -1.0, 0.0, 1.0, 2.0, 3.0]
+    t = torch.from_numpy(b.view(np.int16).copy()).view(torch.bfloat16).double().numpy()
+    assert np.array_equal(t, v)
+    assert 9 * 10804 < 2 ** 24
+    rng = np.random.default_rng(0)
+    a = bf16_bits_to_f64(small_int_bf16_bits((10804,), 5, 7))
+    c = bf16_bits_to_f64(small_int_bf16_bits((10804,), 5, 8))
+    prods = (a * c)[rng.permutation(10804)]
+    s32 = np.float32(0)
+    for p in prods.astype(np.float32):
+        s32 = np.float32(s32 + p)
+    assert float(s32) == float(np.sum(a * c))
+
+
 def test_workload_invariants():
     (tiny,) = make_workload(1)
     assert tiny.offsets.tolist() == [0, 200, 200, 384, 512]

@@ -398,6 +398,58 @@ def test_a3b_zipf_wgrad_whole(name):
     assert r.passed, str(r)
 
 
+# ------------------------------------------- exact results at full size --
+# Operands that are integers in [-3, 3]: every product is an integer of
+# magnitude <= 9 and every partial sum of a reduction of length R at most 9 R,
+# below 2^24 for every reduction here (R <= 10804), so fp32 accumulation in any
+# order is exact.  The kernels then owe the exact value itself -- bf16 outputs
+# its round to nearest even, fp32 outputs the value -- on every element, with
+# no tolerance: a wrong row, column, expert or reduction range changes bits.
+
+def _exact_bf16(kind, exact, got_bits):
+    from oracle import f64_to_bf16_bits
+    want = f64_to_bf16_bits(exact)
+    bad = int((got_bits != want).sum())
+    _say(kind, "elements differing from the rounded exact value:", bad)
+    assert bad == 0, f"{kind}: {bad} of {want.size} elements differ"
+
+
+@pytest.mark.parametrize("name", ["a3b_gate_up", "a3b_down"])
+def test_a3b_mgrouped_exact_on_small_integers(name):
+    from oracle import bf16_bits_to_f64, grouped_dgrad, grouped_fwd
+    from workloads.synth import small_int_bf16_bits
+    (wl,) = make_workload(4, name)
+    _say(wl.name, "exact", wl.rows)
+    xb = small_int_bf16_bits((wl.M, wl.K), 9100, wl.tag, 1)
+    wb = small_int_bf16_bits((wl.E, wl.N, wl.K), 9100, wl.tag, 2)
+    dyb = small_int_bf16_bits((wl.M, wl.N), 9100, wl.tag, 3)
+    hint = int(wl.sizes().max())
+    y, dx = _run_mgrouped(wl.offsets, wl.M, xb, wb, dyb, wl.N, wl.K, hint)
+    last = int(wl.offsets[-1])
+    _check_untouched(y, wl.offsets)
+    _check_untouched(dx, wl.offsets)
+    x, w, dy = bf16_bits_to_f64(xb), bf16_bits_to_f64(wb), bf16_bits_to_f64(dyb)
+    _exact_bf16("fwd", grouped_fwd(x, w, wl.offsets)[:last], y[:last])
+    _exact_bf16("dgrad", grouped_dgrad(dy, w, wl.offsets)[:last], dx[:last])
+
+
+@pytest.mark.parametrize("name", ["a3b_zipf_gw13", "a3b_zipf_gw2"])
+def test_a3b_wgrad_exact_on_small_integers(name):
+    from oracle import bf16_bits_to_f64, grouped_wgrad
+    from workloads.synth import small_int_bf16_bits
+    (wl,) = make_workload(5, name)
+    _say(wl.name, "exact", wl.sizes().max())
+    xb = small_int_bf16_bits((wl.M, wl.K), 9110, wl.tag, 1)
+    dyb = small_int_bf16_bits((wl.M, wl.N), 9110, wl.tag, 2)
+    dw = mg.wgrad(dev_bf16(dyb), dev_bf16(xb), dev_i32(wl.offsets), wl.E,
+                  out=torch.full((wl.E, wl.N, wl.K), float("nan"), device="cuda"))
+    got = dw.cpu().numpy().astype(np.float64)
+    exact = grouped_wgrad(bf16_bits_to_f64(dyb), bf16_bits_to_f64(xb), wl.offsets, wl.E)
+    bad = int((got != exact).sum())
+    _say("wgrad elements differing from the exact value:", bad)
+    assert bad == 0, f"{bad} of {got.size} elements differ"
+
+
 # ------------------------------------- gate-up forward with SwiGLU, gathered --
 
 SW_CASES = [

@@ -62,6 +62,17 @@ def normal_bf16_bits(shape: Sequence[int], scale: float, *key: int) -> np.ndarra
     return out.reshape(tuple(shape))
 
 
+def small_int_bf16_bits(shape: Sequence[int], *key: int) -> np.ndarray:
+    """bf16 bit patterns of integers uniform in [-3, 3] (each exact in bf16)."""
+    rng = _stream(*key)
+    n = int(np.prod(shape, dtype=np.int64))
+    out = np.empty(n, dtype=np.uint16)
+    for lo in range(0, n, _CHUNK):
+        hi = min(n, lo + _CHUNK)
+        out[lo:hi] = _f32_to_bf16_bits(rng.integers(-3, 4, hi - lo).astype(np.float32))
+    return out.reshape(tuple(shape))
+
+
 def offsets_from_sizes(sizes: Sequence[int]) -> np.ndarray:
     """Per-expert row counts -> int32 cumulative offsets with a leading zero."""
     sizes = np.asarray(sizes, dtype=np.int64)
