@@ -1,0 +1,122 @@
+"""Host model of the K-grouped weight gradient's tile placement (CPU).
+
+The device scheduler (`setup_kgrouped` and `balance_kgrouped` in the kernel
+source) places each expert's tiles on the eight XCDs in chunks and deals every
+XCD's list to its workgroups longest-processing-time first.  This file
+restates that rule in Python -- ranking, chunking, the token-split decision,
+the scaled-cost LPT deal with its tie order -- and checks the balance the
+design relies on for the two skewed 30B-A3B weight gradients, against a plain
+snake deal of the same lists.  It is a model of the rule, not a readback of
+the device's placement: that every tile is computed exactly once is shown by
+the GPU parity tests (accumulating calls included).
+"""
+import numpy as np
+
+from workloads import make_workload
+
+BK, BP, BQ = 64, 256, 256
+SPLIT_PER_XCD, SPLIT_MIN_STAGES, SPLIT_COST = 16, 16, 4
+
+
+def chunk_size(k, per, whole):
+    start = lambda j: (0 if j == 0 else per) if whole else (j * per) >> 3
+    return start(k + 1) - start(k)
+
+
+def place(sizes, N, K, nx=32, split=True, deal="lpt"):
+    """Per XCD, the real cost (stages + 3, a split half's stages + 3 + 4) each
+    of its nx workgroups is given."""
+    sizes = [max(int(m), 0) for m in sizes]
+    E = len(sizes)
+    per = ((N + BQ - 1) // BQ) * ((K + BP - 1) // BP)
+    whole = len(set(sizes)) == 1 and E % 8 == 0 and sizes[0] > 0
+    inv = sorted(range(E), key=lambda e: (-sizes[e], e))       # heaviest first
+    stages = lambda m: (m + BK - 1) // BK
+    loads = []
+    for x in range(8):
+        runs = [(sizes[inv[r]], chunk_size((x - r) & 7, per, whole)) for r in range(E)]
+        avg = sum(c * (stages(m) + 3) for m, c in runs) // nx
+        heavy = lambda m: stages(m) >= SPLIT_MIN_STAGES and stages(m) + 3 > avg
+        nheavy = sum(c for m, c in runs if heavy(m))
+        split_on = split and 0 < nheavy <= SPLIT_PER_XCD and 2 * nheavy <= nx
+        pieces = []
+        for m, c in runs:
+            if split_on and heavy(m):
+                pieces.append((2 * c, (stages(m) + 1) // 2 + 3 + SPLIT_COST))
+            else:
+                pieces.append((c, stages(m) + 3))
+        real = [0] * nx
+        if deal == "snake":
+            i = 0
+            for c, w in pieces:
+                for _ in range(c):
+                    lap, pos = divmod(i, nx)
+                    real[pos if lap % 2 == 0 else nx - 1 - pos] += w
+                    i += 1
+            loads.append(real)
+            continue
+        tot = sum(c * w for c, w in pieces)
+        ntiles = sum(c for c, _ in pieces)
+        ws = [w for c, w in pieces if c > 0]
+        sh = 0
+        while (tot >> sh) >= (1 << 15):
+            sh += 1
+        equal = min(ws) >= max(ws) or (((tot >> sh) + ntiles) >> 25) != 0
+        scaled = [0] * nx
+        pos = 0
+        for c, w in pieces:
+            if c == 0:
+                continue
+            full, rem = divmod(c, nx)
+            if equal:
+                rho = [(me - pos) % nx for me in range(nx)]
+                pos = (pos + rem) % nx
+            else:
+                keys = [(scaled[me] << 6) | me for me in range(nx)]
+                order = sorted(range(nx), key=lambda me: keys[me])
+                rho = [0] * nx
+                for rank, me in enumerate(order):
+                    rho[me] = rank
+                ws_ = (w >> sh) + 1
+                for me in range(nx):
+                    scaled[me] += full * ws_ + (ws_ if rho[me] < rem else 0)
+            for me in range(nx):
+                real[me] += (full + (1 if rho[me] < rem else 0)) * w
+        loads.append(real)
+    return loads
+
+
+def worst_over_mean(loads):
+    flat = np.asarray(loads, dtype=np.float64)
+    return float(flat.max() / flat.mean() - 1.0)
+
+
+def test_every_tile_is_placed_once():
+    for name in ("a3b_zipf_gw13", "a3b_zipf_gw2"):
+        (wl,) = make_workload(5, name)
+        sizes = wl.sizes()
+        per = ((wl.N + BQ - 1) // BQ) * ((wl.K + BP - 1) // BP)
+        stages = lambda m: (int(m) + BK - 1) // BK
+        want = sum(per * (stages(m) + 3) for m in sizes)
+        got = sum(map(sum, place(sizes, wl.N, wl.K, split=False)))
+        assert got == want, name
+
+
+def test_lpt_balance_of_the_skewed_weight_gradients():
+    """gw13: no tile above the XCDs' average load, no split, the LPT deal
+    within a few stages of the mean; gw2: its heaviest expert's 172-stage
+    tiles exceed the average, unsplit they leave the worst workgroup ~18%
+    above the mean, split in two the LPT deal comes within a few percent; a
+    snake deal of the same lists is far worse on both."""
+    (g13,) = make_workload(5, "a3b_zipf_gw13")
+    (g2,) = make_workload(5, "a3b_zipf_gw2")
+    lpt13 = worst_over_mean(place(g13.sizes(), g13.N, g13.K))
+    lpt2 = worst_over_mean(place(g2.sizes(), g2.N, g2.K))
+    lpt2_nosplit = worst_over_mean(place(g2.sizes(), g2.N, g2.K, split=False))
+    snake13 = worst_over_mean(place(g13.sizes(), g13.N, g13.K, split=False, deal="snake"))
+    snake2 = worst_over_mean(place(g2.sizes(), g2.N, g2.K, split=False, deal="snake"))
+    print(f"worst/mean - 1: gw13 LPT {lpt13:.3f} snake {snake13:.3f}; "
+          f"gw2 LPT {lpt2:.3f} (unsplit {lpt2_nosplit:.3f}) snake {snake2:.3f}")
+    assert lpt13 < 0.03 and lpt2 < 0.05
+    assert lpt2_nosplit > 0.15
+    assert snake13 > 0.15 and snake2 > 0.5
