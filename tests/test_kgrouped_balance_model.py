@@ -1,4 +1,5 @@
-"""Host model of the K-grouped weight gradient's tile placement (CPU).
+"""Host models of the tile placement rules (CPU): the K-grouped weight
+gradient's and the descriptor list's.
 
 The device scheduler (`setup_kgrouped` and `balance_kgrouped` in the kernel
 source) places each expert's tiles on the eight XCDs in chunks and deals every
@@ -120,3 +121,40 @@ def test_lpt_balance_of_the_skewed_weight_gradients():
     assert lpt13 < 0.03 and lpt2 < 0.05
     assert lpt2_nosplit > 0.15
     assert snake13 > 0.15 and snake2 > 0.5
+
+
+# -- descriptor list: contiguous tile ranges of equal cost per XCD ------------
+
+def list_ranges(groups):
+    """XCD x starts at the number of tiles whose cost midpoint lies below x/8
+    of the total cost (a tile of a group with reduction k costs
+    ceil(k/64) + 3); groups are (m, n, k) with 256 x 256 tiles."""
+    tiles = []
+    for m, n, k in groups:
+        cnt = ((m + BQ - 1) // BQ) * ((n + BP - 1) // BP) if m > 0 and n > 0 else 0
+        tiles += [(max(k, 0) + BK - 1) // BK + 3] * cnt
+    W = sum(tiles)
+    starts, c0 = [], 0
+    mids = []
+    for w in tiles:
+        mids.append(8 * c0 + 4 * w)          # 8 x the cost midpoint
+        c0 += w
+    for x in range(9):
+        starts.append(len(tiles) if x == 8 else sum(1 for mid in mids if mid < x * W))
+    return tiles, starts, W
+
+
+def test_list_xcd_ranges_are_within_one_tile_of_an_eighth():
+    rng = np.random.default_rng(5)
+    cases = [[(1027, 2560, 3072)] * 32 + [(1027, 3072, 1280)] * 32]      # gate-up + down
+    for _ in range(300):
+        G = int(rng.integers(1, 40))
+        cases.append([(int(rng.integers(0, 3000)), int(rng.integers(0, 5)) * 256 + 8 *
+                       int(rng.integers(0, 32)), int(rng.integers(0, 8000))) for _ in range(G)])
+    for groups in cases:
+        tiles, starts, W = list_ranges(groups)
+        assert starts[0] == 0 and starts == sorted(starts)
+        wmax = max(tiles, default=0)
+        for x in range(8):
+            load = sum(tiles[starts[x]:starts[x + 1]])
+            assert abs(8 * load - W) <= 8 * wmax, (groups, x)
