@@ -79,6 +79,9 @@ def parse_args():
     p.add_argument("--mx", action="store_true",
                    help="also time the MXFP8 grouped forward against the bf16 one on the same "
                         "shapes (reported only)")
+    p.add_argument("--ceiling", action="store_true",
+                   help="also run the matrix-core ceiling probe (libmgemm_probe.so): the rate "
+                        "of the bf16 products alone, no memory traffic (reported only)")
     return p.parse_args()
 
 
@@ -628,6 +631,59 @@ def mx(torch, mg, reps=20):
     return out
 
 
+# ------------------------------------------------------------------ ceiling --
+
+def ceiling(torch, seconds=3.0, iters=16384):
+    """The matrix-core ceiling probe: one workgroup of 8 waves per compute
+    unit issuing only v_mfma_f32_32x32x16_bf16 on register-held random
+    operands (include/mgemm_probe.h).  Launches repeat for `seconds` to reach
+    the steady power state; the last second's HIP-event rate is reported with
+    the graphics clock sampled while the probe runs again."""
+    import ctypes
+    path = os.path.join(ROOT, "moe_grouped_gemm_bf16_amd", "libmgemm_probe.so")
+    if not os.path.exists(path):
+        return {"error": "libmgemm_probe.so not built"}
+    lib = ctypes.CDLL(path)
+    lib.mg_probe_mfma_bf16.restype = ctypes.c_int
+    lib.mg_probe_mfma_bf16.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+    lib.mg_probe_mfma_bf16_flops.restype = ctypes.c_double
+    lib.mg_probe_mfma_bf16_flops.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    blocks = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(blocks * 512, dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+
+    def launch():
+        if lib.mg_probe_mfma_bf16(blocks, iters, out.data_ptr(), st) != 0:
+            raise RuntimeError("probe launch failed")
+
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds - 1.0:
+        for _ in range(10):
+            launch()
+        torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 0
+    a.record()
+    t1 = time.perf_counter()
+    while time.perf_counter() - t1 < 1.0:
+        for _ in range(10):
+            launch()
+        n += 10
+        torch.cuda.synchronize()
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / n
+    tflops = lib.mg_probe_mfma_bf16_flops(blocks, iters) / us / 1e6
+    clock = ClockSampler().measure(launch, torch, seconds=2.5)
+    rec = {"tflops": round(tflops, 1), "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 1),
+           "us_per_launch": round(us, 1), "launches_timed": n, "workgroups": blocks,
+           "products_per_wave": iters * 8}
+    if clock:
+        rec["gfx_mhz_median"] = clock.get("gfx_mhz_median")
+    return rec
+
+
 # ------------------------------------------------------------- CPU baseline --
 
 def cpu_baseline(workload: str):
@@ -921,6 +977,11 @@ def main():
         print("[bench] timing the MXFP8 forward", file=sys.stderr, flush=True)
         mxr = mx(torch, mg)
 
+    ceil_rec = None
+    if args.ceiling:
+        print("[bench] running the matrix-core ceiling probe", file=sys.stderr, flush=True)
+        ceil_rec = ceiling(torch)
+
     fused = None
     if args.fusions:
         print("[bench] timing the fused gate-up forward", file=sys.stderr, flush=True)
@@ -972,6 +1033,8 @@ def main():
         line["list_ops"] = listed
     if mxr is not None:
         line["mx_ops"] = mxr
+    if ceil_rec is not None:
+        line["mfma_ceiling"] = ceil_rec
     print(json.dumps(line), flush=True)
 
 

@@ -1,4 +1,5 @@
-"""Build libmgemm.so in-tree with hipcc for gfx950.
+"""Build libmgemm.so (and the matrix-core ceiling probe, libmgemm_probe.so)
+in-tree with hipcc for gfx950.
 
     python moe_grouped_gemm_bf16_amd/build.py [--verbose]
 
@@ -19,6 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmgemm.so")
 SOURCES = ["mgemm_kernels.hip", "mgemm_combine.hip", "mgemm_api.cpp"]
+PROBE_LIB = os.path.join(PKG, "libmgemm_probe.so")
+PROBE_SOURCES = ["mgemm_probe.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -40,9 +43,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libmgemm.so)")
 
 
-def build(verbose: bool = False, extra: list[str] | None = None) -> str:
+def _link(sources: list[str], target: str, verbose: bool, extra: list[str] | None) -> str:
     cmd = [hipcc(), *HIPCC_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", *(extra or []),
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", LIB + ".tmp"]
+           *[os.path.join(CSRC, s) for s in sources], "-o", target + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -52,8 +55,13 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, flush=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(target + ".tmp", target)
+    return target
+
+
+def build(verbose: bool = False, extra: list[str] | None = None) -> str:
+    _link(PROBE_SOURCES, PROBE_LIB, verbose, extra)
+    return _link(SOURCES, LIB, verbose, extra)
 
 
 if __name__ == "__main__":

@@ -233,3 +233,24 @@ def test_host_list_check():
     assert _lib.LIB.mg_check_list_host(arr, 0) == _lib.MG_ERR_SHAPE
     assert _lib.LIB.mgemm_list(None, 1, None) == _lib.MG_ERR_NULL
     assert _lib.LIB.mgemm_list(ctypes.addressof(arr), 2000, None) == _lib.MG_ERR_SHAPE
+
+
+def test_probe_library_exports_its_header_and_rejects_bad_arguments():
+    """libmgemm_probe.so (the matrix-core ceiling probe bench.py --ceiling
+    runs) exports what include/mgemm_probe.h declares; bad arguments return
+    1 before any device call."""
+    probe_h = os.path.join(ROOT, "include", "mgemm_probe.h")
+    text = re.sub(r"/\*.*?\*/", "", open(probe_h).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"if", "defined"})
+    assert names == ["mg_probe_mfma_bf16", "mg_probe_mfma_bf16_flops"]
+    lib = ctypes.CDLL(os.path.join(ROOT, "moe_grouped_gemm_bf16_amd", "libmgemm_probe.so"))
+    for n in names:
+        assert hasattr(lib, n), n
+    lib.mg_probe_mfma_bf16.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+    lib.mg_probe_mfma_bf16_flops.restype = ctypes.c_double
+    lib.mg_probe_mfma_bf16_flops.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    assert lib.mg_probe_mfma_bf16(0, 1, A, None) == 1
+    assert lib.mg_probe_mfma_bf16(1, 0, A, None) == 1
+    assert lib.mg_probe_mfma_bf16(1, 1, None, None) == 1
+    assert lib.mg_probe_mfma_bf16_flops(256, 16384) == 256 * 16384 * 64 * 32768.0
