@@ -417,12 +417,30 @@ def lists(torch, mg, reps=20):
 
 # ----------------------------------------------------------------------- mx --
 
-def per_expert_scaled_mm(torch, x8, xs, w8, ws, offsets, y_grouped):
+def time_alone(torch, fn, reps, warm=3):
+    """Median HIP-event time (us) of fn, launched back to back on its own (a
+    library loop's host cost between its launches is part of its time)."""
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        ts.append((a, b))
+    torch.cuda.synchronize()
+    return statistics.median(a.elapsed_time(b) for a, b in ts) * 1e3
+
+
+def per_expert_scaled_mm(torch, x8, xs, w8, ws, offsets):
     """A loop of torch._scaled_mm calls, one per non-empty expert, on MXFP8
     codes with E8M0 scales per 32 reduction steps (uint8 [rows, K/32]).
-    Returns {"fn": the loop} when the call works here, with the relative
-    Frobenius difference of its result from the grouped call's; else
-    {"error": ...}.  Where the library refuses an expert's row count, each
+    Returns {"fn": the loop, "compare": a function of the grouped call's
+    output giving the relative Frobenius difference from the loop's} when the
+    call works here, else {"error": ...}.  Where the library refuses an
+    expert's row count, each
     expert's rows are copied once (outside any timing) into a block padded
     with zero codes to a multiple of 128 rows, and the loop runs on those."""
     if not hasattr(torch, "_scaled_mm") or not hasattr(torch, "float8_e8m0fnu"):
@@ -459,27 +477,28 @@ def per_expert_scaled_mm(torch, x8, xs, w8, ws, offsets, y_grouped):
             torch.cuda.synchronize()
         except Exception as exc2:
             return {"error": first, "padded_error": f"{type(exc2).__name__}: {str(exc2)[:200]}"}
-    num = den = 0.0
-    for e, ye in zip(live, ys):
-        g = y_grouped[ends[e]:ends[e + 1]].float()
-        num += float((ye[:g.shape[0]].float() - g).pow(2).sum())
-        den += float(g.pow(2).sum())
-    rec = {"fn": lambda: run(blocks),
-           "rel_frobenius_vs_grouped": float(f"{(num / max(den, 1e-300)) ** 0.5:.3e}")}
+    def compare(y_grouped):
+        num = den = 0.0
+        for e, ye in zip(live, ys):
+            g = y_grouped[ends[e]:ends[e + 1]].float()
+            num += float((ye[:g.shape[0]].float() - g).pow(2).sum())
+            den += float(g.pow(2).sum())
+        return float(f"{(num / max(den, 1e-300)) ** 0.5:.3e}")
+
+    rec = {"fn": lambda: run(blocks), "compare": compare}
     if padded:
         rec["rows_padded_to_128"] = sum(int(xa.shape[0]) for _, xa, _ in blocks)
         rec["unpadded_error"] = first
     return rec
 
 
-def per_expert_scaled_mm_wgrad(torch, dyt8, dyts, xt8, xts, offsets, dw_grouped):
+def per_expert_scaled_mm_wgrad(torch, dyt8, dyts, xt8, xts, offsets):
     """The MXFP8 weight gradient as a loop of torch._scaled_mm calls, one per
     non-empty expert: dW_e = DYT[:, rows_e] XT[:, rows_e]^T, on contiguous
     per-expert copies of the codes and plain E8M0 scales (made once, outside
     any timing).  The library's block-scaled path writes bf16 only, so its dW
-    is bf16 where the grouped call's is fp32.  Returns {"fn": ...} with the
-    relative Frobenius difference from the grouped call's result, or
-    {"error": ...}."""
+    is bf16 where the grouped call's is fp32.  Returns {"fn": ..., "compare":
+    ...} as per_expert_scaled_mm does, or {"error": ...}."""
     if not hasattr(torch, "_scaled_mm") or not hasattr(torch, "float8_e8m0fnu"):
         return {"error": "torch._scaled_mm with E8M0 scales not in this build"}
     ends = [int(v) for v in offsets]
@@ -501,13 +520,15 @@ def per_expert_scaled_mm_wgrad(torch, dyt8, dyts, xt8, xts, offsets, dw_grouped)
         torch.cuda.synchronize()
     except Exception as exc:
         return {"error": f"{type(exc).__name__}: {str(exc)[:400]}"}
-    num = den = 0.0
-    for (e, *_), ye in zip(blocks, ys):
-        g = dw_grouped[e]
-        num += float((ye.float() - g).pow(2).sum())
-        den += float(g.pow(2).sum())
-    return {"fn": run, "out_dtype": "bf16",
-            "rel_frobenius_vs_grouped": float(f"{(num / max(den, 1e-300)) ** 0.5:.3e}")}
+    def compare(dw_grouped):
+        num = den = 0.0
+        for (e, *_), ye in zip(blocks, ys):
+            g = dw_grouped[e]
+            num += float((ye.float() - g).pow(2).sum())
+            den += float(g.pow(2).sum())
+        return float(f"{(num / max(den, 1e-300)) ** 0.5:.3e}")
+
+    return {"fn": run, "compare": compare, "out_dtype": "bf16"}
 
 
 def mx(torch, mg, reps=20):
@@ -542,10 +563,9 @@ def mx(torch, mg, reps=20):
         # library comparator: one torch._scaled_mm (hipBLASLt) per expert on the
         # same codes with the plain [rows, K/32] E8M0 scales, where this build
         # supports it; its agreement with the grouped call is reported
-        cmp_rec = per_expert_scaled_mm(torch, x8, xs, w8, ws, wl.offsets, mg.fwd_mx(
-            x8, bx, w8, bw, off, hint, out=y8))
-        if "fn" in cmp_rec:
-            fns.append(cmp_rec.pop("fn"))
+        cmp_rec = per_expert_scaled_mm(torch, x8, xs, w8, ws, wl.offsets)
+        compare = cmp_rec.pop("compare", None)
+        cmp_fn = cmp_rec.pop("fn", None)
         for _ in range(5):
             for fn in fns:
                 fn()
@@ -568,9 +588,12 @@ def mx(torch, mg, reps=20):
             "bf16_us": round(t[1], 1), "speedup_vs_bf16": round(t[1] / t[0], 3),
             "scale_layout_us": round(t[2], 1),
             "scale_layout_GBps": round(sc_bytes / t[2] / 1e3, 1)}
-        if len(t) > 3:
-            cmp_rec["us"] = round(t[3], 1)
-            cmp_rec["speedup_of_grouped"] = round(t[3] / t[0], 3)
+        if cmp_fn is not None:                    # timed on its own, after the others
+            tc = time_alone(torch, cmp_fn, reps)
+            cmp_rec["us"] = round(tc, 1)
+            cmp_rec["speedup_of_grouped"] = round(tc / t[0], 3)
+        if compare is not None:                   # y8: the grouped call's last result
+            cmp_rec["rel_frobenius_vs_grouped"] = compare(y8)
         out[f"fwd_mx:{wl.name}"]["per_expert_scaled_mm"] = cmp_rec
         del x8, w8, xs, ws, bx, bw, x, w, y8, y
         torch.cuda.empty_cache()
@@ -597,10 +620,9 @@ def mx(torch, mg, reps=20):
         fns = [lambda: mg.wgrad_mx(dyt8, bd, xt8, bx, off, E, out=d8),
                lambda: mg.wgrad(dy, x, off, E, out=d16),
                lambda: mg.wgrad_mx_tm(dy8, bd, x8, bx, off, E, out=dtm)]
-        cmp_rec = per_expert_scaled_mm_wgrad(torch, dyt8, dyts, xt8, xts, offn,
-                                             mg.wgrad_mx(dyt8, bd, xt8, bx, off, E, out=d8))
-        if "fn" in cmp_rec:
-            fns.append(cmp_rec.pop("fn"))
+        cmp_rec = per_expert_scaled_mm_wgrad(torch, dyt8, dyts, xt8, xts, offn)
+        compare = cmp_rec.pop("compare", None)
+        cmp_fn = cmp_rec.pop("fn", None)
         for _ in range(3):
             for fn in fns:
                 fn()
@@ -622,9 +644,12 @@ def mx(torch, mg, reps=20):
             "bf16_us": round(t[1], 1), "speedup_vs_bf16": round(t[1] / t[0], 3),
             "token_major_us": round(t[2], 1),
             "token_major_pct_fp8_peak": round(100 * flops / t[2] / 1e6 / PEAK_FP8_TFLOPS, 1)}
-        if len(t) > 3:
-            cmp_rec["us"] = round(t[3], 1)
-            cmp_rec["speedup_of_grouped"] = round(t[3] / t[0], 3)
+        if cmp_fn is not None:                    # timed on its own, after the others
+            tc = time_alone(torch, cmp_fn, reps)
+            cmp_rec["us"] = round(tc, 1)
+            cmp_rec["speedup_of_grouped"] = round(tc / t[0], 3)
+        if compare is not None:                   # d8: the grouped call's last result
+            cmp_rec["rel_frobenius_vs_grouped"] = compare(d8)
         out[f"wgrad_mx:{wl.name}"]["per_expert_scaled_mm"] = cmp_rec
         del dyt8, xt8, dyts, xts, dy8, x8, bd, bx, dy, x, d8, d16, dtm
         torch.cuda.empty_cache()
