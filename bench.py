@@ -153,20 +153,8 @@ def comparators(ops, torch, reps=20):
     TransformerEngine PR #2045 perf table) and torch._grouped_mm where this torch
     has it.  Operands that the libraries want in the other orientation are made
     contiguous before the timed region.  Both emit bf16 for wgrad (the kernel
-    under test writes fp32)."""
-    def timed(fn):
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(reps)]
-        for a, b in ev:
-            a.record()
-            fn()
-            b.record()
-        torch.cuda.synchronize()
-        return statistics.median(a.elapsed_time(b) for a, b in ev) * 1e3
-
+    under test writes fp32).  Each is timed with the host's enqueue hidden
+    (`us`, the GPU's time) and back to back (`us_host_inclusive`)."""
     out = {}
     for op in ops:
         t, o = op.tensors, [int(v) for v in op.wl.offsets]
@@ -187,13 +175,13 @@ def comparators(ops, torch, reps=20):
             dyt, x = t["dy"].t().contiguous(), t["x"]           # dY^T [N, M]
             loop = lambda: [torch.matmul(dyt[:, i:j], x[i:j]) for e, i, j in spans]
             grp = lambda: torch._grouped_mm(dyt, x, offs=ends)
-        us = timed(loop)
-        rec["hipblaslt_per_expert_loop"] = {"us": round(us, 1),
+        th, us = time_library(torch, loop, reps)
+        rec["hipblaslt_per_expert_loop"] = {"us": round(us, 1), "us_host_inclusive": round(th, 1),
                                             "tflops": round(op.flops / us / 1e6, 1)}
         if hasattr(torch, "_grouped_mm"):
             try:
-                us = timed(grp)
-                rec["torch_grouped_mm"] = {"us": round(us, 1),
+                th, us = time_library(torch, grp, reps)
+                rec["torch_grouped_mm"] = {"us": round(us, 1), "us_host_inclusive": round(th, 1),
                                            "tflops": round(op.flops / us / 1e6, 1)}
             except Exception as exc:                       # not supported by this PyTorch
                 rec["torch_grouped_mm"] = {"error": f"{type(exc).__name__}: {str(exc)[:120]}"}
@@ -417,14 +405,21 @@ def lists(torch, mg, reps=20):
 
 # ----------------------------------------------------------------------- mx --
 
-def time_alone(torch, fn, reps, warm=3):
-    """Median HIP-event time (us) of fn, launched back to back on its own (a
-    library loop's host cost between its launches is part of its time)."""
+def time_alone(torch, fn, reps, warm=3, hide_host=False):
+    """Median HIP-event time (us) of fn launched on its own.  By default the
+    launches go back to back, so a library loop's host cost between its
+    launches is part of its time; with hide_host each repetition is enqueued
+    behind a GPU sleep of ~10 ms (torch.cuda._sleep), so that the host has
+    queued the whole loop before the first event runs and the time is the
+    GPU's alone."""
     for _ in range(warm):
         fn()
     torch.cuda.synchronize()
     ts = []
     for _ in range(reps):
+        if hide_host:
+            torch.cuda.synchronize()
+            torch.cuda._sleep(20_000_000)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         fn()
@@ -432,6 +427,14 @@ def time_alone(torch, fn, reps, warm=3):
         ts.append((a, b))
     torch.cuda.synchronize()
     return statistics.median(a.elapsed_time(b) for a, b in ts) * 1e3
+
+
+def time_library(torch, fn, reps):
+    """A library loop's time two ways: back to back (host cost included) and
+    with the host's enqueue hidden (the GPU's time alone)."""
+    host = time_alone(torch, fn, reps)
+    gpu = time_alone(torch, fn, reps, hide_host=hasattr(torch.cuda, "_sleep"))
+    return host, gpu
 
 
 def per_expert_scaled_mm(torch, x8, xs, w8, ws, offsets):
@@ -589,9 +592,10 @@ def mx(torch, mg, reps=20):
             "scale_layout_us": round(t[2], 1),
             "scale_layout_GBps": round(sc_bytes / t[2] / 1e3, 1)}
         if cmp_fn is not None:                    # timed on its own, after the others
-            tc = time_alone(torch, cmp_fn, reps)
-            cmp_rec["us"] = round(tc, 1)
-            cmp_rec["speedup_of_grouped"] = round(tc / t[0], 3)
+            th, tg = time_library(torch, cmp_fn, reps)
+            cmp_rec["us"] = round(tg, 1)
+            cmp_rec["us_host_inclusive"] = round(th, 1)
+            cmp_rec["speedup_of_grouped"] = round(tg / t[0], 3)
         if compare is not None:                   # y8: the grouped call's last result
             cmp_rec["rel_frobenius_vs_grouped"] = compare(y8)
         out[f"fwd_mx:{wl.name}"]["per_expert_scaled_mm"] = cmp_rec
@@ -645,9 +649,10 @@ def mx(torch, mg, reps=20):
             "token_major_us": round(t[2], 1),
             "token_major_pct_fp8_peak": round(100 * flops / t[2] / 1e6 / PEAK_FP8_TFLOPS, 1)}
         if cmp_fn is not None:                    # timed on its own, after the others
-            tc = time_alone(torch, cmp_fn, reps)
-            cmp_rec["us"] = round(tc, 1)
-            cmp_rec["speedup_of_grouped"] = round(tc / t[0], 3)
+            th, tg = time_library(torch, cmp_fn, reps)
+            cmp_rec["us"] = round(tg, 1)
+            cmp_rec["us_host_inclusive"] = round(th, 1)
+            cmp_rec["speedup_of_grouped"] = round(tg / t[0], 3)
         if compare is not None:                   # d8: the grouped call's last result
             cmp_rec["rel_frobenius_vs_grouped"] = compare(d8)
         out[f"wgrad_mx:{wl.name}"]["per_expert_scaled_mm"] = cmp_rec
