@@ -170,6 +170,56 @@ def test_wgrad_first_call_captured_on_fresh_stream():
         assert r.passed, f"replay {rep}: {r}"
 
 
+def test_captured_backward_follows_offsets_changed_in_place():
+    """A graph of one forward, input gradient and weight gradient, captured
+    once (the weight gradient with its stream's workspace, so that the token
+    split is available to it), replayed after each of three routings has been
+    written into the
+    same device offsets array, with eager launches between the replays: the
+    device-side scheduler reads the offsets at every launch, so each replay
+    must match the oracle for the routing it finds, with no re-capture and no
+    host synchronisation on the routing.  The routings keep the row total
+    and include one that puts every row on a single expert."""
+    N, K = 776, 1032
+    routings = [[700, 0, 1300, 45, 2100, 256], [2100, 700, 0, 1300, 256, 45],
+                [0, 0, 4401, 0, 0, 0]]
+    M, E = sum(routings[0]), len(routings[0])
+    assert all(sum(r) == M and len(r) == E for r in routings)
+    off0, _, _, xb, wb, dyb = _inputs(routings[0], N, K, 1900)
+    x, w, dy = dev_bf16(xb), dev_bf16(wb), dev_bf16(dyb)
+    o = dev_i32(off0)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    dx = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    dw = torch.empty((E, N, K), device="cuda")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        mg.wgrad(dy, x, o, out=dw)                  # the stream's workspace, outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    _say("captured fwd + dgrad + wgrad", N, K, routings)
+    with torch.cuda.graph(g, stream=s):
+        mg.fwd(x, w, o, out=y)
+        mg.dgrad(dy, w, o, out=dx)
+        mg.wgrad(dy, x, o, out=dw)
+    torch.cuda.synchronize()
+    scratch = torch.empty((E, N, K), device="cuda")
+    for rep, sizes in enumerate(routings):
+        off = offsets_from_sizes(sizes)
+        o.copy_(dev_i32(off))                       # the new routing, in place
+        y.fill_(float("nan"))
+        dx.fill_(float("nan"))
+        dw.fill_(float("nan"))
+        mg.wgrad(dy, x, dev_i32(offsets_from_sizes(routings[rep - 1])), out=scratch)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, r in (("fwd", gate_fwd_full(xb, wb, off, host_bits(y))),
+                        ("dgrad", gate_dgrad_full(dyb, wb, off, host_bits(dx))),
+                        ("wgrad", gate_wgrad_full(dyb, xb, off, dw.cpu().numpy()))):
+            _say("replay", rep, sizes, name, str(r))
+            assert r.passed, f"replay {rep} {name}: {r}"
+
+
 def test_operands_beyond_4gib_sampled():
     """fwd, dgrad and wgrad where X [1052672, 2176] bf16 (4.58 GB) and the dgrad
     output dX of the same shape extend past 4 GiB, the last expert's rows lying
