@@ -172,11 +172,11 @@ def test_wgrad_first_call_captured_on_fresh_stream():
 
 def test_captured_backward_follows_offsets_changed_in_place():
     """A graph of one forward, input gradient and weight gradient, captured
-    once (the weight gradient with its stream's workspace, so that the token
-    split is available to it), replayed after each of three routings has been
-    written into the
-    same device offsets array, with eager launches between the replays: the
-    device-side scheduler reads the offsets at every launch, so each replay
+    once on a stream that already has its weight-gradient workspace (the
+    captured weight gradient still runs without the token split), replayed
+    after each of three routings has been written into the same device
+    offsets array, with eager launches between the replays: the device-side
+    scheduler reads the offsets at every launch, so each replay
     must match the oracle for the routing it finds, with no re-capture and no
     host synchronisation on the routing.  The routings keep the row total
     and include one that puts every row on a single expert."""
@@ -193,7 +193,7 @@ def test_captured_backward_follows_offsets_changed_in_place():
     dw = torch.empty((E, N, K), device="cuda")
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
-        mg.wgrad(dy, x, o, out=dw)                  # the stream's workspace, outside capture
+        mg.wgrad(dy, x, o, out=dw)                  # allocates the stream's workspace
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     _say("captured fwd + dgrad + wgrad", N, K, routings)
