@@ -243,14 +243,16 @@ def dgrad_swiglu(dy: torch.Tensor, w2: torch.Tensor, gu: torch.Tensor, offsets: 
 
 
 def _matrix(t: torch.Tensor, name: str) -> int:
-    """Row stride of a bf16 matrix view whose rows are contiguous."""
+    """Row stride of a bf16 matrix view whose rows are contiguous; the row
+    length where no stride is needed (one row, or rows of no elements, whose
+    stride torch reports as 1)."""
     if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or t.dim() != 2:
         raise TypeError(f"{name} must be a 2-D bfloat16 tensor")
     if not t.is_cuda:
         raise ValueError(f"{name} must be on a GPU device")
     if t.shape[1] > 1 and t.stride(1) != 1:
         raise ValueError(f"{name} must have contiguous rows")
-    return int(t.stride(0)) if t.shape[0] > 1 else int(t.shape[1])
+    return int(t.stride(0)) if t.shape[0] > 1 and t.shape[1] > 0 else int(t.shape[1])
 
 
 def list_descriptors(groups, outs) -> torch.Tensor:

@@ -676,6 +676,23 @@ def test_grouped_list_mixed_shapes():
             assert (pad == SENTINEL).all(), f"group {g}: padding columns written"
 
 
+def test_grouped_list_zero_width_operands():
+    """Groups with k = 0 whose A and B are plain contiguous [m, 0] and [n, 0]
+    tensors (torch gives such tensors a row stride of 1): the binding passes
+    a row stride the library accepts and the outputs are zeros; a group with
+    n = 0 beside them writes nothing."""
+    a = torch.empty((300, 0), dtype=torch.bfloat16, device="cuda")
+    b = torch.empty((264, 0), dtype=torch.bfloat16, device="cuda")
+    a1 = torch.empty((1, 0), dtype=torch.bfloat16, device="cuda")
+    b0 = torch.empty((0, 8), dtype=torch.bfloat16, device="cuda")
+    a8 = dev_bf16(normal_bf16_bits((40, 8), 1.0, 520, 1))
+    outs = [sentinel_bf16((300, 264)), sentinel_bf16((1, 264)), sentinel_bf16((40, 0))]
+    _say("grouped_list zero-width operands")
+    mg.grouped_list([(a, b), (a1, b), (a8, b0)], outs)
+    torch.cuda.synchronize()
+    assert (host_bits(outs[0]) == 0).all() and (host_bits(outs[1]) == 0).all()
+
+
 def test_grouped_list_equals_mgrouped_forward():
     """Per-expert groups pointing into one X and one W give bitwise the
     M-grouped forward's result (same tiles, same reduction order)."""

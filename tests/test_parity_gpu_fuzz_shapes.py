@@ -1,8 +1,9 @@
-"""Seeded random-shape fuzz of the MXFP8 forward and weight gradients (on
-transposed and on token-major operands), the
-SwiGLU backward and the token-order combine against the oracle (needs an
-MI355X).  Ragged and empty experts, reductions of one block to several
-stages, widths that are not multiples of the tile."""
+"""Seeded random-shape fuzz of the core forward, dgrad and weight gradient,
+the MXFP8 forward and weight gradients (on transposed and on token-major
+operands), the gathered SwiGLU forward and its backward, the token-order
+combine and the descriptor list against the oracle (needs an MI355X).
+Ragged and empty experts, reductions of one block to several stages, widths
+that are not multiples of the tile, strided views."""
 import os
 
 import numpy as np
@@ -196,3 +197,96 @@ def test_fuzz_core_ops(seed):
     rep = gate_wgrad_full(dyb, xb, off, dw.cpu().numpy(),
                           prior=None if prior is None else prior.astype(np.float64))
     assert rep.passed, f"wgrad: {rep}"
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_fuzz_grouped_list(seed):
+    """The descriptor list on random groups: 1-8 independent GEMMs of random
+    m, n, k (empty groups and k = 0 included), operands as views with padded
+    row strides and outputs inside wider buffers, every element against the
+    oracle and the padding columns untouched."""
+    from oracle import check_bf16, grouped_list
+    rng = np.random.default_rng(7000 + seed)
+    G = int(rng.integers(1, 9))
+    shapes = []
+    for _ in range(G):
+        m = int(rng.integers(0, 600)) if rng.random() > 0.15 else 0
+        n = 8 * int(rng.integers(1, 80))
+        k = 8 * int(rng.integers(0, 80)) if rng.random() > 0.1 else 0
+        shapes.append((m, n, k))
+    print("[case] fuzz list", seed, shapes, flush=True)
+    bits, groups, outs, pads = [], [], [], []
+    for g, (m, n, k) in enumerate(shapes):
+        pa, pb, pd = (8 * int(v) for v in rng.integers(0, 4, 3))
+        ab = normal_bf16_bits((m, k), 1.0, 7100, seed, g, 1)
+        bb = normal_bf16_bits((n, k), k ** -0.5 if k else 1.0, 7100, seed, g, 2)
+        abuf = torch.zeros((m, k + pa), dtype=torch.bfloat16, device="cuda")
+        bbuf = torch.zeros((n, k + pb), dtype=torch.bfloat16, device="cuda")
+        if m * k:
+            abuf[:, :k] = dev_bf16(ab)
+        if n * k:
+            bbuf[:, :k] = dev_bf16(bb)
+        dbuf = sentinel_bf16((m, n + pd))
+        bits.append((ab, bb))
+        groups.append((abuf[:, :k], bbuf[:, :k]))
+        outs.append(dbuf[:, :n])
+        pads.append((dbuf, pd))
+    mg.grouped_list(groups, outs)
+    torch.cuda.synchronize()
+    a64 = [(bf16_bits_to_f64(a), bf16_bits_to_f64(b)) for a, b in bits]
+    ref = grouped_list(a64)
+    mag = grouped_list([(np.abs(a), np.abs(b)) for a, b in a64])
+    for g, ((m, n, k), d, r, s, (dbuf, pd)) in enumerate(zip(shapes, outs, ref, mag, pads)):
+        if m == 0:
+            continue
+        rep = check_bf16(host_bits(d), r, s, max(k, 1))
+        assert rep.passed, f"group {g} {shapes[g]}: {rep}"
+        if pd:
+            assert (host_bits(dbuf)[:, n:] == SENTINEL).all(), f"group {g}: padding written"
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_fuzz_fwd_swiglu(seed):
+    """The gate-up forward with SwiGLU on random shapes: rows gathered from a
+    random token map (or not), ragged and empty experts, and for odd seeds the
+    saved pre-activation g | u as well; h on every element against the
+    oracle, g | u against the oracle's plain forward, rows past offsets[E]
+    untouched."""
+    from oracle import check_bf16_swiglu, sample_fwd_swiglu
+    rng = np.random.default_rng(8000 + seed)
+    E = int(rng.integers(1, 8))
+    sizes = _sizes(rng, E, 500)
+    I = 8 * int(rng.integers(1, 50)); K = 8 * int(rng.integers(1, 60))
+    gathered = bool(rng.integers(0, 2))
+    save = bool(seed % 2)
+    off = offsets_from_sizes(sizes)
+    M = int(off[-1]) + 2
+    T = int(rng.integers(1, 700)) if gathered else M
+    print("[case] fuzz fwd_swiglu", seed, sizes, I, K, "T", T if gathered else None,
+          "save" if save else "", flush=True)
+    xb = normal_bf16_bits((T, K), 1.0, 8100, seed, 1)
+    wb = normal_bf16_bits((E, 2 * I, K), K ** -0.5, 8100, seed, 2)
+    gather = rng.integers(0, T, M).astype(np.int32) if gathered else None
+    gu = sentinel_bf16((M, 2 * I)) if save else None
+    h = mg.fwd_swiglu(dev_bf16(xb), dev_bf16(wb), dev_i32(off),
+                      gather=None if gather is None else dev_i32(gather),
+                      out=sentinel_bf16((M, I)), gu_out=gu)
+    torch.cuda.synchronize()
+    got = host_bits(h)
+    o_end = int(off[-1])
+    assert (got[o_end:] == SENTINEL).all()
+    if o_end:
+        rows = np.repeat(np.arange(o_end), I)
+        cols = np.tile(np.arange(I), o_end)
+        hh, g, u, sg, su = sample_fwd_swiglu(xb, gather, wb, off, rows, cols)
+        rep = check_bf16_swiglu(got[rows, cols], hh, g, u, sg, su, K)
+        assert rep.passed, f"h: {rep}"
+    if save:
+        gub = host_bits(gu)
+        assert (gub[o_end:] == SENTINEL).all()
+    if save and o_end:
+        rows_x = xb if gather is None else xb[gather]
+        x64, w64 = bf16_bits_to_f64(rows_x), bf16_bits_to_f64(wb)
+        rep = check_bf16(gub[:o_end], grouped_fwd(x64, w64, off)[:o_end],
+                         grouped_fwd(np.abs(x64), np.abs(w64), off)[:o_end], K)
+        assert rep.passed, f"g | u: {rep}"
