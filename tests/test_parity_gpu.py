@@ -220,6 +220,47 @@ def test_captured_backward_follows_offsets_changed_in_place():
             assert r.passed, f"replay {rep} {name}: {r}"
 
 
+def test_host_threads_on_their_own_streams():
+    """Four host threads, each on a stream of its own, launch the weight
+    gradient (whose token split takes this heavy expert's tiles and a
+    per-stream workspace, allocated on the stream's first call under the
+    library's lock) and the forward five times each, at the same time: every
+    result is bitwise the single-threaded one, which matches the oracle."""
+    import threading
+    sizes, N, K = [2017, 33, 65, 129, 0, 0, 0, 700], 1544, 776
+    off, M, E, xb, wb, dyb = _inputs(sizes, N, K, 2100, x_scale=1.0, w_scale=1.0)
+    dy, x, w, o = dev_bf16(dyb), dev_bf16(xb), dev_bf16(wb), dev_i32(off)
+    ref_dw, ref_y = mg.wgrad(dy, x, o), mg.fwd(x, w, o)
+    torch.cuda.synchronize()
+    r = gate_wgrad_full(dyb, xb, off, ref_dw.cpu().numpy())
+    assert r.passed, str(r)
+    results, errors = {}, []
+
+    def work(t):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                outs = [(mg.wgrad(dy, x, o), mg.fwd(x, w, o)) for _ in range(5)]
+            s.synchronize()
+            results[t] = outs
+        except Exception as ex:                  # reported by the main thread
+            errors.append(repr(ex))
+
+    _say("four host threads, own streams", sizes, N, K)
+    threads = [threading.Thread(target=work, args=(t,)) for t in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=120)
+    assert not errors, errors
+    assert sorted(results) == [0, 1, 2, 3]
+    for t, outs in results.items():
+        for i, (dw, y) in enumerate(outs):
+            assert torch.equal(dw, ref_dw), f"thread {t} call {i}: weight gradient differs"
+            assert torch.equal(y.view(torch.int16), ref_y.view(torch.int16)), \
+                f"thread {t} call {i}: forward differs"
+
+
 def test_operands_beyond_4gib_sampled():
     """fwd, dgrad and wgrad where X [1052672, 2176] bf16 (4.58 GB) and the dgrad
     output dX of the same shape extend past 4 GiB, the last expert's rows lying
