@@ -261,6 +261,26 @@ def test_host_threads_on_their_own_streams():
                 f"thread {t} call {i}: forward differs"
 
 
+def test_validation_and_split_switches():
+    """MGEMM_VALIDATE=1 and MGEMM_SPLIT=0, which the library reads once per
+    process, in a child process (tests/gpu_env_child.py): valid offsets pass
+    and the unsplit weight gradient matches the oracle; decreasing offsets,
+    offsets[E] > M, a missing leading zero and a device descriptor with
+    k = 12 are rejected before any launch, their outputs untouched."""
+    import os
+    import subprocess
+    import sys
+    here = os.path.dirname(os.path.abspath(__file__))
+    env = dict(os.environ, MGEMM_VALIDATE="1", MGEMM_SPLIT="0",
+               PYTHONPATH=os.pathsep.join([os.path.dirname(here), here,
+                                           os.environ.get("PYTHONPATH", "")]))
+    _say("child with MGEMM_VALIDATE=1 MGEMM_SPLIT=0")
+    p = subprocess.run([sys.executable, "-u", os.path.join(here, "gpu_env_child.py")],
+                       env=env, capture_output=True, text=True, timeout=150)
+    print(p.stdout[-3000:], p.stderr[-3000:], flush=True)
+    assert p.returncode == 0 and "[child] ok" in p.stdout
+
+
 def test_operands_beyond_4gib_sampled():
     """fwd, dgrad and wgrad where X [1052672, 2176] bf16 (4.58 GB) and the dgrad
     output dX of the same shape extend past 4 GiB, the last expert's rows lying
